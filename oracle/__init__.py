@@ -1,0 +1,22 @@
+"""fp64 CPU oracle for speculative-decoding verification — TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The library never does, and the two share no code;
+inputs reach both from the ``workloads`` generators.
+
+Parity pins (each checked by ``tests/test_oracle_*.py`` without a GPU):
+  * Philox4x64-10: bit-exact against numpy's independent Philox generator.
+  * softmax: scipy's softmax, closed forms (uniform, two-token logistic).
+  * bf16 widening: torch's bfloat16 -> float32 conversion.
+  * inverse CDF and acceptance: exact law computed with Fractions, interval
+    probes, numpy's searchsorted on cumulative sums.
+  * the whole sampling rule: exact enumeration showing the output law equals
+    the target's (the pages' exactness guarantee), chi-square at 10^6 trials.
+  * greedy: argmax-prefix properties, and the sampling rule's T -> 0 limit.
+  * tree: a chain tree equals greedy; brute-force path enumeration.
+Parity unpinned: individual draws whose uniform lies within 1e-5 of an
+acceptance threshold or CDF boundary (the GPU works in fp32); they are
+counted by the parity tests, not matched.
+"""
+from .philox import philox4x64_10, request_uniforms, uniform24  # noqa: F401
+from .verify import *  # noqa: F401,F403

@@ -1,0 +1,272 @@
+"""Plain fp64 CPU oracle for batched speculative-decoding verification.
+
+Test infrastructure only: imported by ``tests/``, by the smoke check and by
+the CPU-baseline leg of the benchmark, never by the library's product path.
+It shares no code with the HIP library.
+
+Citation key (the pages this follows):
+  [SD]  "【大模型基础设施工程】15：推测解码与 MTP" (juejin.cn): §1.2 (one
+        target forward scores K+1 positions; accepted length per step),
+        §2.1 "算法骨架" (the verification rule), the correctness subsection
+        printed as "1.2 正确性保证" under §2 (output law equals the
+        target's), §2.3 (accepted length alpha in [1, K+1]), §3.3 "Tree
+        Attention" (Medusa tree: each node sees only its ancestors, the
+        longest accepted path wins), §11 (code sketch: drafts [B, K],
+        target logits [B, K+1, V]; greedy speculation reproduces plain
+        greedy output).
+  [FD]  FastDeploy "投机解码", "高效投机解码框架设计" (sampling and
+        verification run per batch sample in parallel).
+
+What the oracle computes, step by step, for one request b with K drafts:
+
+1. Inputs are widened to fp64 exactly (bf16 bit pattern h is the fp32 with
+   bits h << 16).
+2. p_i = softmax(l_i / T) for every target position i = 0..K; q_i is the
+   draft's softmax(l'_i / T) when draft logits are given, otherwise the
+   one-hot vector of the draft token x_i (deterministic drafts: n-gram
+   lookup, MTP greedy heads). [SD §2.1]; T applies to both (reading R1).
+3. Draft x_i is accepted with probability min(1, p_i(x_i) / q_i(x_i)); with a
+   uniform u this is the event u * q_i(x_i) < p_i(x_i) (reading R2). The
+   scan stops at the first rejection. [SD §2.1]
+4. On a rejection at position a the replacement token is drawn from the
+   normalised residual max(0, p_a - q_a); if every draft was accepted a
+   bonus token is drawn from p_K (0-based; the pages' p_{K+1}). [SD §2.1]
+   A residual of total mass zero falls back to p_a (reading R5).
+5. A draw from weights w with uniform u is the inverse CDF: the smallest j
+   whose left-to-right cumulative sum C_j exceeds u * C_{V-1}; if rounding
+   leaves none, the last token of positive weight (reading R6).
+6. Uniforms come from Philox4x64-10 keyed by (seed, request, position,
+   offset), see ``oracle.philox``; one pair per position (reading R3).
+7. Output: tokens x_0..x_{a-1}, then the drawn token, padded with -1;
+   accept_len = a + 1 in [1, K+1] [SD §2.3].
+
+The decision core (``accept_length``, ``residual_weights``, ``inverse_cdf``,
+``verify_request``) uses only +, -, *, comparisons and max, so it runs on
+``fractions.Fraction`` as well as on floats; the tests use that to compute
+the exact output law by enumeration.
+
+Greedy verification: g_i = argmax l_i (lowest index on ties), the longest
+prefix with x_i = g_i is accepted and g_a is emitted [SD §11, greedy output
+equals plain greedy decoding]. Tree verification: node n is accepted when
+its parent is accepted and its token equals the parent's argmax; the
+deepest accepted node wins, lowest index on ties [SD §3.3].
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .philox import request_uniforms
+
+__all__ = [
+    "logits_f64", "softmax_t", "onehot", "accept_length", "residual_weights",
+    "inverse_cdf", "verify_request", "spec_verify_sample", "argmax_lowest",
+    "spec_verify_greedy", "tree_depths", "spec_verify_tree",
+]
+
+
+# ---------------------------------------------------------------- inputs ---
+
+def logits_f64(row, dtype: str) -> np.ndarray:
+    """Widen one logits vector to fp64 exactly. dtype "f32" or "bf16" (uint16 bits)."""
+    a = np.asarray(row)
+    if dtype == "bf16":
+        bits32 = a.astype(np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits32.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def softmax_t(logits: np.ndarray, T: float) -> np.ndarray:
+    """p = softmax(logits / T) in fp64: exp(z - max z) / sum exp(z - max z)."""
+    z = np.asarray(logits, dtype=np.float64) / float(T)
+    m = np.max(z)
+    e = np.exp(z - m)
+    return e / math.fsum(e.tolist())
+
+
+def onehot(V: int, x: int):
+    """q for a deterministic draft token: all mass on x (nothing if x is outside [0, V))."""
+    q = [0.0] * V
+    if 0 <= x < V:
+        q[x] = 1.0
+    return q
+
+
+# --------------------------------------------------------- decision core ---
+
+def accept_length(p_x, q_x, u_acc) -> int:
+    """Number of leading drafts accepted: stop at the first i with not (u_i q_i(x_i) < p_i(x_i))."""
+    a = 0
+    for i in range(len(p_x)):
+        if u_acc[i] * q_x[i] < p_x[i]:
+            a += 1
+        else:
+            break
+    return a
+
+
+def residual_weights(p_row, q_row):
+    """Unnormalised residual max(0, p - q); p itself when that has no mass."""
+    w = [pv - qv if pv > qv else 0 * pv for pv, qv in zip(p_row, q_row)]
+    if not any(v > 0 for v in w):
+        return list(p_row)
+    return w
+
+
+def inverse_cdf(weights, u) -> int:
+    """Smallest j with C_j > u * Z, C_j = w_0 + ... + w_j summed left to right, Z = C_last."""
+    cum = []
+    running = 0 * weights[0]
+    for wj in weights:
+        running = running + wj
+        cum.append(running)
+    target = u * running
+    for j, c in enumerate(cum):
+        if c > target:
+            return j
+    for j in range(len(weights) - 1, -1, -1):      # rounding overshoot
+        if weights[j] > 0:
+            return j
+    return len(weights) - 1
+
+
+def verify_request(p_rows, q_rows, x, u_acc, u_smp) -> dict:
+    """One request: K+1 target distributions, K draft distributions, K drafts, K+1 uniform pairs."""
+    K = len(x)
+    V = len(p_rows[0])
+    p_x = [p_rows[i][x[i]] if 0 <= x[i] < V else 0 * p_rows[i][0] for i in range(K)]
+    q_x = [q_rows[i][x[i]] if 0 <= x[i] < V else 0 * p_rows[i][0] for i in range(K)]
+    a = accept_length(p_x, q_x, u_acc)
+    if a < K:
+        w = residual_weights(p_rows[a], q_rows[a])
+    else:
+        w = list(p_rows[K])
+    y = inverse_cdf(w, u_smp[a])
+    return dict(tokens=list(x[:a]) + [y], accept_len=a + 1, a=a, p_x=p_x, q_x=q_x,
+                weights=w, u_select=u_smp[a], u_acc=list(u_acc))
+
+
+def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0,
+                       target_dtype="f32", draft_dtype="f32", requests=None,
+                       keep_trace=False):
+    """Batched stochastic verification.
+
+    target [B, K+1, V] (fp32 values or bf16 bit patterns), draft [B, >=K, V]
+    or None for one-hot q, draft_tokens [B, K], temperature [B], seeds [B]
+    (uint64), offset: step counter. ``requests`` restricts the work to a
+    subset of request indices (other rows of the outputs stay -1 / 0).
+
+    Returns (tokens [B, K+1] int32, accept_len [B] int32, p_draft [B, K]
+    float64, q_draft [B, K] float64, traces) where traces[b] is the
+    per-request record from ``verify_request`` when keep_trace is set.
+    A request whose temperature is not a finite positive number is refused:
+    accept_len 0, tokens -1, probabilities 0.
+    """
+    B, R, V = target.shape
+    K = R - 1
+    tokens = np.full((B, K + 1), -1, dtype=np.int32)
+    accept_len = np.zeros(B, dtype=np.int32)
+    p_draft = np.zeros((B, K), dtype=np.float64)
+    q_draft = np.zeros((B, K), dtype=np.float64)
+    traces = {}
+    for b in (range(B) if requests is None else requests):
+        T = float(temperature[b])
+        if not (math.isfinite(T) and T > 0):
+            continue
+        p_rows = [softmax_t(logits_f64(target[b, i], target_dtype), T).tolist()
+                  for i in range(K + 1)]
+        x = [int(v) for v in draft_tokens[b, :K]]
+        if draft is not None:
+            q_rows = [softmax_t(logits_f64(draft[b, i], draft_dtype), T).tolist()
+                      for i in range(K)]
+        else:
+            q_rows = [onehot(V, x[i]) for i in range(K)]
+        pairs = [request_uniforms(int(seeds[b]), b, i, int(offset)) for i in range(K + 1)]
+        res = verify_request(p_rows, q_rows, x, [u for u, _ in pairs], [u for _, u in pairs])
+        tokens[b, :res["accept_len"]] = res["tokens"]
+        accept_len[b] = res["accept_len"]
+        p_draft[b, :] = res["p_x"]
+        q_draft[b, :] = res["q_x"]
+        if keep_trace:
+            traces[b] = res
+    return tokens, accept_len, p_draft, q_draft, traces
+
+
+# ------------------------------------------------------- greedy and tree ---
+
+def argmax_lowest(row) -> int:
+    """Index of the largest value, the lowest such index on ties (numpy's argmax rule)."""
+    return int(np.argmax(np.asarray(row, dtype=np.float64)))
+
+
+def spec_verify_greedy(target, draft_tokens, dtype="f32"):
+    """Greedy (argmax-match) verification.
+
+    Returns (tokens [B, K+1] -1 padded, accept_len [B], argmax [B, K+1]).
+    """
+    B, R, V = target.shape
+    K = R - 1
+    tokens = np.full((B, K + 1), -1, dtype=np.int32)
+    accept_len = np.zeros(B, dtype=np.int32)
+    g = np.zeros((B, K + 1), dtype=np.int32)
+    for b in range(B):
+        for i in range(K + 1):
+            g[b, i] = argmax_lowest(logits_f64(target[b, i], dtype))
+        a = 0
+        while a < K and int(draft_tokens[b, a]) == g[b, a]:
+            a += 1
+        tokens[b, :a] = draft_tokens[b, :a]
+        tokens[b, a] = g[b, a]
+        accept_len[b] = a + 1
+    return tokens, accept_len, g
+
+
+def tree_depths(parents) -> list:
+    """Depth of every node; parents[0] = -1 and 0 <= parents[n] < n are required."""
+    parents = [int(p) for p in parents]
+    if not parents or parents[0] != -1:
+        raise ValueError("node 0 must be the root (parent -1)")
+    depth = [0]
+    for n in range(1, len(parents)):
+        if not 0 <= parents[n] < n:
+            raise ValueError(f"parent of node {n} must precede it")
+        depth.append(depth[parents[n]] + 1)
+    return depth
+
+
+def spec_verify_tree(target, node_tokens, parents, dtype="f32"):
+    """Greedy verification of a static draft tree (Medusa style).
+
+    target [B, N, V]: logits at every node (row n predicts the token after
+    node n); node_tokens [B, N] (column 0, the root, is ignored).
+    Returns (tokens [B, N] -1 padded, accept_len [B], best_node [B]).
+    """
+    B, N, V = target.shape
+    depth = tree_depths(parents)
+    tokens = np.full((B, N), -1, dtype=np.int32)
+    accept_len = np.zeros(B, dtype=np.int32)
+    best_node = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        g = [argmax_lowest(logits_f64(target[b, n], dtype)) for n in range(N)]
+        acc = [True] + [False] * (N - 1)
+        for n in range(1, N):
+            p = int(parents[n])
+            acc[n] = acc[p] and int(node_tokens[b, n]) == g[p]
+        best = 0
+        for n in range(1, N):
+            if acc[n] and depth[n] > depth[best]:
+                best = n
+        path = []
+        n = best
+        while n != 0:
+            path.append(int(node_tokens[b, n]))
+            n = int(parents[n])
+        path.reverse()
+        row = path + [g[best]]
+        tokens[b, :len(row)] = row
+        accept_len[b] = len(row)
+        best_node[b] = best
+    return tokens, accept_len, best_node
