@@ -1,0 +1,183 @@
+/*
+ * specverify.h — C ABI of the MI355X (gfx950) speculative-decoding verifier.
+ *
+ * One target forward over K+1 positions yields the logits of K+1 target
+ * distributions per request; these entry points decide which of the K draft
+ * tokens are accepted and produce the one extra token (replacement or bonus)
+ * of the step ("【大模型基础设施工程】15：推测解码与 MTP", juejin: §1.2 and
+ * §2.1). Requests are verified in parallel, one batch per call (FastDeploy
+ * "投机解码", "高效投机解码框架设计": parallel sampling + verification per
+ * batch sample).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer is a DEVICE pointer unless its comment says [host].
+ *  - Logits are row-major with the vocabulary innermost (stride 1) and
+ *    described by sv_logits; strides are in ELEMENTS and may be 0
+ *    (broadcast). Rows whose address and strides are 16-byte aligned take
+ *    the 128-bit load path, others a scalar path with identical results.
+ *  - The caller owns every buffer. The library allocates nothing, keeps no
+ *    state between calls, never synchronises and launches only on `stream`
+ *    (a hipStream_t; NULL = the default stream). Results are ready when the
+ *    stream reaches them.
+ *  - Argument errors are detected on the host before anything is launched
+ *    and returned as a negative status; nothing is written then.
+ *    Device-resident values are not checked on the host; their handling is
+ *    stated per entry point.
+ *  - Workspace: size from spec_verify_workspace_size(), zero-filled ONCE by
+ *    spec_verify_workspace_init() (or any zero fill) before its first use.
+ *    Every call leaves the workspace's counter words zero again, so it can
+ *    be reused by any later call that fits; it must not be shared by calls
+ *    that may run concurrently (different streams).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SV_OK             0
+#define SV_ERR_NULL      -1   /* a required pointer is NULL */
+#define SV_ERR_SHAPE     -2   /* B, K, N or V out of range */
+#define SV_ERR_DTYPE     -3   /* unknown dtype or reserved field not 0 */
+#define SV_ERR_STRIDE    -4   /* negative stride */
+#define SV_ERR_WORKSPACE -5   /* workspace NULL or smaller than required */
+#define SV_ERR_TREE      -6   /* malformed parent array */
+#define SV_ERR_HIP       -7   /* a HIP launch failed (hipGetLastError) */
+
+/* logits element types */
+#define SV_DTYPE_F32  0
+#define SV_DTYPE_BF16 1
+
+/* operation ids for spec_verify_workspace_size */
+#define SV_OP_SAMPLE 0
+#define SV_OP_GREEDY 1
+#define SV_OP_TREE   2
+
+/* limits */
+#define SV_MAX_BATCH      65536
+#define SV_MAX_DRAFT      32          /* K */
+#define SV_MAX_TREE_NODES 64          /* N, root included */
+#define SV_MAX_VOCAB      (1 << 30)
+
+/* A [B, rows, V] logits tensor: element (b, r, v) is at
+ * data + (b * stride_b + r * stride_k + v) * sizeof(element). */
+typedef struct sv_logits {
+  const void* data;    /* device pointer to element (0, 0, 0) */
+  int32_t dtype;       /* SV_DTYPE_F32 or SV_DTYPE_BF16 */
+  int32_t reserved;    /* must be 0 */
+  int64_t stride_b;    /* elements between requests, >= 0 */
+  int64_t stride_k;    /* elements between positions (rows), >= 0 */
+} sv_logits;
+
+/*
+ * Bytes of workspace needed by one call of `op` with batch B, K drafts
+ * (SV_OP_TREE: N nodes) and vocabulary V; `has_draft` is 1 when
+ * spec_verify_sample gets draft logits. The value is valid for either
+ * logits dtype. Returns 0 for arguments out of range.
+ */
+size_t spec_verify_workspace_size(int32_t op, int32_t B, int32_t K_or_N, int32_t V,
+                                  int32_t has_draft);
+
+/* Zero-fill `workspace_bytes` bytes of a workspace on `stream` (a fill
+ * kernel, no memset node). SV_ERR_NULL for a NULL workspace. */
+int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stochastic verification ("推测解码与 MTP" §2.1; exactness: the
+ * correctness subsection under §2).
+ *
+ * For request b with temperature T = temperature[b]:
+ *   p_i = softmax(target[b, i, :] / T), i = 0..K        (K+1 rows)
+ *   q_i = softmax(draft[b, i, :] / T), i = 0..K-1; when draft == NULL q_i is
+ *         one-hot at draft_tokens[b, i] (n-gram / MTP drafts).
+ *   Draft x_i = draft_tokens[b, i] is accepted when u_i * q_i(x_i) < p_i(x_i),
+ *   i.e. with probability min(1, p_i(x_i) / q_i(x_i)); the scan stops at
+ *   the first rejection a, where one token is drawn from the normalised
+ *   residual max(0, p_a - q_a) (p_a if that has no mass); if all K are
+ *   accepted the token is drawn from p_K. Draws are inverse-CDF: the
+ *   smallest token whose running sum exceeds u times the total.
+ *   The two uniforms of (b, i) are the top 24 bits of words 0 and 1 of
+ *   Philox4x64-10 (Salmon et al., SC'11) with counter (i, b, offset, 0) and
+ *   key (seeds[b], 0); the same (seeds, offset) replays a call exactly.
+ *
+ * target        [B, K+1, V] logits (fp32 or bf16)
+ * draft         [host] NULL, or [B, >=K, V] logits (only rows 0..K-1 read)
+ * draft_tokens  [B, K] int32, row-major; may be NULL when K == 0
+ * temperature   [B] float, > 0
+ * seeds         [B] uint64
+ * offset        [host] step counter folded into the Philox counter
+ * B, K, V       1 <= B <= SV_MAX_BATCH, 0 <= K <= SV_MAX_DRAFT,
+ *               1 <= V <= SV_MAX_VOCAB
+ * out_tokens    [B, K+1] int32: accepted drafts, then the drawn token,
+ *               then -1
+ * out_accept_len [B] int32: tokens emitted, a + 1 in [1, K+1]
+ * out_p_draft   [B, K] float or NULL: p_i(x_i) for every i < K
+ * out_q_draft   [B, K] float or NULL: q_i(x_i) for every i < K
+ * Device-side values: a request whose temperature is not a finite positive
+ * number is refused (accept_len 0, tokens -1, p/q 0); a draft token outside
+ * [0, V) has p = q = 0 and is rejected; logits must not be NaN or +inf and
+ * a row must not be entirely -inf (results are then unspecified, never an
+ * out-of-bounds access).
+ */
+int spec_verify_sample(const sv_logits* target, const sv_logits* draft,
+                       const int32_t* draft_tokens, const float* temperature,
+                       const uint64_t* seeds, uint64_t offset,
+                       int32_t B, int32_t K, int32_t V,
+                       int32_t* out_tokens, int32_t* out_accept_len,
+                       float* out_p_draft, float* out_q_draft,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy (argmax-match) verification: g_i = argmax_v target[b, i, v]
+ * (lowest index on ties); the longest prefix with draft_tokens[b, i] == g_i
+ * is accepted (a tokens) and g_a is emitted after it. This reproduces plain
+ * greedy decoding ("推测解码与 MTP" §11; MTP drafts, §6.2).
+ *
+ * target [B, K+1, V]; draft_tokens [B, K] (may be NULL when K == 0);
+ * out_tokens [B, K+1] (-1 padded); out_accept_len [B] in [1, K+1];
+ * out_argmax [B, K+1] or NULL (g_i of every row). Limits as for sampling.
+ * A draft token outside [0, V) never matches.
+ */
+int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
+                       int32_t B, int32_t K, int32_t V,
+                       int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy verification of a static draft tree (Medusa, "推测解码与 MTP"
+ * §3.3: every node attends only to its ancestors; the longest accepted
+ * root path wins).
+ *
+ * target       [B, N, V]: row n holds the logits the target produced at
+ *              node n (its prediction for the token after node n)
+ * node_tokens  [B, N] int32: the draft token of each node (column 0, the
+ *              root, is ignored)
+ * parents      [host] [N] int32: parents[0] == -1, 0 <= parents[n] < n
+ * N, B, V      2 <= N <= SV_MAX_TREE_NODES; B, V as above
+ * Node n != 0 is accepted when its parent is accepted and
+ * node_tokens[b, n] == argmax(row parents[n]) (lowest index on ties); the
+ * deepest accepted node wins (lowest index on ties).
+ * out_tokens     [B, N] int32: the winning path's node tokens (root
+ *                excluded), then the winner's argmax, then -1
+ * out_accept_len [B] int32: depth(best) + 1
+ * out_best_node  [B] int32 or NULL
+ * SV_ERR_TREE when `parents` is malformed.
+ */
+int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
+                     const int32_t* parents, int32_t N, int32_t B, int32_t V,
+                     int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_best_node,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* spec_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

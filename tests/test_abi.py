@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, sizes workspaces, and rejects bad arguments on the host before any
+launch (so these calls never touch HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_verification_05_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)          # never dereferenced: every call below fails validation
+BIG_WS = 1 << 40
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "specverify.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(spec_verify_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree",
+            "spec_verify_workspace_size", "spec_verify_workspace_init",
+            "spec_verify_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(0, -8, -1):
+        s = sv.spec_verify_status_string(code)
+        assert s and s != "unknown status"
+    assert sv.spec_verify_status_string(-99) == "unknown status"
+
+
+def test_workspace_size(lib):
+    f = sv.spec_verify_workspace_size
+    assert f(sv.SV_OP_SAMPLE, 0, 5, 100) == 0
+    assert f(sv.SV_OP_SAMPLE, 1, 33, 100) == 0
+    assert f(sv.SV_OP_TREE, 1, 1, 100) == 0
+    assert f(sv.SV_OP_TREE, 1, 65, 100) == 0
+    assert f(7, 1, 1, 100) == 0
+    a = f(sv.SV_OP_SAMPLE, 256, 5, 128256)
+    assert a > 0 and a % 256 == 0
+    assert f(sv.SV_OP_SAMPLE, 256, 5, 128256, True) > a
+    assert f(sv.SV_OP_SAMPLE, 257, 5, 128256) > a
+    assert f(sv.SV_OP_GREEDY, 128, 3, 129280) > 0
+    assert f(sv.SV_OP_TREE, 32, 31, 32000) > 0
+    # the counter block alone is 4 bytes per request of the largest batch
+    assert f(sv.SV_OP_GREEDY, 1, 0, 1) >= 4 * 65536
+
+
+def desc(dtype=0, reserved=0, sb=10, sk=5, data=FAKE):
+    return sv.SVLogits(data, dtype, reserved, sb, sk)
+
+
+def call_sample(lib, t=None, d=None, B=2, K=1, V=5, ws=FAKE, wsb=BIG_WS, temp=FAKE, seeds=FAKE,
+                tokens=FAKE, out=FAKE):
+    t = desc() if t is None else t
+    return lib.spec_verify_sample(ctypes.byref(t), ctypes.byref(d) if d is not None else None,
+                                  tokens, temp, seeds, 0, B, K, V, out, out, None, None, ws, wsb, None)
+
+
+def test_sample_argument_errors(lib):
+    assert lib.spec_verify_sample(None, None, FAKE, FAKE, FAKE, 0, 1, 1, 5, FAKE, FAKE, None,
+                                  None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert call_sample(lib, t=desc(data=None)) == sv.SV_ERR_NULL
+    assert call_sample(lib, temp=None) == sv.SV_ERR_NULL
+    assert call_sample(lib, seeds=None) == sv.SV_ERR_NULL
+    assert call_sample(lib, tokens=None) == sv.SV_ERR_NULL
+    assert call_sample(lib, out=None) == sv.SV_ERR_NULL
+    assert call_sample(lib, B=0) == sv.SV_ERR_SHAPE
+    assert call_sample(lib, B=65537) == sv.SV_ERR_SHAPE
+    assert call_sample(lib, K=-1) == sv.SV_ERR_SHAPE
+    assert call_sample(lib, K=33) == sv.SV_ERR_SHAPE
+    assert call_sample(lib, V=0) == sv.SV_ERR_SHAPE
+    assert call_sample(lib, V=(1 << 30) + 1) == sv.SV_ERR_SHAPE
+    assert call_sample(lib, t=desc(dtype=2)) == sv.SV_ERR_DTYPE
+    assert call_sample(lib, t=desc(reserved=1)) == sv.SV_ERR_DTYPE
+    assert call_sample(lib, d=desc(dtype=1)) == sv.SV_ERR_DTYPE       # draft dtype differs
+    assert call_sample(lib, t=desc(sb=-1)) == sv.SV_ERR_STRIDE
+    assert call_sample(lib, d=desc(sk=-4)) == sv.SV_ERR_STRIDE
+    assert call_sample(lib, ws=None) == sv.SV_ERR_WORKSPACE
+    need = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, 2, 1, 5)
+    assert call_sample(lib, wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    need_d = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, 2, 1, 5, True)
+    assert call_sample(lib, d=desc(), wsb=need_d - 1) == sv.SV_ERR_WORKSPACE
+
+
+def test_greedy_argument_errors(lib):
+    g = lib.spec_verify_greedy
+    t = desc()
+    assert g(None, FAKE, 1, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert g(ctypes.byref(t), None, 1, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert g(ctypes.byref(t), FAKE, 1, 1, 5, None, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert g(ctypes.byref(t), FAKE, 1, 40, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+    assert g(ctypes.byref(t), FAKE, 1, 1, 5, FAKE, FAKE, None, None, BIG_WS, None) == sv.SV_ERR_WORKSPACE
+    assert g(ctypes.byref(t), FAKE, 1, 1, 5, FAKE, FAKE, None, FAKE, 16, None) == sv.SV_ERR_WORKSPACE
+    bad = desc(dtype=9)
+    assert g(ctypes.byref(bad), FAKE, 1, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_DTYPE
+
+
+def test_tree_argument_errors(lib):
+    tr = lib.spec_verify_tree
+    t = desc()
+
+    def par(*v):
+        return ctypes.cast((ctypes.c_int32 * len(v))(*v), ctypes.c_void_p)
+
+    ok = par(-1, 0, 0)
+    assert tr(ctypes.byref(t), FAKE, None, 3, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert tr(ctypes.byref(t), FAKE, ok, 1, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+    assert tr(ctypes.byref(t), FAKE, ok, 65, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+    assert tr(ctypes.byref(t), FAKE, par(0, 0, 0), 3, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS,
+              None) == sv.SV_ERR_TREE
+    assert tr(ctypes.byref(t), FAKE, par(-1, 0, 2), 3, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS,
+              None) == sv.SV_ERR_TREE
+    assert tr(ctypes.byref(t), FAKE, par(-1, 0, -1), 3, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS,
+              None) == sv.SV_ERR_TREE
+    assert tr(ctypes.byref(t), FAKE, ok, 3, 1, 5, FAKE, FAKE, None, FAKE, 100, None) == sv.SV_ERR_WORKSPACE
+
+
+def test_workspace_init_null(lib):
+    assert lib.spec_verify_workspace_init(None, 100, None) == sv.SV_ERR_NULL
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        sv.load_library(str(tmp_path / "nope.so"))

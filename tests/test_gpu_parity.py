@@ -1,0 +1,263 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Reduced sizes span several 8192-logit segments plus a ragged tail, in both
+the 128-bit and the scalar (misaligned) load paths; the five named workloads
+run at their full sizes in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_verification_05_amd as sv
+import oracle
+from chisq import chisq_pvalue
+from parity import assert_report, classify_sample, new_report, to_device
+from workloads import f32_to_bf16_bits, make, medusa_tree_parents
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def run_sample(wl, draft_bf16=False, offset=None):
+    d = to_device(wl, DEV, draft_bf16=draft_bf16)
+    off = wl["offset"] if offset is None else offset
+    tok, alen, p, q = sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["temperature"],
+                                            d["seeds"], off)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), alen.cpu().numpy(), p.cpu().numpy(), q.cpu().numpy()
+
+
+def check_sample(wl, name, requests=None, draft_bf16=False):
+    print(f"[case] {name} B={wl['B']} K={wl['K']} V={wl['V']} dtype={wl['dtype']}", flush=True)
+    if draft_bf16:
+        wl = dict(wl, draft=f32_to_bf16_bits(wl["draft"]))
+    g = run_sample(wl, draft_bf16=draft_bf16)
+    rep = classify_sample(wl, *g, requests=requests, draft_dtype="bf16" if draft_bf16 else "f32")
+    assert_report(rep, name)
+    return rep
+
+
+# ---------------------------------------------------------------- sample ---
+SAMPLE_REDUCED = [
+    # name, workload, overrides
+    ("c1-full", "c1_tiny", {}),
+    ("c2-ragged", "c2_stoch", dict(B=16, V=3 * 8192 + 1234)),
+    ("c2-odd-V-scalar-path", "c2_stoch", dict(B=12, V=20001)),
+    ("c2-one-segment", "c2_stoch", dict(B=8, V=777)),
+    ("c3-ragged-aligned", "c3_onehot", dict(B=32, V=2 * 8192 + 1232)),
+    ("c3-odd-V-scalar-path", "c3_onehot", dict(B=24, V=2 * 8192 + 777)),
+    ("c3-K1", "c3_onehot", dict(B=40, K=1, V=9000)),
+]
+
+
+@pytest.mark.parametrize("name,cfg,kw", SAMPLE_REDUCED, ids=[c[0] for c in SAMPLE_REDUCED])
+def test_sample_reduced(name, cfg, kw):
+    rep = new_report()
+    for offset in range(3):
+        wl = make(cfg, data_seed=100 + offset, offset=offset, **kw)
+        check_sample(wl, f"{name}/off{offset}", requests=None)
+        rep["requests"] += wl["B"]
+
+
+def test_sample_c1_many_offsets():
+    wl = make("c1_tiny", data_seed=5)
+    d = to_device(wl, DEV)
+    rep = new_report()
+    for off in range(200):
+        tok, alen, p, q = sv.spec_verify_sample(d["target"], d["draft"], d["tokens"], d["temperature"],
+                                                d["seeds"], off)
+        w = dict(wl, offset=off)
+        classify_sample(w, tok.cpu().numpy(), alen.cpu().numpy(), p.cpu().numpy(), q.cpu().numpy(),
+                        report=rep)
+    assert_report(rep, "c1 x 200 offsets")
+
+
+def test_sample_bf16_explicit_draft():
+    wl = make("c2_stoch", data_seed=7, B=10, V=8192 + 100)
+    wl = dict(wl, target=f32_to_bf16_bits(wl["target"]), dtype="bf16")
+    check_sample(wl, "bf16 target + bf16 draft", draft_bf16=True)
+
+
+def test_sample_K0_is_plain_sampling():
+    wl = make("c3_onehot", data_seed=8, B=64, K=0, V=5000)
+    check_sample(wl, "K=0")
+
+
+def test_sample_vocab_one():
+    wl = make("c2_stoch", data_seed=9, B=4, K=2, V=1)
+    g_tok, g_len, _, _ = run_sample(wl)
+    assert np.all(g_len == 3) and np.all(g_tok == 0)
+
+
+def test_sample_edge_device_values():
+    """Refused temperatures, out-of-range drafts, masked logits."""
+    wl = make("c3_onehot", data_seed=10, B=16, V=9000)
+    T = wl["temperature"].copy()
+    T[[1, 2, 3, 4]] = [0.0, -1.0, np.nan, np.inf]
+    tok = wl["draft_tokens"].copy()
+    tok[5, 0] = -1
+    tok[6, 0] = 9000
+    tok[7, 2] = 2**31 - 1
+    tgt = wl["target"].copy()
+    tgt[8, :, ::3] = 0xFF80                    # bf16 -inf: masked vocabulary entries
+    wl = dict(wl, temperature=T, draft_tokens=tok, target=tgt)
+    check_sample(wl, "edge device values")
+
+
+def test_sample_broadcast_and_strided_rows():
+    """stride_b = 0 (one row set for every request) and rows cut from wider storage."""
+    wl = make("c2_stoch", data_seed=11, B=1, K=3, V=10000)
+    base = to_device(wl, DEV)
+    B = 48
+    tgt = base["target"].expand(B, -1, -1)
+    drf = base["draft"].expand(B, -1, -1)
+    rng = np.random.default_rng(3)
+    tokens = rng.integers(0, 10000, size=(B, 3)).astype(np.int32)
+    seeds = rng.integers(0, 2**62, size=B).astype(np.uint64)
+    temp = np.full(B, 0.8, np.float32)
+    g = sv.spec_verify_sample(tgt, drf, torch.from_numpy(tokens).to(DEV), torch.from_numpy(temp).to(DEV),
+                              torch.from_numpy(seeds.view(np.int64)).to(DEV), 3)
+    g = [t.cpu().numpy() for t in g]
+    wlb = dict(wl, B=B, target=np.broadcast_to(wl["target"], (B, 4, 10000)),
+               draft=np.broadcast_to(wl["draft"], (B, 3, 10000)), draft_tokens=tokens, seeds=seeds,
+               temperature=temp, offset=3)
+    assert_report(classify_sample(wlb, *g), "stride_b=0")
+    # rows inside wider storage: stride_k > V
+    wide = make("c3_onehot", data_seed=12, B=8, V=12000)
+    store = np.zeros((8, 6, 12345), np.uint16)
+    store[:, :, :12000] = wide["target"]
+    dt = torch.from_numpy(store.view(np.int16)).to(DEV).view(torch.bfloat16)[:, :, :12000]
+    d = to_device(wide, DEV)
+    out = sv.spec_verify_sample(dt, None, d["tokens"], d["temperature"], d["seeds"], 0)
+    assert_report(classify_sample(wide, *[t.cpu().numpy() for t in out]), "stride_k > V")
+
+
+def test_sample_deterministic_and_workspace_reuse():
+    big = make("c3_onehot", data_seed=13, B=64, V=20000)
+    small = make("c2_stoch", data_seed=14, B=3, V=5000)
+    r1 = run_sample(big)
+    run_sample(small)
+    r2 = run_sample(big)
+    for a, b in zip(r1, r2):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", ["c2_stoch", "c3_onehot"])
+def test_sample_full_size(cfg):
+    wl = make(cfg, data_seed=1)
+    check_sample(wl, f"{cfg} full")
+
+
+def test_gpu_chisquare_exactness():
+    """10^6 GPU draws at the tiny workload's shape follow the target law."""
+    wl = make("c1_tiny", data_seed=3)
+    T = float(wl["temperature"][0])
+    p0 = oracle.softmax_t(oracle.logits_f64(wl["target"][0, 0], "f32"), T)
+    p1 = oracle.softmax_t(oracle.logits_f64(wl["target"][0, 1], "f32"), T)
+    q0 = oracle.softmax_t(oracle.logits_f64(wl["draft"][0, 0], "f32"), T)
+    d = to_device(wl, DEV)
+    B, calls = 65536, 16
+    tgt = d["target"].expand(B, -1, -1)
+    drf = d["draft"].expand(B, -1, -1)
+    temp = torch.full((B,), T, dtype=torch.float32, device=DEV)
+    rng = np.random.default_rng(77)
+    c0 = np.zeros(1000, np.int64)
+    c1 = np.zeros(1000, np.int64)
+    cq, cp1 = np.cumsum(q0), np.cumsum(p1)
+    for call in range(calls):
+        x = np.minimum(np.searchsorted(cq, rng.random(B) * cq[-1], side="right"), 999).astype(np.int32)
+        seeds = rng.integers(0, 2**62, size=B).astype(np.int64)
+        tok, alen, _, _ = sv.spec_verify_sample(tgt, drf, torch.from_numpy(np.ascontiguousarray(x[:, None])).to(DEV), temp,
+                                                torch.from_numpy(seeds).to(DEV), call)
+        tok = tok.cpu().numpy()
+        alen = alen.cpu().numpy()
+        first = tok[:, 0]
+        second = np.where(alen == 2, tok[:, 1],
+                          np.minimum(np.searchsorted(cp1, rng.random(B) * cp1[-1], side="right"), 999))
+        c0 += np.bincount(first, minlength=1000)
+        c1 += np.bincount(second, minlength=1000)
+
+    pval = chisq_pvalue
+    p_first, p_second = pval(c0, p0), pval(c1, p1)
+    print(f"[chisq] gpu first-token p={p_first:.3g} second-token p={p_second:.3g}", flush=True)
+    assert p_first > 1e-4 and p_second > 1e-4
+
+
+# ---------------------------------------------------------------- greedy ---
+def check_greedy(wl, name):
+    print(f"[case] {name} B={wl['B']} K={wl['K']} V={wl['V']} dtype={wl['dtype']}", flush=True)
+    d = to_device(wl, DEV)
+    tok, alen, g = sv.spec_verify_greedy(d["target"], d["tokens"])
+    torch.cuda.synchronize()
+    o_tok, o_len, o_g = oracle.spec_verify_greedy(wl["target"], wl["draft_tokens"], wl["dtype"])
+    np.testing.assert_array_equal(g.cpu().numpy(), o_g)
+    np.testing.assert_array_equal(alen.cpu().numpy(), o_len)
+    np.testing.assert_array_equal(tok.cpu().numpy(), o_tok)
+    print(f"[parity] {name}: exact, mean accept_len={o_len.mean():.3f}", flush=True)
+
+
+@pytest.mark.parametrize("V", [1, 100, 8192, 3 * 8192 + 5, 20001])
+def test_greedy_reduced(V):
+    check_greedy(make("c4_greedy", data_seed=20, B=16, V=V), f"greedy V={V}")
+
+
+def test_greedy_bf16_ties():
+    wl = make("c4_greedy", data_seed=21, B=24, K=4, V=9000)
+    x = np.round(wl["target"] * 2) / 2             # coarse values: many exact ties
+    bits = f32_to_bf16_bits(x.astype(np.float32))
+    bits[3, :, :] = f32_to_bf16_bits(np.float32(1.0))   # an all-equal row: index 0 wins
+    bits[4, 1, :] = 0xFF80                                 # an all -inf row: index 0 wins
+    vals = oracle.logits_f64(bits.reshape(-1), "bf16").reshape(bits.shape)
+    am = vals.argmax(-1)
+    tok = np.where(np.random.default_rng(1).random((24, 4)) < 0.8, am[:, :4], 5).astype(np.int32)
+    tok[0, 0] = -7
+    check_greedy(dict(wl, target=bits, dtype="bf16", draft_tokens=tok, K=4), "greedy bf16 ties")
+
+
+def test_greedy_full_size():
+    check_greedy(make("c4_greedy", data_seed=1), "c4 full")
+
+
+# ------------------------------------------------------------------ tree ---
+def check_tree(wl, parents, name):
+    print(f"[case] {name} B={wl['B']} N={len(parents)} V={wl['V']}", flush=True)
+    d = to_device(wl, DEV)
+    tok, alen, best = sv.spec_verify_tree(d["target"], d["tokens"], list(parents))
+    torch.cuda.synchronize()
+    o_tok, o_len, o_best = oracle.spec_verify_tree(wl["target"], wl["draft_tokens"], parents, wl["dtype"])
+    np.testing.assert_array_equal(best.cpu().numpy(), o_best)
+    np.testing.assert_array_equal(alen.cpu().numpy(), o_len)
+    np.testing.assert_array_equal(tok.cpu().numpy(), o_tok)
+    print(f"[parity] {name}: exact, accept_len histogram={np.bincount(o_len).tolist()}", flush=True)
+
+
+def test_tree_full_size():
+    wl = make("c5_tree", data_seed=1)
+    check_tree(wl, wl["parents"], "c5 full")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tree_random_shapes(seed):
+    rng = np.random.default_rng(300 + seed)
+    N = int(rng.choice([2, 5, 31, 64]))
+    parents = np.array([-1] + [int(rng.integers(0, n)) for n in range(1, N)], np.int32)
+    B, V = 20, int(rng.choice([7, 9000, 20001]))
+    tgt = rng.normal(0, 1, (B, N, V)).astype(np.float32)
+    g = tgt.argmax(-1)
+    tok = rng.integers(0, V, (B, N)).astype(np.int32)
+    for n in range(1, N):                    # make acceptance likely along some edges
+        hit = rng.random(B) < 0.7
+        tok[hit, n] = g[hit, parents[n]]
+    wl = dict(target=tgt, draft_tokens=tok, B=B, V=V, dtype="f32", seeds=np.zeros(B, np.uint64))
+    check_tree(wl, parents, f"tree N={N} V={V}")
+
+
+def test_chain_tree_equals_greedy_on_gpu():
+    wl = make("c4_greedy", data_seed=22, B=16, K=5, V=10000)
+    d = to_device(wl, DEV)
+    g_tok, g_len, _ = sv.spec_verify_greedy(d["target"], d["tokens"])
+    node_tok = torch.cat([torch.full((16, 1), -1, dtype=torch.int32, device=DEV), d["tokens"]], 1).contiguous()
+    t_tok, t_len, best = sv.spec_verify_tree(d["target"], node_tok, list(range(-1, 5)))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(t_len.cpu().numpy(), g_len.cpu().numpy())
+    np.testing.assert_array_equal(t_tok.cpu().numpy(), g_tok.cpu().numpy())

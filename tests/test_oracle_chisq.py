@@ -10,9 +10,9 @@ import os
 
 import numpy as np
 import pytest
-from scipy import stats
 
 import oracle
+from chisq import chisq_pvalue
 from workloads import make
 
 N_TRIALS = 1_000_000
@@ -73,22 +73,7 @@ def _run(p, q, n, mutate=False):
     return counts, joint
 
 
-def _chisq_p(observed, probs):
-    exp = probs * observed.sum()
-    order = np.argsort(exp)
-    obs_m, exp_m = [], []
-    acc_o = acc_e = 0.0
-    for i in order:                         # merge small-expectation bins
-        acc_o += observed[i]
-        acc_e += exp[i]
-        if acc_e >= 5:
-            obs_m.append(acc_o)
-            exp_m.append(acc_e)
-            acc_o = acc_e = 0.0
-    if acc_e > 0:
-        obs_m[-1] += acc_o
-        exp_m[-1] += acc_e
-    return stats.chisquare(obs_m, exp_m).pvalue
+_chisq_p = chisq_pvalue
 
 
 @pytest.mark.slow

@@ -192,9 +192,11 @@ def make(name: str, data_seed: int = 0, *, B: int | None = None, K: int | None =
         if K:
             am = np.argmax(tgt_vals[:, :K, :], axis=-1)
             hit = rng.random((B, K)) < cfg.p_match
-            if cfg.mode == "greedy":
+            if cfg.mode == "greedy" and V > 1:
                 other = rng.integers(0, V - 1, size=(B, K))
                 other = other + (other >= am)          # uniform over tokens != argmax
+            elif cfg.mode == "greedy":
+                other = am
             else:
                 other = rng.integers(0, V, size=(B, K))
             tokens = np.where(hit, am, other).astype(np.int32)
