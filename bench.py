@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of batched speculative-decoding verification on one MI355X.
+
+One step = one call of the verification entry point over one batch of
+synthetic logits already resident in HBM (all kernels of the path). The
+default workload is B=256 requests, K=5 one-hot drafts, V=128256, bf16
+target logits, T=0.7 (``c3_onehot`` in ``workloads``). Inputs rotate over
+several copies so the 256 MB memory-side cache cannot serve them.
+
+Prints one JSON line: logits GB/s (algorithmic bytes / step time), us/step,
+the dominant kernel's roofline, and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "spec-verify µs/step and logits GB/s (% HBM peak) at B=256,K=5,V=128256"
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "draft_verification_05_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, seg_elems=8192) -> int:
+    """One read of every logits row the rule consults, plus the draw's one
+    re-read segment per request (greedy and tree draw nothing)."""
+    es = 2 if wl["dtype"] == "bf16" else 4
+    B, V = wl["B"], wl["V"]
+    if wl["mode"] == "tree":
+        return B * len(wl["parents"]) * V * es
+    K = wl["K"]
+    rows = K + 1 + (K if wl.get("draft") is not None else 0)
+    total = B * rows * V * es
+    if wl["mode"] == "sample":
+        total += B * min(seg_elems, V) * es
+        if wl.get("draft") is not None:
+            # explicit drafts: the rejected requests re-read target and draft stop rows
+            total += B * 2 * V * es
+    return total
+
+
+def traffic_record(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds: float):
+    import oracle
+    B = wl["B"]
+    t0 = time.perf_counter()
+    n = 0
+    while n < B and (time.perf_counter() - t0) < seconds:
+        oracle.spec_verify_sample(wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"],
+                                  wl["seeds"], wl["offset"], target_dtype=wl["dtype"], requests=[n])
+        n += 1
+    dt = time.perf_counter() - t0
+    sample_bytes = algorithmic_bytes(wl) * n / B
+    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {B} requests of {wl['name']} ({n * (wl['K'] + 1)} logits rows), "
+                      f"{dt:.1f} s, single thread",
+            "us_per_step_equiv": round(dt / n * B * 1e6, 1)}
+
+
+def run_copy(args):
+    """Plain device copy of a known size (calibrates the HBM byte counters)."""
+    import torch
+    n = 1 << 28                                # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                      "launches": args.steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3_onehot")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["verify", "copy"], default="verify")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the verification path has no multi-GPU form here "
+              "(requests would shard across GPUs with no communication). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.mode == "copy":
+        return run_copy(args)
+
+    import draft_verification_05_amd as sv
+    from workloads import make
+
+    dev = torch.device("cuda:0")
+    wl = make(args.workload, data_seed=0)
+    lib = sv.load_library()
+    B, K, V = wl["B"], wl["K"], wl["V"]
+    mode = wl["mode"]
+
+    if wl["dtype"] == "bf16":
+        tgt0 = torch.from_numpy(wl["target"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        tgt0 = torch.from_numpy(wl["target"]).to(dev)
+    copies = [tgt0] + [tgt0.clone() for _ in range(max(args.copies, 1) - 1)]
+    draft = None
+    if wl.get("draft") is not None:
+        d0 = torch.from_numpy(wl["draft"]).to(dev)
+        draft = [d0] + [d0.clone() for _ in range(max(args.copies, 1) - 1)]
+    tokens = torch.from_numpy(wl["draft_tokens"]).to(dev)
+    out_tok = torch.empty((B, tokens.shape[1] if mode == "tree" else K + 1), dtype=torch.int32, device=dev)
+    out_len = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    if mode == "sample":
+        temp = torch.from_numpy(wl["temperature"]).to(dev)
+        seeds = torch.from_numpy(wl["seeds"].view(np.int64)).to(dev)
+        out_p = torch.empty((B, K), dtype=torch.float32, device=dev)
+        out_q = torch.empty((B, K), dtype=torch.float32, device=dev)
+        ws_bytes = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, B, K, V, draft is not None)
+    elif mode == "greedy":
+        out_g = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        ws_bytes = sv.spec_verify_workspace_size(sv.SV_OP_GREEDY, B, K, V)
+    else:
+        N = len(wl["parents"])
+        parents = (ctypes.c_int32 * N)(*[int(v) for v in wl["parents"]])
+        out_best = torch.empty(B, dtype=torch.int32, device=dev)
+        ws_bytes = sv.spec_verify_workspace_size(sv.SV_OP_TREE, B, N, V)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    sv.spec_verify_workspace_init(ws)
+
+    descs = [sv._desc(t, "target") for t in copies]
+    ddescs = [sv._desc(t, "draft") for t in draft] if draft is not None else None
+
+    def step(i):
+        c = i % len(copies)
+        if mode == "sample":
+            rc = lib.spec_verify_sample(ctypes.byref(descs[c]),
+                                        ctypes.byref(ddescs[c]) if ddescs else None,
+                                        tokens.data_ptr(), temp.data_ptr(), seeds.data_ptr(), i, B, K, V,
+                                        out_tok.data_ptr(), out_len.data_ptr(), out_p.data_ptr(),
+                                        out_q.data_ptr(), ws.data_ptr(), ws_bytes, stream)
+        elif mode == "greedy":
+            rc = lib.spec_verify_greedy(ctypes.byref(descs[c]), tokens.data_ptr(), B, K, V,
+                                        out_tok.data_ptr(), out_len.data_ptr(), out_g.data_ptr(),
+                                        ws.data_ptr(), ws_bytes, stream)
+        else:
+            rc = lib.spec_verify_tree(ctypes.byref(descs[c]), tokens.data_ptr(),
+                                      ctypes.cast(parents, ctypes.c_void_p), N, B, V,
+                                      out_tok.data_ptr(), out_len.data_ptr(), out_best.data_ptr(),
+                                      ws.data_ptr(), ws_bytes, stream)
+        if rc:
+            raise sv.SpecVerifyError(rc, "bench step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, per-launch event pairs on the launch stream.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    region0.record()
+    for i in range(args.steps):
+        starts[i].record()
+        step(args.warmup + i)
+        ends[i].record()
+    region1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    per_launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    mean_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+    region_ms = region0.elapsed_time(region1)
+    ms_per_step = region_ms / args.steps
+    nbytes = algorithmic_bytes(wl)
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
+    accept = out_len.cpu().numpy()
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "mode": mode, "B": B, "K": K, "V": V,
+                   "logits_dtype": wl["dtype"], "draft": "explicit" if draft is not None else
+                   ("one-hot" if mode == "sample" else "tokens"),
+                   "temperature": None if wl["temperature"] is None else float(wl["temperature"][0]),
+                   "algorithmic_bytes_per_step": nbytes, "input_copies": len(copies)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_record(wl["name"]),
+                     "kernel": "sv_rows_kernel" if not (mode == "sample" and draft is not None)
+                     else "whole step (row pass + residual pass)",
+                     "launch_us_mean": round(mean_launch_ms * 1e3, 2),
+                     "launch_us_p10": round(per_launch_ms[len(per_launch_ms) // 10] * 1e3, 2),
+                     "launch_us_p90": round(per_launch_ms[(9 * len(per_launch_ms)) // 10] * 1e3, 2)},
+        "accept_len_hist": np.bincount(accept, minlength=(K + 2) if mode != "tree" else 5).tolist(),
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

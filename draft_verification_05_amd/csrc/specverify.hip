@@ -1,31 +1,34 @@
 // gfx950 kernels and host entry points of the speculative-decoding verifier.
 //
 // Design (one GPU, one stream, no host synchronisation):
-//   row pass   one workgroup per (request, row, segment of V). It streams its
-//              segment once with 128-bit loads and writes a partial: the
-//              online-softmax pair (max, sum of 2^(y - max)) with
-//              y = logit * log2(e) / T for sampling, or (max, argmax) for
-//              greedy/tree. The last workgroup of a request (per-request
-//              atomic ticket) merges the partials and runs that request's
-//              tail: Philox uniforms, the acceptance scan, and the draw.
-//   draw       the draw needs only the partials plus ONE re-read segment:
-//              the segment sums locate the segment that holds u * Z, and a
-//              workgroup scan inside it finds the token. With one-hot
-//              drafts the row pass already leaves the draft token out of
-//              its row's sums, so the residual max(0, p - onehot) costs no
-//              extra pass.
+//   row pass   the logits of every (request, row) are cut into 4 KiB chunks
+//              (2048 bf16 or 1024 fp32 logits). A workgroup owns a run of
+//              chunks of one row; each of its four waves streams chunks
+//              with 128-bit loads, the next chunk always in flight while
+//              the current one is reduced, and writes one partial per
+//              chunk: the online-softmax pair (max, sum of 2^(y - max))
+//              with y = logit * log2(e) / T for sampling, or (max, argmax)
+//              for greedy/tree. It also keeps the logit of each row's draft
+//              token.
+//   tail       one workgroup per request merges that request's partials
+//              and runs the rule: Philox uniforms, the acceptance scan and
+//              the draw. The launch boundary is the only synchronisation
+//              between the two.
+//   draw       the chunk sums locate the chunk that holds u * Z, and one
+//              workgroup scan over that single re-read chunk finds the
+//              token. With one-hot drafts the row pass already leaves the
+//              draft token out of its row's sums, so the residual
+//              max(0, p - onehot) costs no extra pass.
 //   residual   (explicit draft logits only) the residual max(0, p_a - q_a)
-//   pass       needs the normalisers of both rows, so a second launch
-//              streams the stop rows of the rejected requests in segments
-//              and its last workgroup per request draws the token.
-// The rule follows "【大模型基础设施工程】15：推测解码与 MTP" §2.1 (accept x_i
-// with probability min(1, p_i(x_i)/q_i(x_i)); on the first rejection draw
-// from the normalised max(0, p_i - q_i) and stop; bonus from the last
-// row when all are accepted), §3.3 (tree) and §11 (greedy).
+//   pass       needs the normalisers of both rows, so a third launch
+//              streams the stop rows of the rejected requests in chunks;
+//              the last of its workgroups per request (a per-request
+//              ticket) draws the token.
 #include <hip/hip_runtime.h>
 
 #include <climits>
 #include <cstdint>
+#include <cstdlib>
 
 #include "specverify.h"
 #include "sv_device.hpp"
@@ -35,13 +38,8 @@ namespace sv {
 enum Mode { kOneHot = 0, kExplicit = 1, kGreedy = 2, kTree = 3 };
 
 constexpr int kMaxRows = 2 * SV_MAX_DRAFT + 1;
+constexpr int kMaxChunksPerWg = 256;
 constexpr size_t kCounterBytes = 4u * SV_MAX_BATCH;
-constexpr int kSegMin = 2048;             // smallest segment any dtype uses
-
-// Loads per thread per segment: 4 x 16 B for bf16 (8192 logits), 8 x 16 B
-// for fp32 (8192 logits): 16 / 32 KiB per workgroup.
-constexpr int kUBf16 = 4;
-constexpr int kUF32 = 8;
 
 // Hand-off from the row pass to the residual pass (explicit draft logits).
 struct Record {
@@ -63,27 +61,28 @@ struct Args {
   int B, K, V;
   int R;          // target rows per request
   int rows;       // rows per request in the row pass (target + draft)
-  int n_seg;      // segments per row
+  int n_chunk;    // chunks per row
+  int cpw;        // chunks per workgroup
+  int wpr;        // workgroups per row
   int out_cols;   // row length of out_tokens
   int32_t* out_tokens; int32_t* out_len; float* out_p; float* out_q; int32_t* out_aux;
   unsigned* counters;   // [B], zero between calls
-  float2* part;         // [B * rows * n_seg]
+  float2* part;         // [B * rows * n_chunk]
+  int n_full;           // chunks per row that lie entirely below V
+  float* gath;          // [B * rows]: logit of the row's draft token
   Record* rec;          // [B]
-  float* res_part;      // [B * n_seg]
+  float* res_part;      // [B * n_chunk]
   int n_nodes;
   int8_t parent[SV_MAX_TREE_NODES];
 };
 
+// The tail keeps a request's partials in LDS when they fit, so the draw
+// can locate its chunk without another trip to memory.
+constexpr int kPartCache = 1024;
+
 struct TailLds {
-  float red[kWaves];
-  float red2[kWaves];
-  int red_i[kWaves];
-  int imin, imax, a, found;
-  float tin;
+  float2 pcache[kPartCache];
   float rowM[kMaxRows], rowS[kMaxRows];
-  float selM[SV_MAX_DRAFT + 1], selZ[SV_MAX_DRAFT + 1];
-  float p[SV_MAX_DRAFT + 1], q[SV_MAX_DRAFT + 1];
-  float uacc[SV_MAX_DRAFT + 1], usmp[SV_MAX_DRAFT + 1];
   int x[SV_MAX_TREE_NODES], g[SV_MAX_TREE_NODES], path[SV_MAX_TREE_NODES];
   int depth[SV_MAX_TREE_NODES];
 };
@@ -93,260 +92,326 @@ __device__ inline const char* row_ptr(const Args& A, int b, int r) {
                  : A.drf + (int64_t)b * A.d_sb + (int64_t)(r - A.R) * A.d_sk;
 }
 
+// ------------------------------------------------ in-launch hand-off ---
+// In the residual pass the workgroups of one request meet through the
+// workspace inside a single launch. The L2 of each XCD is not coherent with the others, and an
+// agent-scope fence writes back and invalidates a whole L2 per workgroup.
+// Instead every hand-off value is written and read with device-coherent
+// (relaxed agent-scope atomic, sc1) accesses that bypass the non-coherent
+// cache levels; a vmcnt(0) wait makes each wave's publishes complete
+// before its workgroup takes the ticket, and the ticket is a device atomic.
+__device__ inline void publish(float2* p, float2 v) {
+  const uint64_t bits = ((uint64_t)__float_as_uint(v.y) << 32) | __float_as_uint(v.x);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline float2 fetch(const float2* p) {
+  const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)bits), __uint_as_float((uint32_t)(bits >> 32)));
+}
+
+__device__ inline float fetch(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every wave waits for its own publishes, then thread 0 takes the ticket:
+// the count before its increment. Exactly one of the n workgroups of a
+// request sees n - 1; it runs the tail and resets the counter.
+__device__ inline bool last_of_request(unsigned* counter, unsigned n, int* s_last) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = (prev == n - 1);
+    if (prev == n - 1) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *s_last != 0;
+}
+
 // ------------------------------------------------------------ drawing ---
-// Which segment holds the draw: Z = sum_s W(s), t = u * Z, first s whose
-// running sum exceeds t. Leaves S.found = segment (or the last segment of
-// positive weight when rounding leaves none, with S.tin = +inf) and
-// S.tin = t minus the weight before it. Returns Z.
+// Every draw is done by one wave: the tail of a request is short and runs
+// once per request per call, so it is kept small and free of workgroup
+// barriers.
+
+// Chunk holding the draw among n chunk weights W(s): Z = sum of all, t =
+// u * Z, first s whose running sum exceeds t (only chunks of positive
+// weight qualify). Returns Z; *found = that chunk (or the last chunk of
+// positive weight when rounding leaves none, with *t_in = +inf; -1 if no
+// weight at all) and *t_in = t minus the weight before it.
 template <class WFn>
-__device__ float locate_segment(int n_seg, float u, WFn W, TailLds& S) {
-  const int tid = threadIdx.x;
+__device__ float wave_locate(int n, float u, WFn W, int* found, float* t_in) {
+  const int lane = threadIdx.x & 63;
   float Z = 0.f;
-  for (int base = 0; base < n_seg; base += kThreads) {
-    const int s = base + tid;
-    Z += block_sum(s < n_seg ? W(s) : 0.f, S.red);
+  for (int base = 0; base < n; base += 64) {
+    const int s = base + lane;
+    Z += wave_sum_all(s < n ? W(s) : 0.f);
   }
   const float t = u * Z;
-  if (tid == 0) { S.imin = INT_MAX; S.imax = -1; }
-  __syncthreads();
   float carry = 0.f;
-  for (int base = 0; base < n_seg; base += kThreads) {
-    const int s = base + tid;
-    const float w = s < n_seg ? W(s) : 0.f;
-    float tot;
-    const float incl = carry + block_incl_scan(w, S.red, tot);
-    if (s < n_seg && incl > t && w > 0.f) atomicMin(&S.imin, s);
-    if (s < n_seg && w > 0.f) atomicMax(&S.imax, s);
-    __syncthreads();
-    const int hit = S.imin;
-    if (hit != INT_MAX) {
-      if (s == hit) S.tin = t - (incl - w);
-      break;
+  int last = -1;
+  for (int base = 0; base < n; base += 64) {
+    const int s = base + lane;
+    const float w = s < n ? W(s) : 0.f;
+    const float incl = carry + wave_scan_incl(w);
+    const int hit = first_lane(s < n && incl > t && w > 0.f);
+    if (hit >= 0) {
+      *found = base + hit;
+      *t_in = t - lane_f(incl - w, hit);
+      return Z;
     }
-    carry += tot;
+    const int lp = last_lane(w > 0.f);
+    if (lp >= 0) last = base + lp;
+    carry = lane_f(incl, 63);
   }
-  __syncthreads();
-  if (tid == 0) {
-    if (S.imin != INT_MAX) {
-      S.found = S.imin;
-    } else {
-      S.found = S.imax;                 // rounding overshoot: last positive segment
-      S.tin = __builtin_inff();
-    }
-  }
-  __syncthreads();
+  *found = last;
+  *t_in = __builtin_inff();
   return Z;
 }
 
-// Inside one segment: the smallest element whose running weight sum
-// exceeds t_in, scanning vectors in index order (vector j of thread t is
-// the (j * kThreads + t)-th of the segment); the last element of positive
-// weight if rounding leaves none.
-template <int kPer, int U>
-__device__ int pick_in_segment(const float (&w)[U * kPer], int64_t seg0, float t_in, TailLds& S) {
-  const int tid = threadIdx.x;
-  if (tid == 0) { S.imin = INT_MAX; S.imax = -1; }
-  __syncthreads();
-  float carry = 0.f;
-  for (int j = 0; j < U; ++j) {
-    float vs = 0.f;
+// Inside one chunk whose lane l holds the E weights of logits
+// c0 + l * E ... + E - 1: the smallest logit whose running weight sum
+// exceeds t_in, else the last logit of positive weight, else -1.
+template <int E>
+__device__ int wave_pick(const float (&w)[E], int64_t c0, float t_in) {
+  const int lane = threadIdx.x & 63;
+  float vs = 0.f;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) vs += w[j * kPer + k];
-    float tot;
-    const float incl = carry + block_incl_scan(vs, S.red, tot);
-    const int e0 = (int)(seg0 + (int64_t)(j * kThreads + tid) * kPer);
-    if (incl > t_in) {
-      float run = incl - vs;
-      int hit = -1;
+  for (int k = 0; k < E; ++k) vs += w[k];
+  float run = wave_scan_incl(vs) - vs;
+  int hit = -1, last = -1;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        run += w[j * kPer + k];
-        if (hit < 0 && run > t_in && w[j * kPer + k] > 0.f) hit = k;
-      }
-      if (hit >= 0) atomicMin(&S.imin, e0 + hit);
-    }
-    int last = -1;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      if (w[j * kPer + k] > 0.f) last = e0 + k;
-    if (last >= 0) atomicMax(&S.imax, last);
-    __syncthreads();
-    if (S.imin != INT_MAX) break;
-    carry += tot;
+  for (int k = 0; k < E; ++k) {
+    run += w[k];
+    if (hit < 0 && run > t_in && w[k] > 0.f) hit = k;
+    if (w[k] > 0.f) last = k;
   }
-  __syncthreads();
-  const int y = S.imin != INT_MAX ? S.imin : S.imax;
-  __syncthreads();
-  return y;
+  const int lh = first_lane(hit >= 0);
+  if (lh >= 0) return (int)(c0 + (int64_t)lh * E + lane_i(hit, lh));
+  const int ll = last_lane(last >= 0);
+  if (ll >= 0) return (int)(c0 + (int64_t)ll * E + lane_i(last, ll));
+  return -1;
+}
+
+// Lane l's E consecutive logits c0 + l * E ... of one chunk (-inf past V).
+template <int DT, bool kVec, int E>
+__device__ __forceinline__ void load_lane_run(const char* row, int64_t c0, int V, float (&x)[E]) {
+  constexpr int kPer = Elem<DT>::kPerVec;
+  const int64_t e0 = c0 + (int64_t)(threadIdx.x & 63) * E;
+  if (kVec && e0 + E <= V) {
+#pragma unroll
+    for (int j = 0; j < E / kPer; ++j) load_vec16<DT>(row + (e0 + j * kPer) * Elem<DT>::kBytes, &x[j * kPer]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < E; ++k) x[k] = (e0 + k < V) ? load_one<DT>(row, e0 + k) : kNegInf;
+  }
+}
+
+// Partial (row rr of request b, chunk s), written by the row pass: from
+// the tail's LDS copy when the request's partials fit there, else from the
+// workspace.
+__device__ inline float2 partial(const Args& A, int b, int rr, int s, const TailLds& S, bool cached) {
+  return cached ? S.pcache[rr * A.n_chunk + s]
+                : A.part[((int64_t)b * A.rows + rr) * A.n_chunk + s];
 }
 
 // Draw from one row's softmax weights 2^(y - M) (optionally without token
 // `xe`) using that row's row-pass partials; used for the one-hot residual
 // and the bonus token. Returns -1 when the weights have no mass.
-template <int DT, int U, bool kVec>
+template <int DT, bool kVec>
 __device__ int draw_softmax_row(const Args& A, int b, int r, float c, float M, int xe, float u,
-                                TailLds& S) {
-  constexpr int kPer = Elem<DT>::kPerVec, kLen = kThreads * U * kPer;
-  const float2* pr = A.part + ((int64_t)b * A.rows + r) * A.n_seg;
+                                const TailLds& S, bool cached) {
+  constexpr int E = Chunk<DT>::kElems / 64;
   auto W = [&](int s) {
-    const float2 v = pr[s];
+    const float2 v = partial(A, b, r, s, S, cached);
     return v.x == kNegInf ? 0.f : v.y * fast_exp2(v.x - M);
   };
-  const float Z = locate_segment(A.n_seg, u, W, S);
-  if (!(Z > 0.f) || S.found < 0) return -1;
-  const int seg = S.found;
-  const float t_in = S.tin;
-  const int64_t seg0 = (int64_t)seg * kLen;
-  float x[U * kPer];
-  load_segment<DT, U, kVec>(row_ptr(A, b, r), seg0, A.V, x);
-  float w[U * kPer];
+  int found;
+  float t_in;
+  const float Z = wave_locate(A.n_chunk, u, W, &found, &t_in);
+  if (!(Z > 0.f) || found < 0) return -1;
+  const int64_t c0 = (int64_t)found * Chunk<DT>::kElems;
+  float x[E], w[E];
+  load_lane_run<DT, kVec, E>(row_ptr(A, b, r), c0, A.V, x);
+  const int64_t e0 = c0 + (int64_t)(threadIdx.x & 63) * E;
 #pragma unroll
-  for (int j = 0; j < U; ++j) {
-    const int64_t e0 = seg0 + (int64_t)(j * kThreads + threadIdx.x) * kPer;
+  for (int k = 0; k < E; ++k) {
+    const float v = fast_exp2(fmaf(x[k], c, -M));
+    w[k] = (e0 + k == xe) ? 0.f : v;
+  }
+  return wave_pick<E>(w, c0, t_in);
+}
+
+// Copies a request's n partials to LDS (one round of loads) when they fit.
+__device__ bool stage_partials(const Args& A, int b, TailLds& S) {
+  const int lane = threadIdx.x & 63;
+  const int n = A.rows * A.n_chunk;
+  if (n > kPartCache) return false;
+  const float2* pb = A.part + (int64_t)b * n;
+  for (int base = 0; base < n; base += 8 * 64) {
+    float2 t[8];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const float v = fast_exp2(fmaf(x[j * kPer + k], c, -M));
-      w[j * kPer + k] = (e0 + k == xe) ? 0.f : v;
+    for (int q = 0; q < 8; ++q) {
+      const int i = base + q * 64 + lane;
+      t[q] = i < n ? pb[i] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int i = base + q * 64 + lane;
+      if (i < n) S.pcache[i] = t[q];
     }
   }
-  return pick_in_segment<kPer, U>(w, seg0, t_in, S);
+  __syncthreads();
+  return true;
+}
+
+// Per-row (max, sum) of a request's partials into S.rowM / S.rowS.
+__device__ void merge_softmax_rows(const Args& A, int b, TailLds& S, bool cached) {
+  const int lane = threadIdx.x & 63;
+  for (int rr = 0; rr < A.rows; ++rr) {
+    float m = kNegInf, s = 0.f;
+    for (int sg = lane; sg < A.n_chunk; sg += 64) {
+      const float2 v = partial(A, b, rr, sg, S, cached);
+      ms_merge(m, s, v.x, v.y);
+    }
+    const float wm = wave_max_all(m);
+    s = (m == kNegInf) ? 0.f : s * fast_exp2(m - wm);
+    s = wave_sum_all(s);
+    if (lane == 0) { S.rowM[rr] = wm; S.rowS[rr] = s; }
+  }
+  __syncthreads();
+}
+
+// Per-row argmax of a request's partials into S.g.
+__device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, bool cached) {
+  const int lane = threadIdx.x & 63;
+  for (int rr = 0; rr < n_rows; ++rr) {
+    float v = kNegInf;
+    int idx = INT_MAX;
+    for (int sg = lane; sg < A.n_chunk; sg += 64) {
+      const float2 t = partial(A, b, rr, sg, S, cached);
+      am_step(v, idx, t.x, __float_as_int(t.y));
+    }
+    wave_argmax_all(v, idx);
+    if (lane == 0) S.g[rr] = idx;
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------- row tails ---
-template <int DT, int U, bool kVec, int MODE>
+// One wave per request.
+template <int DT, bool kVec, int MODE>
 __device__ void sample_tail(const Args& A, int b, TailLds& S) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
   const int K = A.K, V = A.V, R = A.R;
-  for (int rr = wave; rr < A.rows; rr += kWaves) {
-    float m = kNegInf, s = 0.f;
-    const float2* pr = A.part + ((int64_t)b * A.rows + rr) * A.n_seg;
-    for (int sg = lane; sg < A.n_seg; sg += 64) {
-      const float2 v = pr[sg];
-      ms_merge(m, s, v.x, v.y);
-    }
-    wave_reduce_ms(m, s);
-    if (lane == 0) { S.rowM[rr] = m; S.rowS[rr] = s; }
+  const int64_t rowg0 = (int64_t)b * A.rows;
+  // independent loads first: draft tokens, gathered logits, partials
+  int x = -1;
+  float lx = kNegInf, ld = kNegInf;
+  if (lane < K) {
+    x = A.tokens[(int64_t)b * K + lane];
+    lx = A.gath[rowg0 + lane];
+    if (MODE == kExplicit) ld = A.gath[rowg0 + R + lane];
   }
   const float T = A.temperature[b];
-  const bool ok = T > 0.f && T < __builtin_inff();
-  const float c = kLog2e / T;
+  const uint64_t seed = A.seeds[b];
+  const bool cached = stage_partials(A, b, S);
+  float uacc = 0.f, usmp = 0.f;
+  if (lane <= K) {
+    const Philox4 rnd = philox4x64_10((uint64_t)lane, (uint64_t)b, A.offset, 0ull, seed, 0ull);
+    uacc = top24(rnd.w0);
+    usmp = top24(rnd.w1);
+  }
+  merge_softmax_rows(A, b, S, cached);
   int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
-  __syncthreads();
-  if (!ok) {                                  // refused request
-    if (tid <= K) otok[tid] = -1;
-    if (tid < K && A.out_p) A.out_p[(int64_t)b * K + tid] = 0.f;
-    if (tid < K && A.out_q) A.out_q[(int64_t)b * K + tid] = 0.f;
-    if (tid == 0) {
+  if (!(T > 0.f && T < __builtin_inff())) {      // refused request
+    if (lane <= K) otok[lane] = -1;
+    if (lane < K && A.out_p) A.out_p[(int64_t)b * K + lane] = 0.f;
+    if (lane < K && A.out_q) A.out_q[(int64_t)b * K + lane] = 0.f;
+    if (lane == 0) {
       A.out_len[b] = 0;
       if (MODE == kExplicit) A.rec[b].pending = 0;
     }
     return;
   }
-  if (tid <= K) {
-    const int i = tid;
-    const Philox4 rnd = philox4x64_10((uint64_t)i, (uint64_t)b, A.offset, 0ull, A.seeds[b], 0ull);
-    S.uacc[i] = top24(rnd.w0);
-    S.usmp[i] = top24(rnd.w1);
-    if (i < K) {
-      const int x = A.tokens[(int64_t)b * K + i];
-      S.x[i] = x;
-      const bool valid = (unsigned)x < (unsigned)V;
-      const float lx = valid ? load_one<DT>(row_ptr(A, b, i), x) : kNegInf;
-      float p, q;
-      if (MODE == kOneHot) {
-        // row-pass sums of row i leave x out: add its own term back for p(x)
-        const float Mi = S.rowM[i], Si = S.rowS[i];
-        const float Mn = fmaxf(Mi, lx * c);
-        const float Sx = (Mi == kNegInf) ? 0.f : Si * fast_exp2(Mi - Mn);
-        const float e = (valid && Mn != kNegInf) ? fast_exp2(fmaf(lx, c, -Mn)) : 0.f;
-        const float St = Sx + e;
-        p = St > 0.f ? e / St : 0.f;
-        q = valid ? 1.f : 0.f;
-        S.selM[i] = Mn;
-        S.selZ[i] = Sx;
-      } else {
-        const float Mp = S.rowM[i], Sp = S.rowS[i];
-        const float Mq = S.rowM[R + i], Sq = S.rowS[R + i];
-        const float ld = valid ? load_one<DT>(row_ptr(A, b, R + i), x) : kNegInf;
-        p = (valid && Sp > 0.f) ? fast_exp2(fmaf(lx, c, -Mp)) / Sp : 0.f;
-        q = (valid && Sq > 0.f) ? fast_exp2(fmaf(ld, c, -Mq)) / Sq : 0.f;
-      }
-      S.p[i] = p;
-      S.q[i] = q;
-      if (A.out_p) A.out_p[(int64_t)b * K + i] = p;
-      if (A.out_q) A.out_q[(int64_t)b * K + i] = q;
+  const float c = kLog2e / T;
+  float p = 0.f, q = 0.f, Mx = kNegInf;
+  if (lane < K) {
+    const bool valid = (unsigned)x < (unsigned)V;
+    if (!valid) { lx = kNegInf; ld = kNegInf; }
+    if (MODE == kOneHot) {
+      // row `lane`'s sums leave x out: add its own term back for p(x)
+      const float Mi = S.rowM[lane], Si = S.rowS[lane];
+      Mx = fmaxf(Mi, lx * c);
+      const float Sx = (Mi == kNegInf) ? 0.f : Si * fast_exp2(Mi - Mx);
+      const float e = (valid && Mx != kNegInf) ? fast_exp2(fmaf(lx, c, -Mx)) : 0.f;
+      const float St = Sx + e;
+      p = St > 0.f ? e / St : 0.f;
+      q = valid ? 1.f : 0.f;
+    } else {
+      const float Mp = S.rowM[lane], Sp = S.rowS[lane];
+      const float Mq = S.rowM[R + lane], Sq = S.rowS[R + lane];
+      p = (valid && Sp > 0.f) ? fast_exp2(fmaf(lx, c, -Mp)) / Sp : 0.f;
+      q = (valid && Sq > 0.f) ? fast_exp2(fmaf(ld, c, -Mq)) / Sq : 0.f;
     }
+    if (A.out_p) A.out_p[(int64_t)b * K + lane] = p;
+    if (A.out_q) A.out_q[(int64_t)b * K + lane] = q;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int a = 0;
-    while (a < K && S.uacc[a] * S.q[a] < S.p[a]) ++a;
-    S.a = a;
-  }
-  __syncthreads();
-  const int a = S.a;
-  if (tid <= K && tid != a) otok[tid] = tid < a ? S.x[tid] : -1;
-  if (tid == 0) A.out_len[b] = a + 1;
+  // the first position whose draft is rejected, K if none
+  const int rej = first_lane(lane < K && !(uacc * q < p));
+  const int a = rej < 0 ? K : rej;
+  if (lane <= K && lane != a) otok[lane] = lane < a ? x : -1;
+  if (lane == 0) A.out_len[b] = a + 1;
+  const float ua = lane_f(usmp, a);
   if (MODE == kExplicit) {
     if (a < K) {
-      if (tid == 0) {
+      if (lane == 0) {
         Record rc;
-        rc.a = a; rc.pending = 1; rc.c = c; rc.u = S.usmp[a];
+        rc.a = a; rc.pending = 1; rc.c = c; rc.u = ua;
         rc.Mp = S.rowM[a]; rc.Sp = S.rowS[a]; rc.Mq = S.rowM[R + a]; rc.Sq = S.rowS[R + a];
         A.rec[b] = rc;
       }
       return;
     }
-    if (tid == 0) A.rec[b].pending = 0;
+    if (lane == 0) A.rec[b].pending = 0;
   }
   const bool resid = (MODE == kOneHot && a < K);
-  const float M = resid ? S.selM[a] : S.rowM[a];
-  const int xe = resid ? S.x[a] : -1;
-  int y = draw_softmax_row<DT, U, kVec>(A, b, a, c, M, xe, S.usmp[a], S);
+  const float M = resid ? lane_f(Mx, a) : S.rowM[a];
+  const int xe = resid ? lane_i(x, a) : -1;
+  int y = draw_softmax_row<DT, kVec>(A, b, a, c, M, xe, ua, S, cached);
   if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
-  if (tid == 0) otok[a] = y;
-}
-
-__device__ inline void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int rr = wave; rr < n_rows; rr += kWaves) {
-    float v = kNegInf;
-    int idx = INT_MAX;
-    const float2* pr = A.part + ((int64_t)b * A.rows + rr) * A.n_seg;
-    for (int sg = lane; sg < A.n_seg; sg += 64) {
-      const float2 t = pr[sg];
-      am_merge(v, idx, t.x, __float_as_int(t.y));
-    }
-    wave_reduce_am(v, idx);
-    if (lane == 0) S.g[rr] = idx;
-  }
+  if (lane == 0) otok[a] = y;
 }
 
 __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
-  const int tid = threadIdx.x, K = A.K;
-  merge_argmax_rows(A, b, A.rows, S);
-  if (tid < K) S.x[tid] = A.tokens[(int64_t)b * K + tid];
-  __syncthreads();
-  if (tid == 0) {
-    int a = 0;
-    while (a < K && S.x[a] == S.g[a]) ++a;
-    S.a = a;
-    A.out_len[b] = a + 1;
+  const int lane = threadIdx.x & 63, K = A.K;
+  const int x = lane < K ? A.tokens[(int64_t)b * K + lane] : -1;
+  const bool cached = stage_partials(A, b, S);
+  merge_argmax_rows(A, b, A.rows, S, cached);
+  const int g = lane <= K ? S.g[lane] : -1;
+  const int mis = first_lane(lane < K && x != g);
+  const int a = mis < 0 ? K : mis;
+  if (lane <= K) {
+    A.out_tokens[(int64_t)b * A.out_cols + lane] = lane < a ? x : (lane == a ? g : -1);
+    if (A.out_aux) A.out_aux[(int64_t)b * (K + 1) + lane] = g;
   }
-  __syncthreads();
-  const int a = S.a;
-  if (tid <= K) {
-    A.out_tokens[(int64_t)b * A.out_cols + tid] = tid < a ? S.x[tid] : (tid == a ? S.g[a] : -1);
-    if (A.out_aux) A.out_aux[(int64_t)b * (K + 1) + tid] = S.g[tid];
-  }
+  if (lane == 0) A.out_len[b] = a + 1;
 }
 
 __device__ void tree_tail(const Args& A, int b, TailLds& S) {
-  const int tid = threadIdx.x, N = A.n_nodes;
-  merge_argmax_rows(A, b, N, S);
-  if (tid < N) S.x[tid] = A.tokens[(int64_t)b * N + tid];
-  __syncthreads();
-  if (tid == 0) {
+  const int lane = threadIdx.x & 63, N = A.n_nodes;
+  if (lane < N) S.x[lane] = A.tokens[(int64_t)b * N + lane];
+  const bool cached = stage_partials(A, b, S);
+  merge_argmax_rows(A, b, N, S, cached);
+  if (lane == 0) {
     uint64_t acc = 1ull;
     int best = 0;
     S.depth[0] = 0;
@@ -365,98 +430,213 @@ __device__ void tree_tail(const Args& A, int b, TailLds& S) {
       n = A.parent[n];
     }
     S.path[len] = S.g[best];
-    S.a = len;
+    S.depth[SV_MAX_TREE_NODES - 1] = len;       // hand the length to the other lanes
     A.out_len[b] = len + 1;
     if (A.out_aux) A.out_aux[b] = best;
   }
   __syncthreads();
-  if (tid < N) A.out_tokens[(int64_t)b * A.out_cols + tid] = tid <= S.a ? S.path[tid] : -1;
+  const int len = S.depth[SV_MAX_TREE_NODES - 1];
+  if (lane < N) A.out_tokens[(int64_t)b * A.out_cols + lane] = lane <= len ? S.path[lane] : -1;
 }
 
 // ------------------------------------------------------------ row pass ---
-template <int MODE, int DT, int U, bool kVec>
-__global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
-  constexpr int kPer = Elem<DT>::kPerVec, kLen = kThreads * U * kPer;
-  __shared__ TailLds S;
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int seg = (int)(blockIdx.x % (unsigned)A.n_seg);
-  const int rowg = (int)(blockIdx.x / (unsigned)A.n_seg);
-  const int b = rowg / A.rows, r = rowg % A.rows;
-  const int64_t seg0 = (int64_t)seg * kLen;
+// Logit (j, k) of a lane's chunk: word k / kPerWord of vector j, widened.
+template <int DT>
+__device__ __forceinline__ uint32_t& raw_word(ChunkRaw& r, int j, int w) {
+  return w == 0 ? r.v[j].x : w == 1 ? r.v[j].y : w == 2 ? r.v[j].z : r.v[j].w;
+}
+template <int DT>
+__device__ __forceinline__ float raw_elem(ChunkRaw& r, int j, int k) {
+  if constexpr (DT == kF32) {
+    return __uint_as_float(raw_word<DT>(r, j, k));
+  } else {
+    const uint32_t w = raw_word<DT>(r, j, k >> 1);
+    return (k & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+}
+// Sets logit (j, k) to -inf when `hit`.
+template <int DT>
+__device__ __forceinline__ void raw_mask(ChunkRaw& r, int j, int k, bool hit) {
+  if constexpr (DT == kF32) {
+    uint32_t& w = raw_word<DT>(r, j, k);
+    w = hit ? 0xFF800000u : w;
+  } else {
+    uint32_t& w = raw_word<DT>(r, j, k >> 1);
+    const uint32_t masked = (k & 1) ? ((w & 0x0000FFFFu) | 0xFF800000u) : ((w & 0xFFFF0000u) | 0xFF80u);
+    w = hit ? masked : w;
+  }
+}
+// Opaque to the optimiser: the second pass over a chunk re-widens the
+// packed words instead of keeping every widened logit live across passes.
+__device__ __forceinline__ void touch(ChunkRaw& r) {
+#pragma unroll
+  for (int j = 0; j < kLoadsPerLane; ++j)
+    asm volatile("" : "+v"(r.v[j].x), "+v"(r.v[j].y), "+v"(r.v[j].z), "+v"(r.v[j].w));
+}
 
-  float x[U * kPer];
-  load_segment<DT, U, kVec>(row_ptr(A, b, r), seg0, A.V, x);
-
-  float2 res;
+// One chunk's partial from one wave: (max y, sum 2^(y - max)) for sampling,
+// (max logit, lowest index of it) for greedy/tree. With a draft token xe in
+// this chunk, its logit goes to `gath` and, for one-hot drafts, it is left
+// out of the sums. `r` holds the lane's four 16-byte vectors.
+template <int MODE, int DT>
+__device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, int c0, int xe, float c, float* gath) {
+  constexpr int kPer = Elem<DT>::kPerVec;
+  const int lane0 = (threadIdx.x & 63) * kPer;   // first logit of the lane's vector 0
   if constexpr (MODE == kOneHot || MODE == kExplicit) {
-    if (MODE == kOneHot && r < A.K) {
-      // one-hot residual: this row's sums leave the draft token out
-      const int xe = A.tokens[(int64_t)b * A.K + r];
+    const int dx = xe - c0;                       // the draft token's offset in this chunk
+    if (xe >= 0 && (unsigned)dx < (unsigned)Chunk<DT>::kElems) {
+      // only the wave holding the chunk with the token gets here (uniform
+      // branch). Vector, lane and 32-bit word of the token are uniform.
+      constexpr int kWordElems = kPer / 4;        // logits per 32-bit word
+      const int vec = dx / kPer;
+      const int jt = vec >> 6, lt = vec & 63;
+      const int wt = (dx % kPer) / kWordElems, half = (dx % kPer) % kWordElems;
+      const bool own = (threadIdx.x & 63) == lt;
+      uint32_t w = 0;
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int64_t d = (int64_t)xe - (seg0 + (int64_t)(j * kThreads + tid) * kPer);
-        if (d >= 0 && d < kPer) {
+      for (int j = 0; j < kLoadsPerLane; ++j)
 #pragma unroll
-          for (int k = 0; k < kPer; ++k)
-            if (k == d) x[j * kPer + k] = kNegInf;
-        }
+        for (int q = 0; q < 4; ++q) w = (j == jt && q == wt) ? raw_word<DT>(r, j, q) : w;
+      if (own) {
+        float lx;
+        if constexpr (DT == kF32) lx = __uint_as_float(w);
+        else lx = half ? bf16_hi(w) : bf16_lo(w);
+        *gath = lx;                               // once per row
+      }
+      if (MODE == kOneHot) {
+        uint32_t masked;
+        if constexpr (DT == kF32) masked = 0xFF800000u;
+        else masked = half ? ((w & 0x0000FFFFu) | 0xFF800000u) : ((w & 0xFFFF0000u) | 0xFF80u);
+#pragma unroll
+        for (int j = 0; j < kLoadsPerLane; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t& dst = raw_word<DT>(r, j, q);
+            dst = (own && j == jt && q == wt) ? masked : dst;
+          }
       }
     }
-    const float c = kLog2e / A.temperature[b];
+    touch(r);
+    // lane: sum of 2^(y - m_lane); wave: rescale each lane once to the
+    // wave's max and add.
     float mx = kNegInf;
 #pragma unroll
-    for (int e = 0; e < U * kPer; ++e) mx = fmaxf(mx, x[e]);
-    const float msub = (mx == kNegInf) ? 0.f : mx * c;
-    float acc[U];
+    for (int j = 0; j < kLoadsPerLane; ++j)
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
+      for (int k = 0; k < kPer; ++k) mx = fmaxf(mx, raw_elem<DT>(r, j, k));
+    touch(r);
+    const float msub = (mx == kNegInf) ? 0.f : mx * c;
+    float acc[kLoadsPerLane];
+#pragma unroll
+    for (int j = 0; j < kLoadsPerLane; ++j) {
       acc[j] = 0.f;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) acc[j] += fast_exp2(fmaf(x[j * kPer + k], c, -msub));
+      for (int k = 0; k < kPer; ++k) acc[j] += fast_exp2(fmaf(raw_elem<DT>(r, j, k), c, -msub));
     }
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < U; ++j) s += acc[j];
-    float m = (mx == kNegInf) ? kNegInf : msub;
-    wave_reduce_ms(m, s);
-    if (lane == 0) { S.red[wave] = m; S.red2[wave] = s; }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < kWaves; ++w) ms_merge(m, s, S.red[w], S.red2[w]);
-      res = make_float2(m, s);
-    }
+    float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const float wmx = wave_max_all(mx);
+    const float m = (wmx == kNegInf) ? kNegInf : wmx * c;
+    s = (mx == kNegInf) ? 0.f : s * fast_exp2(msub - m);
+    s = wave_sum_all(s);
+    return make_float2(m, s);
   } else {
-    float best = x[0];
-    int bi = (int)(seg0 + (int64_t)tid * kPer);
+    float best = raw_elem<DT>(r, 0, 0);
+    int bi = c0 + lane0;
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int e0 = (int)(seg0 + (int64_t)(j * kThreads + tid) * kPer);
+    for (int j = 0; j < kLoadsPerLane; ++j) {
 #pragma unroll
-      for (int k = 0; k < kPer; ++k)
-        if (x[j * kPer + k] > best) { best = x[j * kPer + k]; bi = e0 + k; }
+      for (int k = 0; k < kPer; ++k) {
+        const float v = raw_elem<DT>(r, j, k);
+        if (v > best) { best = v; bi = c0 + lane0 + j * 64 * kPer + k; }
+      }
     }
-    wave_reduce_am(best, bi);
-    if (lane == 0) { S.red[wave] = best; S.red_i[wave] = bi; }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < kWaves; ++w) am_merge(best, bi, S.red[w], S.red_i[w]);
-      res = make_float2(best, __int_as_float(bi));
-    }
+    wave_argmax_all(best, bi);
+    return make_float2(best, __int_as_float(bi));
+  }
+}
+
+// Workgroup w owns chunks [c_lo, c_hi) of row (w / wpr); wave v of it
+// streams chunks c_lo + v, c_lo + v + 4, ... Full chunks go through a
+// two-deep pipeline of raw 16-byte loads; a row's last, partial chunk and
+// rows that are not 16-byte aligned take the checked element path.
+template <int MODE, int DT, bool kVec>
+__global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
+  constexpr int kCE = Chunk<DT>::kElems;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
+  const int wi = (int)(blockIdx.x % (unsigned)A.wpr);
+  const int rowg = (int)(blockIdx.x / (unsigned)A.wpr);
+  const int b = rowg / A.rows, r = rowg % A.rows;
+  const char* row = row_ptr(A, b, r);
+  const int c_lo = wi * A.cpw;
+  const int c_hi = min(c_lo + A.cpw, A.n_chunk);
+  // Partials collect in LDS and leave in one store at the end: no global
+  // store sits between the chunk loads.
+  __shared__ float2 s_part[kMaxChunksPerWg];
+  float* gath = A.gath + rowg;
+
+  int ch = c_lo + wave;
+  const int ch_end = kVec ? min(c_hi, A.n_full) : c_lo;
+  const bool piped = ch < ch_end;
+  ChunkRaw ra, rb;
+  if (piped) issue_chunk<DT>(row, (int64_t)ch * kCE, ra);   // first loads before anything else
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The draft token of this row (if any): its logit is kept for the tail,
+  // and with one-hot drafts it is left out of the row's sums.
+  int xe = -1;
+  float c = 0.f;
+  if (MODE == kOneHot || MODE == kExplicit) {
+    const int i = r < A.R ? r : r - A.R;
+    if (i < A.K) xe = A.tokens[(int64_t)b * A.K + i];
+    c = kLog2e / A.temperature[b];
   }
 
-  if (tid == 0) {
-    A.part[(int64_t)rowg * A.n_seg + seg] = res;
-    __threadfence();                              // publish the partial ...
-    const unsigned prev = atomicAdd(&A.counters[b], 1u);   // ... then take a ticket
-    s_last = (prev == (unsigned)(A.rows * A.n_seg - 1));
+  if (piped) {
+    // The prefetch is unconditional so that every iteration has the same
+    // loads in flight (the waits stay exact); past the end it re-reads the
+    // current chunk, which the L2 still holds.
+    while (true) {
+      int nx = ch + kWaves;
+      bool more = nx < ch_end;
+      issue_chunk<DT>(row, (int64_t)(more ? nx : ch) * kCE, rb);
+      __builtin_amdgcn_sched_barrier(0);           // keep the prefetch ahead of the math
+      {
+        const float2 res = chunk_partial<MODE, DT>(ra, ch * kCE, xe, c, gath);
+        if (lane == 0) s_part[ch - c_lo] = res;
+      }
+      ch = nx;
+      if (!more) break;
+      nx = ch + kWaves;
+      more = nx < ch_end;
+      issue_chunk<DT>(row, (int64_t)(more ? nx : ch) * kCE, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const float2 res = chunk_partial<MODE, DT>(rb, ch * kCE, xe, c, gath);
+        if (lane == 0) s_part[ch - c_lo] = res;
+      }
+      ch = nx;
+      if (!more) break;
+    }
+  }
+  for (; ch < c_hi; ch += kWaves) {               // checked path
+    ChunkRaw rr;
+    load_chunk_checked<DT>(row, (int64_t)ch * kCE, A.V, rr);
+    const float2 res = chunk_partial<MODE, DT>(rr, ch * kCE, xe, c, gath);
+    if (lane == 0) s_part[ch - c_lo] = res;
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();                                // see every partial of request b
-  if (tid == 0) A.counters[b] = 0u;               // clean for the next call
+  float2* part = A.part + (int64_t)rowg * A.n_chunk;
+  for (int i = tid; i < c_hi - c_lo; i += kThreads) part[c_lo + i] = s_part[i];
+}
+
+// One wave per request: the rule on the merged partials.
+template <int MODE, int DT, bool kVec>
+__global__ __launch_bounds__(64) void sv_tail_kernel(Args A) {
+  __shared__ TailLds S;
+  const int b = blockIdx.x;
   if constexpr (MODE == kOneHot || MODE == kExplicit) {
-    sample_tail<DT, U, kVec, MODE>(A, b, S);
+    sample_tail<DT, kVec, MODE>(A, b, S);
   } else if constexpr (MODE == kGreedy) {
     greedy_tail(A, b, S);
   } else {
@@ -465,16 +645,17 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
 }
 
 // ------------------------------------------------------ residual pass ---
-// Explicit draft logits: for requests that stopped at a < K, segment sums of
+// Explicit draft logits: for requests that stopped at a < K, chunk sums of
 // max(0, p_a - q_a); the last workgroup of the request draws the token.
-template <int DT, int U, bool kVec>
+template <int DT, bool kVec>
 __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
-  constexpr int kPer = Elem<DT>::kPerVec, kLen = kThreads * U * kPer;
+  constexpr int kCE = Chunk<DT>::kElems;
   __shared__ TailLds S;
   __shared__ int s_last;
-  const int tid = threadIdx.x;
-  const int seg = (int)(blockIdx.x % (unsigned)A.n_seg);
-  const int b = (int)(blockIdx.x / (unsigned)A.n_seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
+  const int wi = (int)(blockIdx.x % (unsigned)A.wpr);
+  const int b = (int)(blockIdx.x / (unsigned)A.wpr);
   const Record rc = A.rec[b];
   if (!rc.pending) return;
   const int a = rc.a;
@@ -482,48 +663,56 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   const float ip = 1.f / rc.Sp, iq = 1.f / rc.Sq;
   const char* rowp = row_ptr(A, b, a);
   const char* rowq = row_ptr(A, b, A.R + a);
-  const int64_t seg0 = (int64_t)seg * kLen;
+  const int c_lo = wi * A.cpw;
+  const int c_hi = min(c_lo + A.cpw, A.n_chunk);
 
-  float xp[U * kPer], xq[U * kPer];
-  load_segment<DT, U, kVec>(rowp, seg0, A.V, xp);
-  load_segment<DT, U, kVec>(rowq, seg0, A.V, xq);
-  float s = 0.f;
+  constexpr int kPer = Elem<DT>::kPerVec;
+  for (int ch = c_lo + wave; ch < c_hi; ch += kWaves) {
+    const int64_t c0 = (int64_t)ch * kCE;
+    ChunkRaw rp, rq;
+    if (kVec && ch < A.n_full) {
+      issue_chunk<DT>(rowp, c0, rp);
+      issue_chunk<DT>(rowq, c0, rq);
+    } else {
+      load_chunk_checked<DT>(rowp, c0, A.V, rp);
+      load_chunk_checked<DT>(rowq, c0, A.V, rq);
+    }
+    float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < U * kPer; ++e)
-    s += fmaxf(fast_exp2(fmaf(xp[e], c, -rc.Mp)) * ip - fast_exp2(fmaf(xq[e], c, -rc.Mq)) * iq, 0.f);
-  s = block_sum(s, S.red);
-  if (tid == 0) {
-    A.res_part[(int64_t)b * A.n_seg + seg] = s;
-    __threadfence();
-    const unsigned prev = atomicAdd(&A.counters[b], 1u);
-    s_last = (prev == (unsigned)(A.n_seg - 1));
+    for (int j = 0; j < kLoadsPerLane; ++j)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        s += fmaxf(fast_exp2(fmaf(raw_elem<DT>(rp, j, k), c, -rc.Mp)) * ip -
+                   fast_exp2(fmaf(raw_elem<DT>(rq, j, k), c, -rc.Mq)) * iq, 0.f);
+    s = wave_sum_all(s);
+    if (lane == 0) publish(A.res_part + (int64_t)b * A.n_chunk + ch, s);
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) A.counters[b] = 0u;
+  if (!last_of_request(A.counters + b, (unsigned)A.wpr, &s_last)) return;
+  if (wave != 0) return;                          // the draw is one wave's work
 
-  const float* rp = A.res_part + (int64_t)b * A.n_seg;
-  auto W = [&](int sg) { return rp[sg]; };
-  const float Z = locate_segment(A.n_seg, rc.u, W, S);
-  int y;
-  if (Z > 0.f && S.found >= 0) {
-    const int fs = S.found;
-    const float t_in = S.tin;
-    const int64_t f0 = (int64_t)fs * kLen;
-    load_segment<DT, U, kVec>(rowp, f0, A.V, xp);
-    load_segment<DT, U, kVec>(rowq, f0, A.V, xq);
-    float w[U * kPer];
+  constexpr int E = kCE / 64;
+  const float* rpart = A.res_part + (int64_t)b * A.n_chunk;
+  auto W = [&](int sg) { return fetch(rpart + sg); };
+  int found;
+  float t_in;
+  const float Z = wave_locate(A.n_chunk, rc.u, W, &found, &t_in);
+  int y = -1;
+  if (Z > 0.f && found >= 0) {
+    const int64_t c0 = (int64_t)found * kCE;
+    float xp[E], xq[E], w[E];
+    load_lane_run<DT, kVec, E>(rowp, c0, A.V, xp);
+    load_lane_run<DT, kVec, E>(rowq, c0, A.V, xq);
 #pragma unroll
-    for (int e = 0; e < U * kPer; ++e)
-      w[e] = fmaxf(fast_exp2(fmaf(xp[e], c, -rc.Mp)) * ip - fast_exp2(fmaf(xq[e], c, -rc.Mq)) * iq, 0.f);
-    y = pick_in_segment<kPer, U>(w, f0, t_in, S);
-  } else {
-    // p_a and q_a agree everywhere: draw from p_a
-    y = draw_softmax_row<DT, U, kVec>(A, b, a, c, rc.Mp, -1, rc.u, S);
+    for (int k = 0; k < E; ++k)
+      w[k] = fmaxf(fast_exp2(fmaf(xp[k], c, -rc.Mp)) * ip - fast_exp2(fmaf(xq[k], c, -rc.Mq)) * iq, 0.f);
+    y = wave_pick<E>(w, c0, t_in);
+  }
+  if (y < 0) {
+    // p_a and q_a agree everywhere: draw from p_a with the row pass's partials
+    y = draw_softmax_row<DT, kVec>(A, b, a, c, rc.Mp, -1, rc.u, S, false);
     if (y < 0) y = 0;
   }
-  if (tid == 0) A.out_tokens[(int64_t)b * A.out_cols + a] = y;
+  if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + a] = y;
 }
 
 __global__ void sv_zero_kernel(unsigned char* p, size_t n) {
@@ -549,26 +738,24 @@ using namespace sv;
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t part, rec, res, total;
+  size_t part, gath, rec, res, total;
 };
 
-// Workspace: [counters: 4 * SV_MAX_BATCH][partials][records][residual partials]
+// Workspace: [counters: 4 * SV_MAX_BATCH][partials][gathered logits]
+//            [records][residual partials]
 Layout layout(int64_t B, int64_t rows, int64_t V) {
-  const int64_t nseg = (V + kSegMin - 1) / kSegMin;
+  const int64_t ce = Chunk<kF32>::kElems;          // the smaller chunk: a bound for both dtypes
+  const int64_t nch = (V + ce - 1) / ce;
   Layout L;
   L.part = align_up(kCounterBytes, 256);
-  L.rec = align_up(L.part + (size_t)(B * rows * nseg) * sizeof(float2), 256);
+  L.gath = align_up(L.part + (size_t)(B * rows * nch) * sizeof(float2), 256);
+  L.rec = align_up(L.gath + (size_t)(B * rows) * sizeof(float), 256);
   L.res = align_up(L.rec + (size_t)B * sizeof(Record), 256);
-  L.total = align_up(L.res + (size_t)(B * nseg) * sizeof(float), 256);
+  L.total = align_up(L.res + (size_t)(B * nch) * sizeof(float), 256);
   return L;
 }
 
 int elem_bytes(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
-
-int seg_len(int dtype) {
-  return dtype == SV_DTYPE_BF16 ? kThreads * kUBf16 * Elem<kBF16>::kPerVec
-                                : kThreads * kUF32 * Elem<kF32>::kPerVec;
-}
 
 int check_desc(const sv_logits* d) {
   if (!d || !d->data) return SV_ERR_NULL;
@@ -584,19 +771,39 @@ bool aligned16(const sv_logits* d) {
          ((d->stride_k * es) % 16 == 0);
 }
 
-void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int rows,
-                 void* ws, int dtype) {
-  const int64_t es = elem_bytes(dtype);
+// Chunks per workgroup: enough workgroups to keep every CU busy through
+// the launch (about 4096), each long enough that its four waves stream
+// several chunks apiece. SPECVERIFY_CHUNKS_PER_WG overrides (tuning).
+int chunks_per_wg(int64_t rows_total, int n_chunk) {
+  static const int env = [] {
+    const char* e = getenv("SPECVERIFY_CHUNKS_PER_WG");
+    return e ? atoi(e) : 0;
+  }();
+  int64_t cpw = env > 0 ? env : (rows_total * n_chunk + 4095) / 4096;
+  cpw = (cpw + kWaves - 1) / kWaves * kWaves;
+  if (cpw < kWaves) cpw = kWaves;
+  if (cpw > kMaxChunksPerWg) cpw = kMaxChunksPerWg;
+  if (cpw > n_chunk) cpw = n_chunk;
+  return (int)cpw;
+}
+
+void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int rows, void* ws) {
+  const int64_t es = elem_bytes(t->dtype);
   A.tgt = static_cast<const char*>(t->data);
   A.t_sb = t->stride_b * es;
   A.t_sk = t->stride_k * es;
   A.drf = nullptr; A.d_sb = 0; A.d_sk = 0;
   A.B = B; A.K = K; A.V = V; A.R = R; A.rows = rows;
-  A.n_seg = (V + seg_len(dtype) - 1) / seg_len(dtype);
+  const int ce = t->dtype == SV_DTYPE_BF16 ? Chunk<kBF16>::kElems : Chunk<kF32>::kElems;
+  A.n_chunk = (V + ce - 1) / ce;
+  A.n_full = V / ce;
+  A.cpw = chunks_per_wg((int64_t)B * rows, A.n_chunk);
+  A.wpr = (A.n_chunk + A.cpw - 1) / A.cpw;
   const Layout L = layout(B, rows, V);
   unsigned char* base = static_cast<unsigned char*>(ws);
   A.counters = reinterpret_cast<unsigned*>(base);
   A.part = reinterpret_cast<float2*>(base + L.part);
+  A.gath = reinterpret_cast<float*>(base + L.gath);
   A.rec = reinterpret_cast<Record*>(base + L.rec);
   A.res_part = reinterpret_cast<float*>(base + L.res);
   A.out_p = nullptr; A.out_q = nullptr; A.out_aux = nullptr;
@@ -608,24 +815,37 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
 #define SV_LAUNCH(KERNEL, grid, st, A) \
   hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(kThreads), 0, st, A)
 
+// Row pass over every (request, row, chunk run), then one tail workgroup
+// per request, back to back on the caller's stream.
 template <int MODE>
 void launch_rows(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
+  const unsigned B = (unsigned)A.B;
   if (dtype == SV_DTYPE_BF16) {
-    if (vec) SV_LAUNCH((sv_rows_kernel<MODE, kBF16, kUBf16, true>), grid, st, A);
-    else     SV_LAUNCH((sv_rows_kernel<MODE, kBF16, kUBf16, false>), grid, st, A);
+    if (vec) {
+      SV_LAUNCH((sv_rows_kernel<MODE, kBF16, true>), grid, st, A);
+      hipLaunchKernelGGL((sv_tail_kernel<MODE, kBF16, true>), dim3(B), dim3(64), 0, st, A);
+    } else {
+      SV_LAUNCH((sv_rows_kernel<MODE, kBF16, false>), grid, st, A);
+      hipLaunchKernelGGL((sv_tail_kernel<MODE, kBF16, false>), dim3(B), dim3(64), 0, st, A);
+    }
   } else {
-    if (vec) SV_LAUNCH((sv_rows_kernel<MODE, kF32, kUF32, true>), grid, st, A);
-    else     SV_LAUNCH((sv_rows_kernel<MODE, kF32, kUF32, false>), grid, st, A);
+    if (vec) {
+      SV_LAUNCH((sv_rows_kernel<MODE, kF32, true>), grid, st, A);
+      hipLaunchKernelGGL((sv_tail_kernel<MODE, kF32, true>), dim3(B), dim3(64), 0, st, A);
+    } else {
+      SV_LAUNCH((sv_rows_kernel<MODE, kF32, false>), grid, st, A);
+      hipLaunchKernelGGL((sv_tail_kernel<MODE, kF32, false>), dim3(B), dim3(64), 0, st, A);
+    }
   }
 }
 
 void launch_residual(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
   if (dtype == SV_DTYPE_BF16) {
-    if (vec) SV_LAUNCH((sv_residual_kernel<kBF16, kUBf16, true>), grid, st, A);
-    else     SV_LAUNCH((sv_residual_kernel<kBF16, kUBf16, false>), grid, st, A);
+    if (vec) SV_LAUNCH((sv_residual_kernel<kBF16, true>), grid, st, A);
+    else     SV_LAUNCH((sv_residual_kernel<kBF16, false>), grid, st, A);
   } else {
-    if (vec) SV_LAUNCH((sv_residual_kernel<kF32, kUF32, true>), grid, st, A);
-    else     SV_LAUNCH((sv_residual_kernel<kF32, kUF32, false>), grid, st, A);
+    if (vec) SV_LAUNCH((sv_residual_kernel<kF32, true>), grid, st, A);
+    else     SV_LAUNCH((sv_residual_kernel<kF32, false>), grid, st, A);
   }
 }
 
@@ -693,7 +913,7 @@ int spec_verify_sample(const sv_logits* target, const sv_logits* draft,
   if (workspace_bytes < layout(B, rows, V).total) return SV_ERR_WORKSPACE;
 
   Args A;
-  fill_common(A, target, B, K, V, R, rows, workspace, target->dtype);
+  fill_common(A, target, B, K, V, R, rows, workspace);
   if (explicit_q) {
     const int64_t es = elem_bytes(draft->dtype);
     A.drf = static_cast<const char*>(draft->data);
@@ -709,14 +929,18 @@ int spec_verify_sample(const sv_logits* target, const sv_logits* draft,
   A.out_len = out_accept_len;
   A.out_p = out_p_draft;
   A.out_q = out_q_draft;
-  const int64_t wgs = (int64_t)B * rows * A.n_seg;
+  const int64_t wgs = (int64_t)B * rows * A.wpr;
   if ((st = check_grid(wgs))) return st;
   const bool vec = aligned16(target) && (!explicit_q || aligned16(draft));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (explicit_q) {
     launch_rows<kExplicit>(A, target->dtype, vec, (unsigned)wgs, s);
     if ((st = hip_status())) return st;
-    launch_residual(A, target->dtype, vec, (unsigned)((int64_t)B * A.n_seg), s);
+    // the residual pass streams one stop row pair per request
+    Args A2 = A;
+    A2.cpw = chunks_per_wg(B, A.n_chunk);
+    A2.wpr = (A.n_chunk + A2.cpw - 1) / A2.cpw;
+    launch_residual(A2, target->dtype, vec, (unsigned)((int64_t)B * A2.wpr), s);
   } else {
     launch_rows<kOneHot>(A, target->dtype, vec, (unsigned)wgs, s);
   }
@@ -737,13 +961,13 @@ int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
   const int R = K + 1;
   if (workspace_bytes < layout(B, R, V).total) return SV_ERR_WORKSPACE;
   Args A;
-  fill_common(A, target, B, K, V, R, R, workspace, target->dtype);
+  fill_common(A, target, B, K, V, R, R, workspace);
   A.tokens = draft_tokens;
   A.out_cols = K + 1;
   A.out_tokens = out_tokens;
   A.out_len = out_accept_len;
   A.out_aux = out_argmax;
-  const int64_t wgs = (int64_t)B * R * A.n_seg;
+  const int64_t wgs = (int64_t)B * R * A.wpr;
   if ((st = check_grid(wgs))) return st;
   launch_rows<kGreedy>(A, target->dtype, aligned16(target), (unsigned)wgs,
                        static_cast<hipStream_t>(stream));
@@ -765,7 +989,7 @@ int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
   if (!workspace) return SV_ERR_WORKSPACE;
   if (workspace_bytes < layout(B, N, V).total) return SV_ERR_WORKSPACE;
   Args A;
-  fill_common(A, target, B, 0, V, N, N, workspace, target->dtype);
+  fill_common(A, target, B, 0, V, N, N, workspace);
   A.tokens = node_tokens;
   A.out_cols = N;
   A.out_tokens = out_tokens;
@@ -773,7 +997,7 @@ int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
   A.out_aux = out_best_node;
   A.n_nodes = N;
   for (int n = 0; n < N; ++n) A.parent[n] = (int8_t)parents[n];
-  const int64_t wgs = (int64_t)B * N * A.n_seg;
+  const int64_t wgs = (int64_t)B * N * A.wpr;
   if ((st = check_grid(wgs))) return st;
   launch_rows<kTree>(A, target->dtype, aligned16(target), (unsigned)wgs,
                      static_cast<hipStream_t>(stream));

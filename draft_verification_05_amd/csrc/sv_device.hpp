@@ -75,38 +75,170 @@ __device__ inline float load_one(const char* row, int64_t e) {
   }
 }
 
-// A segment is kThreads * U vectors of Elem::kPerVec logits. Thread t holds
-// vectors t, t + kThreads, ..., so each of the U loads of a wave is one
-// contiguous 1 KiB run. Elements at or past V read as -inf.
-template <int DT, int U, bool kVec>
-__device__ inline void load_segment(const char* row, int64_t seg0, int V,
-                                    float (&x)[U * Elem<DT>::kPerVec]) {
+// A chunk is 4 KiB of consecutive logits (2048 bf16 or 1024 fp32): the
+// unit of one partial, and what one wave reads per step (four 16-byte
+// loads per lane, each load instruction one contiguous 1 KiB of the wave).
+constexpr int kChunkBytes = 4096;
+constexpr int kLoadsPerLane = kChunkBytes / (64 * 16);
+
+template <int DT> struct Chunk {
+  static constexpr int kPer = Elem<DT>::kPerVec;             // logits per 16-byte load
+  static constexpr int kElems = kChunkBytes / Elem<DT>::kBytes;
+  static constexpr int kPerLane = kElems / 64;                // logits per lane
+  static constexpr int kPerThread = kElems / kThreads;        // when a workgroup reads it
+};
+
+// Raw 16-byte vectors of one chunk for one lane: vector j covers logits
+// c0 + (j * 64 + lane) * kPer ... + kPer - 1.
+struct ChunkRaw { uint4 v[kLoadsPerLane]; };
+
+template <int DT>
+__device__ __forceinline__ void issue_chunk(const char* row, int64_t c0, ChunkRaw& r) {
   constexpr int kPer = Elem<DT>::kPerVec;
-  constexpr int kLen = kThreads * U * kPer;
-  const int tid = threadIdx.x;
-  if (kVec && seg0 + kLen <= V) {
+  const char* p = row + (c0 + (int64_t)(threadIdx.x & 63) * kPer) * Elem<DT>::kBytes;
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int64_t e0 = seg0 + (int64_t)(j * kThreads + tid) * kPer;
-      load_vec16<DT>(row + e0 * Elem<DT>::kBytes, &x[j * kPer]);
-    }
-  } else {
+  for (int j = 0; j < kLoadsPerLane; ++j)
+    r.v[j] = *reinterpret_cast<const uint4*>(p + j * 64 * 16);
+}
+
+// Same layout as issue_chunk, element by element with bounds checks (a
+// row's last, partial chunk; rows that are not 16-byte aligned). Logits at
+// or past V read as -inf (bf16 0xFF80, fp32 0xFF800000).
+template <int DT>
+__device__ __forceinline__ void load_chunk_checked(const char* row, int64_t c0, int V, ChunkRaw& r) {
+  constexpr int kPer = Elem<DT>::kPerVec;
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int64_t e0 = seg0 + (int64_t)(j * kThreads + tid) * kPer;
-      if (kVec && e0 + kPer <= V) {
-        load_vec16<DT>(row + e0 * Elem<DT>::kBytes, &x[j * kPer]);
+  for (int j = 0; j < kLoadsPerLane; ++j) {
+    const int64_t e0 = c0 + (int64_t)(j * 64 + (threadIdx.x & 63)) * kPer;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (DT == kF32) {
+        const int64_t e = e0 + q;
+        w[q] = e < V ? __float_as_uint(load_one<DT>(row, e)) : 0xFF800000u;
       } else {
-#pragma unroll
-        for (int k = 0; k < kPer; ++k)
-          x[j * kPer + k] = (e0 + k < V) ? load_one<DT>(row, e0 + k) : kNegInf;
+        const int64_t e = e0 + 2 * q;
+        const uint32_t lo = e < V ? (uint32_t)reinterpret_cast<const uint16_t*>(row)[e] : 0xFF80u;
+        const uint32_t hi = e + 1 < V ? (uint32_t)reinterpret_cast<const uint16_t*>(row)[e + 1] : 0xFF80u;
+        w[q] = lo | (hi << 16);
       }
     }
+    r.v[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// A whole workgroup reads one chunk: thread t holds logits
+// c0 + t * kPerThread ... + kPerThread - 1, in index order.
+template <int DT, bool kVec>
+__device__ inline void load_chunk_wg(const char* row, int64_t c0, int V,
+                                     float (&x)[Chunk<DT>::kPerThread]) {
+  constexpr int kPT = Chunk<DT>::kPerThread;
+  const int64_t e0 = c0 + (int64_t)threadIdx.x * kPT;
+  if (kVec && e0 + kPT <= V) {
+    load_vec16<DT>(row + e0 * Elem<DT>::kBytes, x);    // kPerThread logits = one 16-byte vector
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPT; ++k)
+      x[k] = (e0 + k < V) ? load_one<DT>(row, e0 + k) : kNegInf;
   }
 }
 
 // ------------------------------------------------------ reductions ---
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave64 reductions on the DPP network: inside each row of 16 lanes, lane i
+// meets lanes i^1, i^2 (quad permutes), then 7-i (half-row mirror) and 15-i
+// (row mirror), after which every lane holds its row's result; the four
+// row results are then combined through scalar reads. No LDS traffic.
+template <int kCtrl>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+template <int kCtrl>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ inline float wave_max_all(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Sum over the wave, same value in every lane (fixed association order).
+__device__ inline float wave_sum_all(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order: Kogge-Stone row
+// shifts by 1, 2, 4, 8 inside each row of 16, then row 15 broadcast into
+// rows 1 and 3 and lane 31 into rows 2 and 3.
+__device__ inline float wave_scan_incl(float v) {
+  v += dpp_f<0x111>(v);
+  v += dpp_f<0x112>(v);
+  v += dpp_f<0x114>(v);
+  v += dpp_f<0x118>(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+// Lowest / highest lane whose predicate holds, -1 if none (wave-uniform).
+__device__ inline int first_lane(bool p) {
+  const unsigned long long m = __ballot(p);
+  return m ? __builtin_ctzll(m) : -1;
+}
+__device__ inline int last_lane(bool p) {
+  const unsigned long long m = __ballot(p);
+  return m ? 63 - __builtin_clzll(m) : -1;
+}
+__device__ inline float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ inline int lane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// (value, index) argmax over the wave: larger value, then lower index.
+__device__ inline void am_step(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+template <int kCtrl>
+__device__ inline void am_dpp(float& v, int& i) {
+  const float v2 = dpp_f<kCtrl>(v);
+  const int i2 = dpp_i<kCtrl>(i);
+  am_step(v, i, v2, i2);
+}
+__device__ inline void wave_argmax_all(float& v, int& i) {
+  am_dpp<kDppXor1>(v, i);
+  am_dpp<kDppXor2>(v, i);
+  am_dpp<kDppHalfMirror>(v, i);
+  am_dpp<kDppMirror>(v, i);
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int row = 1; row < 4; ++row)
+    am_step(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), row * 16)),
+            __builtin_amdgcn_readlane(i, row * 16));
+  v = bv;
+  i = bi;
+}
 
 // Merge two (max, sum of 2^(y - max)) pairs.
 __device__ inline void ms_merge(float& m, float& s, float m2, float s2) {
