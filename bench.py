@@ -38,21 +38,27 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, seg_elems=8192) -> int:
-    """One read of every logits row the rule consults, plus the draw's one
-    re-read segment per request (greedy and tree draw nothing)."""
+CHUNK_BYTES = 4096        # the draw re-reads one 4 KiB chunk of logits per request
+
+
+def algorithmic_bytes(wl, rejected=None) -> int:
+    """Bytes one call must read: every logits row the rule consults once
+    (B*(K+1) target rows, plus B*K draft rows when q is explicit), plus the
+    draw's one chunk per request, plus (explicit drafts only) the stop rows
+    of target and draft again for each request that rejected (`rejected`
+    requests; all B when unknown). Greedy and tree draw nothing."""
     es = 2 if wl["dtype"] == "bf16" else 4
     B, V = wl["B"], wl["V"]
     if wl["mode"] == "tree":
         return B * len(wl["parents"]) * V * es
     K = wl["K"]
-    rows = K + 1 + (K if wl.get("draft") is not None else 0)
+    explicit = wl.get("draft") is not None
+    rows = K + 1 + (K if explicit else 0)
     total = B * rows * V * es
     if wl["mode"] == "sample":
-        total += B * min(seg_elems, V) * es
-        if wl.get("draft") is not None:
-            # explicit drafts: the rejected requests re-read target and draft stop rows
-            total += B * 2 * V * es
+        total += B * min(CHUNK_BYTES, V * es)
+        if explicit:
+            total += (B if rejected is None else rejected) * 2 * V * es
     return total
 
 
@@ -189,30 +195,38 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K steps, per-launch event pairs on the launch stream.
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: exactly K back-to-back steps between two events on the
+    # launch stream (no events in between, so nothing pads the steps).
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     region0.record()
     for i in range(args.steps):
-        starts[i].record()
         step(args.warmup + i)
-        ends[i].record()
     region1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    region_ms = region0.elapsed_time(region1)
+
+    # Per-call durations: a second pass with an event pair around every call
+    # (both launches of the call; the events add a small gap between calls).
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record()
+        step(args.warmup + args.steps + i)
+        ends[i].record()
+    torch.cuda.synchronize()
 
     per_launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     mean_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
-    region_ms = region0.elapsed_time(region1)
     ms_per_step = region_ms / args.steps
-    nbytes = algorithmic_bytes(wl)
+    accept = out_len.cpu().numpy()
+    rejected = int((accept < K + 1).sum()) if mode == "sample" else None
+    nbytes = algorithmic_bytes(wl, rejected)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
-    accept = out_len.cpu().numpy()
 
     line = {
         "metric": METRIC,
@@ -238,8 +252,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_record(wl["name"]),
-                     "kernel": "sv_rows_kernel" if not (mode == "sample" and draft is not None)
-                     else "whole step (row pass + residual pass)",
+                     "kernel": "one verification call: row pass + tail" +
+                               (" + residual pass" if mode == "sample" and draft is not None else ""),
                      "launch_us_mean": round(mean_launch_ms * 1e3, 2),
                      "launch_us_p10": round(per_launch_ms[len(per_launch_ms) // 10] * 1e3, 2),
                      "launch_us_p90": round(per_launch_ms[(9 * len(per_launch_ms)) // 10] * 1e3, 2)},

@@ -67,7 +67,8 @@ struct Args {
   int out_cols;   // row length of out_tokens
   int32_t* out_tokens; int32_t* out_len; float* out_p; float* out_q; int32_t* out_aux;
   unsigned* counters;   // [B], zero between calls
-  float2* part;         // [B * rows * n_chunk]
+  float2* part;         // [B * rows * n_chunk]: one partial per chunk
+  float2* wpart;        // [B * rows * wpr]: one partial per row-pass workgroup
   int n_full;           // chunks per row that lie entirely below V
   float* gath;          // [B * rows]: logit of the row's draft token
   Record* rec;          // [B]
@@ -250,60 +251,79 @@ __device__ int draw_softmax_row(const Args& A, int b, int r, float c, float M, i
   return wave_pick<E>(w, c0, t_in);
 }
 
-// Copies a request's n partials to LDS (one round of loads) when they fit.
-__device__ bool stage_partials(const Args& A, int b, TailLds& S) {
+// Copying a request's partials to LDS when they fit: stage_issue starts the
+// loads of the first 512 (8 per lane) so independent work can overlap
+// them; stage_commit stores them, copies any rest, and syncs. Returns
+// whether the partials are cached.
+struct Staged { float2 v[8]; };
+
+__device__ inline void stage_issue(const Args& A, int b, Staged& t) {
+  const int lane = threadIdx.x & 63;
+  const int n = A.rows * A.n_chunk;
+  if (n > kPartCache) return;
+  const float2* pb = A.part + (int64_t)b * n;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = q * 64 + lane;
+    t.v[q] = i < n ? pb[i] : make_float2(0.f, 0.f);
+  }
+}
+
+__device__ bool stage_commit(const Args& A, int b, TailLds& S, Staged& t) {
   const int lane = threadIdx.x & 63;
   const int n = A.rows * A.n_chunk;
   if (n > kPartCache) return false;
   const float2* pb = A.part + (int64_t)b * n;
   for (int base = 0; base < n; base += 8 * 64) {
-    float2 t[8];
+    if (base) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = base + q * 64 + lane;
-      t[q] = i < n ? pb[i] : make_float2(0.f, 0.f);
+      for (int q = 0; q < 8; ++q) {
+        const int i = base + q * 64 + lane;
+        t.v[q] = i < n ? pb[i] : make_float2(0.f, 0.f);
+      }
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int i = base + q * 64 + lane;
-      if (i < n) S.pcache[i] = t[q];
+      if (i < n) S.pcache[i] = t.v[q];
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
   return true;
 }
 
-// Per-row (max, sum) of a request's partials into S.rowM / S.rowS.
-__device__ void merge_softmax_rows(const Args& A, int b, TailLds& S, bool cached) {
+
+// Per-row (max, sum) into S.rowM / S.rowS from the row pass's
+// per-workgroup partials: one lane per row.
+__device__ void merge_softmax_rows(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63;
-  for (int rr = 0; rr < A.rows; ++rr) {
+  const float2* wp = A.wpart + (int64_t)b * A.rows * A.wpr;
+  for (int rr = lane; rr < A.rows; rr += 64) {
     float m = kNegInf, s = 0.f;
-    for (int sg = lane; sg < A.n_chunk; sg += 64) {
-      const float2 v = partial(A, b, rr, sg, S, cached);
+    for (int w = 0; w < A.wpr; ++w) {
+      const float2 v = wp[rr * A.wpr + w];
       ms_merge(m, s, v.x, v.y);
     }
-    const float wm = wave_max_all(m);
-    s = (m == kNegInf) ? 0.f : s * fast_exp2(m - wm);
-    s = wave_sum_all(s);
-    if (lane == 0) { S.rowM[rr] = wm; S.rowS[rr] = s; }
+    S.rowM[rr] = m;
+    S.rowS[rr] = s;
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
 }
 
-// Per-row argmax of a request's partials into S.g.
-__device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, bool cached) {
+// Per-row argmax into S.g from the per-workgroup partials.
+__device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S) {
   const int lane = threadIdx.x & 63;
-  for (int rr = 0; rr < n_rows; ++rr) {
+  const float2* wp = A.wpart + (int64_t)b * A.rows * A.wpr;
+  for (int rr = lane; rr < n_rows; rr += 64) {
     float v = kNegInf;
     int idx = INT_MAX;
-    for (int sg = lane; sg < A.n_chunk; sg += 64) {
-      const float2 t = partial(A, b, rr, sg, S, cached);
+    for (int w = 0; w < A.wpr; ++w) {
+      const float2 t = wp[rr * A.wpr + w];
       am_step(v, idx, t.x, __float_as_int(t.y));
     }
-    wave_argmax_all(v, idx);
-    if (lane == 0) S.g[rr] = idx;
+    S.g[rr] = idx;
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
 }
 
 // ---------------------------------------------------------- row tails ---
@@ -323,14 +343,18 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   }
   const float T = A.temperature[b];
   const uint64_t seed = A.seeds[b];
-  const bool cached = stage_partials(A, b, S);
+  Staged st;
+  stage_issue(A, b, st);
+  // the uniforms depend on nothing in memory but the seed: compute them
+  // while the partials are on their way
   float uacc = 0.f, usmp = 0.f;
   if (lane <= K) {
     const Philox4 rnd = philox4x64_10((uint64_t)lane, (uint64_t)b, A.offset, 0ull, seed, 0ull);
     uacc = top24(rnd.w0);
     usmp = top24(rnd.w1);
   }
-  merge_softmax_rows(A, b, S, cached);
+  const bool cached = stage_commit(A, b, S, st);
+  merge_softmax_rows(A, b, S);
   int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
   if (!(T > 0.f && T < __builtin_inff())) {      // refused request
     if (lane <= K) otok[lane] = -1;
@@ -394,8 +418,7 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
 __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63, K = A.K;
   const int x = lane < K ? A.tokens[(int64_t)b * K + lane] : -1;
-  const bool cached = stage_partials(A, b, S);
-  merge_argmax_rows(A, b, A.rows, S, cached);
+  merge_argmax_rows(A, b, A.rows, S);
   const int g = lane <= K ? S.g[lane] : -1;
   const int mis = first_lane(lane < K && x != g);
   const int a = mis < 0 ? K : mis;
@@ -409,8 +432,7 @@ __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
 __device__ void tree_tail(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63, N = A.n_nodes;
   if (lane < N) S.x[lane] = A.tokens[(int64_t)b * N + lane];
-  const bool cached = stage_partials(A, b, S);
-  merge_argmax_rows(A, b, N, S, cached);
+  merge_argmax_rows(A, b, N, S);
   if (lane == 0) {
     uint64_t acc = 1ull;
     int best = 0;
@@ -434,7 +456,7 @@ __device__ void tree_tail(const Args& A, int b, TailLds& S) {
     A.out_len[b] = len + 1;
     if (A.out_aux) A.out_aux[b] = best;
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
   const int len = S.depth[SV_MAX_TREE_NODES - 1];
   if (lane < N) A.out_tokens[(int64_t)b * A.out_cols + lane] = lane <= len ? S.path[lane] : -1;
 }
@@ -524,7 +546,6 @@ __device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, int c0, int xe, flo
     for (int j = 0; j < kLoadsPerLane; ++j)
 #pragma unroll
       for (int k = 0; k < kPer; ++k) mx = fmaxf(mx, raw_elem<DT>(r, j, k));
-    touch(r);
     const float msub = (mx == kNegInf) ? 0.f : mx * c;
     float acc[kLoadsPerLane];
 #pragma unroll
@@ -621,16 +642,36 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   }
   for (; ch < c_hi; ch += kWaves) {               // checked path
     ChunkRaw rr;
-    load_chunk_checked<DT>(row, (int64_t)ch * kCE, A.V, rr);
+    load_chunk_checked<DT, kVec>(row, (int64_t)ch * kCE, A.V, rr);
     const float2 res = chunk_partial<MODE, DT>(rr, ch * kCE, xe, c, gath);
     if (lane == 0) s_part[ch - c_lo] = res;
   }
   __syncthreads();
   float2* part = A.part + (int64_t)rowg * A.n_chunk;
   for (int i = tid; i < c_hi - c_lo; i += kThreads) part[c_lo + i] = s_part[i];
+  // wave 0 also folds the workgroup's partials into one, so the tail merges
+  // wpr values per row instead of n_chunk
+  if (wave == 0) {
+    float2 acc;
+    if constexpr (MODE == kOneHot || MODE == kExplicit) {
+      float m = kNegInf, s = 0.f;
+      for (int i = lane; i < c_hi - c_lo; i += 64) ms_merge(m, s, s_part[i].x, s_part[i].y);
+      const float wm = wave_max_all(m);
+      s = wave_sum_all((m == kNegInf) ? 0.f : s * fast_exp2(m - wm));
+      acc = make_float2(wm, s);
+    } else {
+      float v = kNegInf;
+      int idx = INT_MAX;
+      for (int i = lane; i < c_hi - c_lo; i += 64) am_step(v, idx, s_part[i].x, __float_as_int(s_part[i].y));
+      wave_argmax_all(v, idx);
+      acc = make_float2(v, __int_as_float(idx));
+    }
+    if (lane == 0) A.wpart[(int64_t)rowg * A.wpr + wi] = acc;
+  }
 }
 
-// One wave per request: the rule on the merged partials.
+// One wave per request: the rule on the merged partials. The launch
+// boundary after the row pass is the only synchronisation the tail needs.
 template <int MODE, int DT, bool kVec>
 __global__ __launch_bounds__(64) void sv_tail_kernel(Args A) {
   __shared__ TailLds S;
@@ -674,8 +715,8 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
       issue_chunk<DT>(rowp, c0, rp);
       issue_chunk<DT>(rowq, c0, rq);
     } else {
-      load_chunk_checked<DT>(rowp, c0, A.V, rp);
-      load_chunk_checked<DT>(rowq, c0, A.V, rq);
+      load_chunk_checked<DT, kVec>(rowp, c0, A.V, rp);
+      load_chunk_checked<DT, kVec>(rowq, c0, A.V, rq);
     }
     float s = 0.f;
 #pragma unroll
@@ -738,17 +779,18 @@ using namespace sv;
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t part, gath, rec, res, total;
+  size_t part, wpart, gath, rec, res, total;
 };
 
-// Workspace: [counters: 4 * SV_MAX_BATCH][partials][gathered logits]
-//            [records][residual partials]
+// Workspace: [counters: 4 * SV_MAX_BATCH][chunk partials][workgroup
+//            partials][gathered logits][records][residual partials]
 Layout layout(int64_t B, int64_t rows, int64_t V) {
   const int64_t ce = Chunk<kF32>::kElems;          // the smaller chunk: a bound for both dtypes
   const int64_t nch = (V + ce - 1) / ce;
   Layout L;
   L.part = align_up(kCounterBytes, 256);
-  L.gath = align_up(L.part + (size_t)(B * rows * nch) * sizeof(float2), 256);
+  L.wpart = align_up(L.part + (size_t)(B * rows * nch) * sizeof(float2), 256);
+  L.gath = align_up(L.wpart + (size_t)(B * rows * nch) * sizeof(float2), 256);   // wpr <= nch
   L.rec = align_up(L.gath + (size_t)(B * rows) * sizeof(float), 256);
   L.res = align_up(L.rec + (size_t)B * sizeof(Record), 256);
   L.total = align_up(L.res + (size_t)(B * nch) * sizeof(float), 256);
@@ -803,6 +845,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   unsigned char* base = static_cast<unsigned char*>(ws);
   A.counters = reinterpret_cast<unsigned*>(base);
   A.part = reinterpret_cast<float2*>(base + L.part);
+  A.wpart = reinterpret_cast<float2*>(base + L.wpart);
   A.gath = reinterpret_cast<float*>(base + L.gath);
   A.rec = reinterpret_cast<Record*>(base + L.rec);
   A.res_part = reinterpret_cast<float*>(base + L.res);
@@ -815,26 +858,26 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
 #define SV_LAUNCH(KERNEL, grid, st, A) \
   hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(kThreads), 0, st, A)
 
-// Row pass over every (request, row, chunk run), then one tail workgroup
-// per request, back to back on the caller's stream.
+// Row pass over every (request, row, chunk run), then one tail wave per
+// request, back to back on the caller's stream.
 template <int MODE>
 void launch_rows(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
-  const unsigned B = (unsigned)A.B;
+  const dim3 tails((unsigned)A.B), wave(64);
   if (dtype == SV_DTYPE_BF16) {
     if (vec) {
       SV_LAUNCH((sv_rows_kernel<MODE, kBF16, true>), grid, st, A);
-      hipLaunchKernelGGL((sv_tail_kernel<MODE, kBF16, true>), dim3(B), dim3(64), 0, st, A);
+      hipLaunchKernelGGL((sv_tail_kernel<MODE, kBF16, true>), tails, wave, 0, st, A);
     } else {
       SV_LAUNCH((sv_rows_kernel<MODE, kBF16, false>), grid, st, A);
-      hipLaunchKernelGGL((sv_tail_kernel<MODE, kBF16, false>), dim3(B), dim3(64), 0, st, A);
+      hipLaunchKernelGGL((sv_tail_kernel<MODE, kBF16, false>), tails, wave, 0, st, A);
     }
   } else {
     if (vec) {
       SV_LAUNCH((sv_rows_kernel<MODE, kF32, true>), grid, st, A);
-      hipLaunchKernelGGL((sv_tail_kernel<MODE, kF32, true>), dim3(B), dim3(64), 0, st, A);
+      hipLaunchKernelGGL((sv_tail_kernel<MODE, kF32, true>), tails, wave, 0, st, A);
     } else {
       SV_LAUNCH((sv_rows_kernel<MODE, kF32, false>), grid, st, A);
-      hipLaunchKernelGGL((sv_tail_kernel<MODE, kF32, false>), dim3(B), dim3(64), 0, st, A);
+      hipLaunchKernelGGL((sv_tail_kernel<MODE, kF32, false>), tails, wave, 0, st, A);
     }
   }
 }

@@ -101,15 +101,20 @@ __device__ __forceinline__ void issue_chunk(const char* row, int64_t c0, ChunkRa
     r.v[j] = *reinterpret_cast<const uint4*>(p + j * 64 * 16);
 }
 
-// Same layout as issue_chunk, element by element with bounds checks (a
-// row's last, partial chunk; rows that are not 16-byte aligned). Logits at
-// or past V read as -inf (bf16 0xFF80, fp32 0xFF800000).
-template <int DT>
+// Same layout as issue_chunk with bounds checks: a row's last, partial
+// chunk (16-byte loads for the vectors inside the row when kVec) and rows
+// that are not 16-byte aligned (element loads). Logits at or past V read as
+// -inf (bf16 0xFF80, fp32 0xFF800000).
+template <int DT, bool kVec>
 __device__ __forceinline__ void load_chunk_checked(const char* row, int64_t c0, int V, ChunkRaw& r) {
   constexpr int kPer = Elem<DT>::kPerVec;
 #pragma unroll
   for (int j = 0; j < kLoadsPerLane; ++j) {
     const int64_t e0 = c0 + (int64_t)(j * 64 + (threadIdx.x & 63)) * kPer;
+    if (kVec && e0 + kPer <= V) {
+      r.v[j] = *reinterpret_cast<const uint4*>(row + e0 * Elem<DT>::kBytes);
+      continue;
+    }
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
