@@ -73,6 +73,7 @@ struct Args {
   float* gath;          // [B * rows]: logit of the row's draft token
   Record* rec;          // [B]
   float* res_part;      // [B * n_chunk]
+  float2* unif;         // [B * R]: (u_accept, u_sample) of each position
   int n_nodes;
   int8_t parent[SV_MAX_TREE_NODES];
 };
@@ -80,17 +81,25 @@ struct Args {
 // The tail keeps a request's partials in LDS when they fit, so the draw
 // can locate its chunk without another trip to memory.
 constexpr int kPartCache = 1024;
+// Per-workgroup partials of one request the tail stages in one batch of
+// loads (8 per lane); more fall back to direct loads.
+constexpr int kWPartCache = 512;
 
 struct TailLds {
   float2 pcache[kPartCache];
+  float2 wcache[kWPartCache];
   float rowM[kMaxRows], rowS[kMaxRows];
   int x[SV_MAX_TREE_NODES], g[SV_MAX_TREE_NODES], path[SV_MAX_TREE_NODES];
   int depth[SV_MAX_TREE_NODES];
 };
 
+// Row r of request b: target rows first, then draft rows. Written as
+// selects so that both descriptors load in one batch of scalar loads.
 __device__ inline const char* row_ptr(const Args& A, int b, int r) {
-  return r < A.R ? A.tgt + (int64_t)b * A.t_sb + (int64_t)r * A.t_sk
-                 : A.drf + (int64_t)b * A.d_sb + (int64_t)(r - A.R) * A.d_sk;
+  const bool t = r < A.R;
+  const char* base = t ? A.tgt : A.drf;
+  const int64_t sb = t ? A.t_sb : A.d_sb, sk = t ? A.t_sk : A.d_sk;
+  return base + (int64_t)b * sb + (int64_t)(t ? r : r - A.R) * sk;
 }
 
 // ------------------------------------------------ in-launch hand-off ---
@@ -293,15 +302,50 @@ __device__ bool stage_commit(const Args& A, int b, TailLds& S, Staged& t) {
 }
 
 
-// Per-row (max, sum) into S.rowM / S.rowS from the row pass's
-// per-workgroup partials: one lane per row.
-__device__ void merge_softmax_rows(const Args& A, int b, TailLds& S) {
+// The row pass's per-workgroup partials of a request, wpr per row: issued
+// as one batch of independent loads (8 per lane) at the start of the tail,
+// parked in LDS, then merged by one lane per row. Requests with more than
+// kWPartCache of them read them straight from the workspace instead.
+struct WStaged { float2 v[8]; };
+
+__device__ inline void wstage_issue(const Args& A, int b, int n_rows, WStaged& t) {
   const int lane = threadIdx.x & 63;
+  const int n = n_rows * A.wpr;
+  if (n > kWPartCache) return;
   const float2* wp = A.wpart + (int64_t)b * A.rows * A.wpr;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = q * 64 + lane;
+    if (i < n) t.v[q] = wp[i];
+  }
+}
+
+// Partial w of row rr: from LDS when staged.
+__device__ inline float2 wpartial(const Args& A, int b, int rr, int w, const TailLds& S, bool staged) {
+  return staged ? S.wcache[rr * A.wpr + w] : A.wpart[((int64_t)b * A.rows + rr) * A.wpr + w];
+}
+
+__device__ inline bool wstage_commit(const Args& A, int n_rows, TailLds& S, const WStaged& t) {
+  const int lane = threadIdx.x & 63;
+  const int n = n_rows * A.wpr;
+  if (n > kWPartCache) return false;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = q * 64 + lane;
+    if (i < n) S.wcache[i] = t.v[q];
+  }
+  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
+  return true;
+}
+
+// Per-row (max, sum) into S.rowM / S.rowS.
+__device__ void merge_softmax_rows(const Args& A, int b, TailLds& S, const WStaged& t) {
+  const int lane = threadIdx.x & 63;
+  const bool staged = wstage_commit(A, A.rows, S, t);
   for (int rr = lane; rr < A.rows; rr += 64) {
     float m = kNegInf, s = 0.f;
     for (int w = 0; w < A.wpr; ++w) {
-      const float2 v = wp[rr * A.wpr + w];
+      const float2 v = wpartial(A, b, rr, w, S, staged);
       ms_merge(m, s, v.x, v.y);
     }
     S.rowM[rr] = m;
@@ -310,16 +354,16 @@ __device__ void merge_softmax_rows(const Args& A, int b, TailLds& S) {
   __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
 }
 
-// Per-row argmax into S.g from the per-workgroup partials.
-__device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S) {
+// Per-row argmax into S.g.
+__device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, const WStaged& t) {
   const int lane = threadIdx.x & 63;
-  const float2* wp = A.wpart + (int64_t)b * A.rows * A.wpr;
+  const bool staged = wstage_commit(A, n_rows, S, t);
   for (int rr = lane; rr < n_rows; rr += 64) {
     float v = kNegInf;
     int idx = INT_MAX;
     for (int w = 0; w < A.wpr; ++w) {
-      const float2 t = wp[rr * A.wpr + w];
-      am_step(v, idx, t.x, __float_as_int(t.y));
+      const float2 p = wpartial(A, b, rr, w, S, staged);
+      am_step(v, idx, p.x, __float_as_int(p.y));
     }
     S.g[rr] = idx;
   }
@@ -342,19 +386,15 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
     if (MODE == kExplicit) ld = A.gath[rowg0 + R + lane];
   }
   const float T = A.temperature[b];
-  const uint64_t seed = A.seeds[b];
+  float2 un = make_float2(0.f, 0.f);
+  if (lane <= K) un = A.unif[(int64_t)b * R + lane];
+  WStaged ws;
+  wstage_issue(A, b, A.rows, ws);
   Staged st;
   stage_issue(A, b, st);
-  // the uniforms depend on nothing in memory but the seed: compute them
-  // while the partials are on their way
-  float uacc = 0.f, usmp = 0.f;
-  if (lane <= K) {
-    const Philox4 rnd = philox4x64_10((uint64_t)lane, (uint64_t)b, A.offset, 0ull, seed, 0ull);
-    uacc = top24(rnd.w0);
-    usmp = top24(rnd.w1);
-  }
+  const float uacc = un.x, usmp = un.y;   // drawn by the row pass
+  merge_softmax_rows(A, b, S, ws);
   const bool cached = stage_commit(A, b, S, st);
-  merge_softmax_rows(A, b, S);
   int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
   if (!(T > 0.f && T < __builtin_inff())) {      // refused request
     if (lane <= K) otok[lane] = -1;
@@ -418,7 +458,9 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
 __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63, K = A.K;
   const int x = lane < K ? A.tokens[(int64_t)b * K + lane] : -1;
-  merge_argmax_rows(A, b, A.rows, S);
+  WStaged ws;
+  wstage_issue(A, b, A.rows, ws);
+  merge_argmax_rows(A, b, A.rows, S, ws);
   const int g = lane <= K ? S.g[lane] : -1;
   const int mis = first_lane(lane < K && x != g);
   const int a = mis < 0 ? K : mis;
@@ -431,8 +473,11 @@ __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
 
 __device__ void tree_tail(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63, N = A.n_nodes;
-  if (lane < N) S.x[lane] = A.tokens[(int64_t)b * N + lane];
-  merge_argmax_rows(A, b, N, S);
+  const int xn = lane < N ? A.tokens[(int64_t)b * N + lane] : -1;
+  WStaged ws;
+  wstage_issue(A, b, N, ws);
+  if (lane < N) S.x[lane] = xn;
+  merge_argmax_rows(A, b, N, S, ws);
   if (lane == 0) {
     uint64_t acc = 1ull;
     int best = 0;
@@ -496,12 +541,27 @@ __device__ __forceinline__ void touch(ChunkRaw& r) {
     asm volatile("" : "+v"(r.v[j].x), "+v"(r.v[j].y), "+v"(r.v[j].z), "+v"(r.v[j].w));
 }
 
-// One chunk's partial from one wave: (max y, sum 2^(y - max)) for sampling,
+// Running softmax reference of one wave over the chunks it streams. Each
+// lane sums 2^(y - ref) against its own reference `ref` (a scaled logit
+// the lane has seen, so y - ref only exceeds 64 for data that triggers a
+// recount); the wave's partial is taken against M, the largest lane
+// reference, with f = 2^(ref - M) cached until some lane's reference moves.
+struct RefState {
+  float ref = kNegInf;   // lane
+  float f = 0.f;         // lane: 2^(ref - M), 0 while ref is -inf
+  float M = kNegInf;     // wave-uniform
+  bool first = true;     // wave-uniform: no chunk seen yet
+};
+
+// One chunk's partial from one wave: (M, sum 2^(y - M)) for sampling, where
+// M is a reference no larger than the row's maximum scaled logit (and, for
+// a chunk with finite logits, no smaller than any of them minus 64);
 // (max logit, lowest index of it) for greedy/tree. With a draft token xe in
 // this chunk, its logit goes to `gath` and, for one-hot drafts, it is left
 // out of the sums. `r` holds the lane's four 16-byte vectors.
 template <int MODE, int DT>
-__device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, int c0, int xe, float c, float* gath) {
+__device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, int c0, int xe, float c, float* gath,
+                                                RefState& st) {
   constexpr int kPer = Elem<DT>::kPerVec;
   const int lane0 = (threadIdx.x & 63) * kPer;   // first logit of the lane's vector 0
   if constexpr (MODE == kOneHot || MODE == kExplicit) {
@@ -539,27 +599,53 @@ __device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, int c0, int xe, flo
       }
     }
     touch(r);
-    // lane: sum of 2^(y - m_lane); wave: rescale each lane once to the
-    // wave's max and add.
-    float mx = kNegInf;
+    const bool seeded = st.first;                 // uniform: the references move
+    if (seeded) {
+      // seed each lane's reference with the largest logit of its first vector
+      float m0 = kNegInf;
 #pragma unroll
-    for (int j = 0; j < kLoadsPerLane; ++j)
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) mx = fmaxf(mx, raw_elem<DT>(r, j, k));
-    const float msub = (mx == kNegInf) ? 0.f : mx * c;
+      for (int k = 0; k < kPer; ++k) m0 = fmaxf(m0, raw_elem<DT>(r, 0, k));
+      st.ref = m0 * c;                            // -inf stays -inf
+      st.first = false;
+    }
+    // One pass: sum 2^(y - ref). A lane with no finite reference yet gets
+    // NaN or inf here, and one with a logit more than 64 above its
+    // reference gets a sum above 2^64: both recount exactly below.
     float acc[kLoadsPerLane];
 #pragma unroll
     for (int j = 0; j < kLoadsPerLane; ++j) {
       acc[j] = 0.f;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) acc[j] += fast_exp2(fmaf(raw_elem<DT>(r, j, k), c, -msub));
+      for (int k = 0; k < kPer; ++k) acc[j] += fast_exp2(fmaf(raw_elem<DT>(r, j, k), c, -st.ref));
     }
     float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    const float wmx = wave_max_all(mx);
-    const float m = (wmx == kNegInf) ? kNegInf : wmx * c;
-    s = (mx == kNegInf) ? 0.f : s * fast_exp2(msub - m);
-    s = wave_sum_all(s);
-    return make_float2(m, s);
+    const bool recount = !(s <= 0x1p64f);
+    if (seeded || __ballot(recount) != 0ull) {    // uniform branch, rare after the first chunk
+      if (recount) {
+        touch(r);                                 // reconvert rather than keep 32 values live
+        float mx = kNegInf;
+#pragma unroll
+        for (int j = 0; j < kLoadsPerLane; ++j)
+#pragma unroll
+          for (int k = 0; k < kPer; ++k) mx = fmaxf(mx, raw_elem<DT>(r, j, k));
+        st.ref = fmaxf(st.ref, mx * c);
+        touch(r);
+        s = 0.f;
+        if (st.ref != kNegInf) {
+#pragma unroll
+          for (int j = 0; j < kLoadsPerLane; ++j) {
+            acc[j] = 0.f;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) acc[j] += fast_exp2(fmaf(raw_elem<DT>(r, j, k), c, -st.ref));
+          }
+          s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        }
+      }
+      st.M = wave_max_all(st.ref);
+      st.f = (st.ref == kNegInf) ? 0.f : fast_exp2(st.ref - st.M);
+    }
+    s = wave_sum_all(s * st.f);
+    return make_float2(st.M, s);
   } else {
     float best = raw_elem<DT>(r, 0, 0);
     int bi = c0 + lane0;
@@ -594,10 +680,12 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   // Partials collect in LDS and leave in one store at the end: no global
   // store sits between the chunk loads.
   __shared__ float2 s_part[kMaxChunksPerWg];
+  __shared__ float2 s_unif[SV_MAX_DRAFT + 1];
   float* gath = A.gath + rowg;
 
   int ch = c_lo + wave;
   const int ch_end = kVec ? min(c_hi, A.n_full) : c_lo;
+  RefState rs;
   const bool piped = ch < ch_end;
   ChunkRaw ra, rb;
   if (piped) issue_chunk<DT>(row, (int64_t)ch * kCE, ra);   // first loads before anything else
@@ -611,6 +699,14 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
     const int i = r < A.R ? r : r - A.R;
     if (i < A.K) xe = A.tokens[(int64_t)b * A.K + i];
     c = kLog2e / A.temperature[b];
+    // The two uniforms of every position i <= K of request b, one lane per
+    // position: drawn by one wave of the last (shortest) workgroup of the
+    // request's first row while its first loads are in flight, and left for
+    // the tail, which would otherwise wait on this chain of 64-bit multiplies.
+    if (r == 0 && wi == A.wpr - 1 && wave == 0 && lane < A.R) {
+      const Philox4 rnd = philox4x64_10((uint64_t)lane, (uint64_t)b, A.offset, 0ull, A.seeds[b], 0ull);
+      s_unif[lane] = make_float2(top24(rnd.w0), top24(rnd.w1));
+    }
   }
 
   if (piped) {
@@ -623,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
       issue_chunk<DT>(row, (int64_t)(more ? nx : ch) * kCE, rb);
       __builtin_amdgcn_sched_barrier(0);           // keep the prefetch ahead of the math
       {
-        const float2 res = chunk_partial<MODE, DT>(ra, ch * kCE, xe, c, gath);
+        const float2 res = chunk_partial<MODE, DT>(ra, ch * kCE, xe, c, gath, rs);
         if (lane == 0) s_part[ch - c_lo] = res;
       }
       ch = nx;
@@ -633,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
       issue_chunk<DT>(row, (int64_t)(more ? nx : ch) * kCE, ra);
       __builtin_amdgcn_sched_barrier(0);
       {
-        const float2 res = chunk_partial<MODE, DT>(rb, ch * kCE, xe, c, gath);
+        const float2 res = chunk_partial<MODE, DT>(rb, ch * kCE, xe, c, gath, rs);
         if (lane == 0) s_part[ch - c_lo] = res;
       }
       ch = nx;
@@ -643,12 +739,15 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   for (; ch < c_hi; ch += kWaves) {               // checked path
     ChunkRaw rr;
     load_chunk_checked<DT, kVec>(row, (int64_t)ch * kCE, A.V, rr);
-    const float2 res = chunk_partial<MODE, DT>(rr, ch * kCE, xe, c, gath);
+    const float2 res = chunk_partial<MODE, DT>(rr, ch * kCE, xe, c, gath, rs);
     if (lane == 0) s_part[ch - c_lo] = res;
   }
   __syncthreads();
   float2* part = A.part + (int64_t)rowg * A.n_chunk;
   for (int i = tid; i < c_hi - c_lo; i += kThreads) part[c_lo + i] = s_part[i];
+  if (MODE == kOneHot || MODE == kExplicit) {
+    if (r == 0 && wi == A.wpr - 1 && tid < A.R) A.unif[(int64_t)b * A.R + tid] = s_unif[tid];
+  }
   // wave 0 also folds the workgroup's partials into one, so the tail merges
   // wpr values per row instead of n_chunk
   if (wave == 0) {
@@ -779,11 +878,12 @@ using namespace sv;
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t part, wpart, gath, rec, res, total;
+  size_t part, wpart, gath, rec, res, unif, total;
 };
 
 // Workspace: [counters: 4 * SV_MAX_BATCH][chunk partials][workgroup
 //            partials][gathered logits][records][residual partials]
+//            [uniforms]
 Layout layout(int64_t B, int64_t rows, int64_t V) {
   const int64_t ce = Chunk<kF32>::kElems;          // the smaller chunk: a bound for both dtypes
   const int64_t nch = (V + ce - 1) / ce;
@@ -793,7 +893,8 @@ Layout layout(int64_t B, int64_t rows, int64_t V) {
   L.gath = align_up(L.wpart + (size_t)(B * rows * nch) * sizeof(float2), 256);   // wpr <= nch
   L.rec = align_up(L.gath + (size_t)(B * rows) * sizeof(float), 256);
   L.res = align_up(L.rec + (size_t)B * sizeof(Record), 256);
-  L.total = align_up(L.res + (size_t)(B * nch) * sizeof(float), 256);
+  L.unif = align_up(L.res + (size_t)(B * nch) * sizeof(float), 256);
+  L.total = align_up(L.unif + (size_t)(B * rows) * sizeof(float2), 256);   // R <= rows
   return L;
 }
 
@@ -813,20 +914,21 @@ bool aligned16(const sv_logits* d) {
          ((d->stride_k * es) % 16 == 0);
 }
 
-// Chunks per workgroup: enough workgroups to keep every CU busy through
-// the launch (about 4096), each long enough that its four waves stream
-// several chunks apiece. SPECVERIFY_CHUNKS_PER_WG overrides (tuning).
+// Chunks per workgroup: about 8192 workgroups, so the launch fills the chip
+// in several whole rounds of resident workgroups (fewer, longer runs leave
+// the last round a fraction full), at least one chunk per wave, and the runs
+// of one row balanced (a 63-chunk row splits 11x5 + 8, not 12x5 + 3). SPECVERIFY_CHUNKS_PER_WG overrides the
+// target run length (tuning).
 int chunks_per_wg(int64_t rows_total, int n_chunk) {
   static const int env = [] {
     const char* e = getenv("SPECVERIFY_CHUNKS_PER_WG");
     return e ? atoi(e) : 0;
   }();
-  int64_t cpw = env > 0 ? env : (rows_total * n_chunk + 4095) / 4096;
-  cpw = (cpw + kWaves - 1) / kWaves * kWaves;
-  if (cpw < kWaves) cpw = kWaves;
-  if (cpw > kMaxChunksPerWg) cpw = kMaxChunksPerWg;
-  if (cpw > n_chunk) cpw = n_chunk;
-  return (int)cpw;
+  int64_t target = env > 0 ? env : (rows_total * n_chunk + 8191) / 8192;
+  if (target < kWaves) target = kWaves;
+  if (target > kMaxChunksPerWg) target = kMaxChunksPerWg;
+  const int64_t wpr = (n_chunk + target - 1) / target;
+  return (int)((n_chunk + wpr - 1) / wpr);
 }
 
 void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int rows, void* ws) {
@@ -849,6 +951,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.gath = reinterpret_cast<float*>(base + L.gath);
   A.rec = reinterpret_cast<Record*>(base + L.rec);
   A.res_part = reinterpret_cast<float*>(base + L.res);
+  A.unif = reinterpret_cast<float2*>(base + L.unif);
   A.out_p = nullptr; A.out_q = nullptr; A.out_aux = nullptr;
   A.temperature = nullptr; A.seeds = nullptr; A.offset = 0;
   A.n_nodes = 0;
