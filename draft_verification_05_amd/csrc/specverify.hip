@@ -76,18 +76,15 @@ struct Args {
   float2* unif;         // [B * R]: (u_accept, u_sample) of each position
   int n_nodes;
   int8_t parent[SV_MAX_TREE_NODES];
+  int8_t depth[SV_MAX_TREE_NODES];   // depth of each node (root 0)
 };
 
 // The tail keeps a request's partials in LDS when they fit, so the draw
 // can locate its chunk without another trip to memory.
 constexpr int kPartCache = 1024;
-// Per-workgroup partials of one request the tail stages in one batch of
-// loads (8 per lane); more fall back to direct loads.
-constexpr int kWPartCache = 512;
 
 struct TailLds {
   float2 pcache[kPartCache];
-  float2 wcache[kWPartCache];
   float rowM[kMaxRows], rowS[kMaxRows];
   int x[SV_MAX_TREE_NODES], g[SV_MAX_TREE_NODES], path[SV_MAX_TREE_NODES];
   int depth[SV_MAX_TREE_NODES];
@@ -160,6 +157,21 @@ __device__ inline bool last_of_request(unsigned* counter, unsigned n, int* s_las
 template <class WFn>
 __device__ float wave_locate(int n, float u, WFn W, int* found, float* t_in) {
   const int lane = threadIdx.x & 63;
+  if (n <= 64) {                                   // one weight per lane: a single pass
+    const float w = lane < n ? W(lane) : 0.f;
+    const float Z = wave_sum_all(w);
+    const float t = u * Z;
+    const float incl = wave_scan_incl(w);
+    const int hit = first_lane(lane < n && incl > t && w > 0.f);
+    if (hit >= 0) {
+      *found = hit;
+      *t_in = t - lane_f(incl - w, hit);
+    } else {
+      *found = last_lane(w > 0.f);
+      *t_in = __builtin_inff();
+    }
+    return Z;
+  }
   float Z = 0.f;
   for (int base = 0; base < n; base += 64) {
     const int s = base + lane;
@@ -302,54 +314,60 @@ __device__ bool stage_commit(const Args& A, int b, TailLds& S, Staged& t) {
 }
 
 
-// The row pass's per-workgroup partials of a request, wpr per row: issued
-// as one batch of independent loads (8 per lane) at the start of the tail,
-// parked in LDS, then merged by one lane per row. Requests with more than
-// kWPartCache of them read them straight from the workspace instead.
-struct WStaged { float2 v[8]; };
+// The row pass's per-workgroup partials of a request, wpr per row, loaded
+// in one batch at the start of the tail: row rr's partials sit in a group
+// of G lanes (G = wpr rounded up to a power of two, 64 / G rows per load,
+// padded with the merge's identity), so every row merges at once with
+// segmented reductions. Requests that would need more than 8 loads per
+// lane merge serially from the workspace instead.
+struct WStaged { float2 v[8]; int G, per, passes; };
 
-__device__ inline void wstage_issue(const Args& A, int b, int n_rows, WStaged& t) {
+__device__ inline void wstage_issue(const Args& A, int b, int n_rows, float2 identity, WStaged& t) {
   const int lane = threadIdx.x & 63;
-  const int n = n_rows * A.wpr;
-  if (n > kWPartCache) return;
+  int G = 1;
+  while (G < A.wpr && G < 128) G <<= 1;
+  t.G = G;
+  t.per = G <= 64 ? 64 / G : 0;
+  t.passes = t.per > 0 ? (n_rows + t.per - 1) / t.per : 0;
+  if (t.per == 0 || t.passes > 8) { t.passes = 0; return; }
   const float2* wp = A.wpart + (int64_t)b * A.rows * A.wpr;
+  const int w = lane & (G - 1), rsub = lane / G;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int i = q * 64 + lane;
-    if (i < n) t.v[q] = wp[i];
+    const int rr = q * t.per + rsub;
+    t.v[q] = identity;
+    if (q < t.passes && rr < n_rows && w < A.wpr) t.v[q] = wp[rr * A.wpr + w];
   }
-}
-
-// Partial w of row rr: from LDS when staged.
-__device__ inline float2 wpartial(const Args& A, int b, int rr, int w, const TailLds& S, bool staged) {
-  return staged ? S.wcache[rr * A.wpr + w] : A.wpart[((int64_t)b * A.rows + rr) * A.wpr + w];
-}
-
-__device__ inline bool wstage_commit(const Args& A, int n_rows, TailLds& S, const WStaged& t) {
-  const int lane = threadIdx.x & 63;
-  const int n = n_rows * A.wpr;
-  if (n > kWPartCache) return false;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int i = q * 64 + lane;
-    if (i < n) S.wcache[i] = t.v[q];
-  }
-  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
-  return true;
 }
 
 // Per-row (max, sum) into S.rowM / S.rowS.
 __device__ void merge_softmax_rows(const Args& A, int b, TailLds& S, const WStaged& t) {
   const int lane = threadIdx.x & 63;
-  const bool staged = wstage_commit(A, A.rows, S, t);
-  for (int rr = lane; rr < A.rows; rr += 64) {
-    float m = kNegInf, s = 0.f;
-    for (int w = 0; w < A.wpr; ++w) {
-      const float2 v = wpartial(A, b, rr, w, S, staged);
-      ms_merge(m, s, v.x, v.y);
+  if (t.passes > 0) {
+    const int rsub = lane / t.G;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q < t.passes) {                          // uniform: all lanes take part
+        float m = t.v[q].x, s = t.v[q].y;
+        seg_reduce_ms(t.G, m, s);
+        const int rr = q * t.per + rsub;
+        if ((lane & (t.G - 1)) == 0 && rr < A.rows) {
+          S.rowM[rr] = m;
+          S.rowS[rr] = s;
+        }
+      }
     }
-    S.rowM[rr] = m;
-    S.rowS[rr] = s;
+  } else {
+    const float2* wp = A.wpart + (int64_t)b * A.rows * A.wpr;
+    for (int rr = lane; rr < A.rows; rr += 64) {
+      float m = kNegInf, s = 0.f;
+      for (int w = 0; w < A.wpr; ++w) {
+        const float2 v = wp[rr * A.wpr + w];
+        ms_merge(m, s, v.x, v.y);
+      }
+      S.rowM[rr] = m;
+      S.rowS[rr] = s;
+    }
   }
   __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
 }
@@ -357,15 +375,29 @@ __device__ void merge_softmax_rows(const Args& A, int b, TailLds& S, const WStag
 // Per-row argmax into S.g.
 __device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, const WStaged& t) {
   const int lane = threadIdx.x & 63;
-  const bool staged = wstage_commit(A, n_rows, S, t);
-  for (int rr = lane; rr < n_rows; rr += 64) {
-    float v = kNegInf;
-    int idx = INT_MAX;
-    for (int w = 0; w < A.wpr; ++w) {
-      const float2 p = wpartial(A, b, rr, w, S, staged);
-      am_step(v, idx, p.x, __float_as_int(p.y));
+  if (t.passes > 0) {
+    const int rsub = lane / t.G;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q < t.passes) {                          // uniform: all lanes take part
+        float v = t.v[q].x;
+        int idx = __float_as_int(t.v[q].y);
+        seg_reduce_am(t.G, v, idx);
+        const int rr = q * t.per + rsub;
+        if ((lane & (t.G - 1)) == 0 && rr < n_rows) S.g[rr] = idx;
+      }
     }
-    S.g[rr] = idx;
+  } else {
+    const float2* wp = A.wpart + (int64_t)b * A.rows * A.wpr;
+    for (int rr = lane; rr < n_rows; rr += 64) {
+      float v = kNegInf;
+      int idx = INT_MAX;
+      for (int w = 0; w < A.wpr; ++w) {
+        const float2 p = wp[rr * A.wpr + w];
+        am_step(v, idx, p.x, __float_as_int(p.y));
+      }
+      S.g[rr] = idx;
+    }
   }
   __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
 }
@@ -389,7 +421,7 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   float2 un = make_float2(0.f, 0.f);
   if (lane <= K) un = A.unif[(int64_t)b * R + lane];
   WStaged ws;
-  wstage_issue(A, b, A.rows, ws);
+  wstage_issue(A, b, A.rows, make_float2(kNegInf, 0.f), ws);
   Staged st;
   stage_issue(A, b, st);
   const float uacc = un.x, usmp = un.y;   // drawn by the row pass
@@ -407,7 +439,7 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
     return;
   }
   const float c = kLog2e / T;
-  float p = 0.f, q = 0.f, Mx = kNegInf;
+  float p = 0.f, q = 0.f, Mx = kNegInf, lp = kNegInf, lq = kNegInf;
   if (lane < K) {
     const bool valid = (unsigned)x < (unsigned)V;
     if (!valid) { lx = kNegInf; ld = kNegInf; }
@@ -423,14 +455,22 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
     } else {
       const float Mp = S.rowM[lane], Sp = S.rowS[lane];
       const float Mq = S.rowM[R + lane], Sq = S.rowS[R + lane];
-      p = (valid && Sp > 0.f) ? fast_exp2(fmaf(lx, c, -Mp)) / Sp : 0.f;
-      q = (valid && Sq > 0.f) ? fast_exp2(fmaf(ld, c, -Mq)) / Sq : 0.f;
+      const float dp = fmaf(lx, c, -Mp), dq = fmaf(ld, c, -Mq);
+      p = (valid && Sp > 0.f) ? fast_exp2(dp) / Sp : 0.f;
+      q = (valid && Sq > 0.f) ? fast_exp2(dq) / Sq : 0.f;
+      // log2 p and log2 q: finite where p and q underflow fp32 (both can, for
+      // improbable drafts), so the test below keeps the ratio p / q
+      lp = (valid && Sp > 0.f) ? dp - __log2f(Sp) : kNegInf;
+      lq = (valid && Sq > 0.f) ? dq - __log2f(Sq) : kNegInf;
     }
     if (A.out_p) A.out_p[(int64_t)b * K + lane] = p;
     if (A.out_q) A.out_q[(int64_t)b * K + lane] = q;
   }
-  // the first position whose draft is rejected, K if none
-  const int rej = first_lane(lane < K && !(uacc * q < p));
+  // the first position whose draft is rejected (u q >= p), K if none; with
+  // draft logits the test is log2 u + log2 q < log2 p (log2 0 = -inf)
+  const bool accept = MODE == kOneHot ? (uacc * q < p)
+                                      : (__log2f(uacc) + lq < lp);
+  const int rej = first_lane(lane < K && !accept);
   const int a = rej < 0 ? K : rej;
   if (lane <= K && lane != a) otok[lane] = lane < a ? x : -1;
   if (lane == 0) A.out_len[b] = a + 1;
@@ -459,7 +499,7 @@ __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63, K = A.K;
   const int x = lane < K ? A.tokens[(int64_t)b * K + lane] : -1;
   WStaged ws;
-  wstage_issue(A, b, A.rows, ws);
+  wstage_issue(A, b, A.rows, make_float2(kNegInf, __int_as_float(INT_MAX)), ws);
   merge_argmax_rows(A, b, A.rows, S, ws);
   const int g = lane <= K ? S.g[lane] : -1;
   const int mis = first_lane(lane < K && x != g);
@@ -471,39 +511,42 @@ __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
   if (lane == 0) A.out_len[b] = a + 1;
 }
 
+// The tree's acceptance in parallel, one lane per node: a node is accepted
+// when its token is its parent's argmax and its parent is accepted, settled
+// one depth level at a time; the answer is the deepest accepted node (the
+// lowest index among equals), and its root path is read off the parents.
 __device__ void tree_tail(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63, N = A.n_nodes;
   const int xn = lane < N ? A.tokens[(int64_t)b * N + lane] : -1;
   WStaged ws;
-  wstage_issue(A, b, N, ws);
-  if (lane < N) S.x[lane] = xn;
+  wstage_issue(A, b, N, make_float2(kNegInf, __int_as_float(INT_MAX)), ws);
+  const int par = lane < N ? A.parent[lane] : -1;
+  const int dep = lane < N ? A.depth[lane] : 0;
   merge_argmax_rows(A, b, N, S, ws);
+  const int g_par = S.g[par < 0 ? 0 : par];
+  const bool ok = lane == 0 || (lane < N && xn == g_par);
+  const int max_depth = (int)wave_max_all((float)dep);
+  int acc = lane == 0 ? 1 : 0;
+  for (int d = 1; d <= max_depth; ++d) {           // uniform: all lanes take part
+    const int pacc = __shfl(acc, par < 0 ? 0 : par);
+    if (dep == d) acc = (ok && pacc) ? 1 : 0;
+  }
+  // deepest accepted node, lowest index among equals: key depth * 128 + 127 - node
+  const int key = (lane < N && acc) ? dep * 128 + (127 - lane) : 0;
+  const int kmax = (int)wave_max_all((float)key);
+  const int best = 127 - (kmax & 127), len = kmax >> 7;
+  uint64_t on_path = 0ull;
+  for (int n = best; n > 0; n = A.parent[n]) on_path |= 1ull << n;
+  // each position once: path nodes fill 0..len-1 (one node per depth), then
+  // the argmax at the deepest node, then -1
+  int32_t* out = A.out_tokens + (int64_t)b * A.out_cols;
+  if (lane > 0 && lane < N && ((on_path >> lane) & 1ull)) out[dep - 1] = xn;
+  if (lane == len) out[len] = S.g[best];
+  if (lane > len && lane < N) out[lane] = -1;
   if (lane == 0) {
-    uint64_t acc = 1ull;
-    int best = 0;
-    S.depth[0] = 0;
-    for (int n = 1; n < N; ++n) {
-      const int p = A.parent[n];
-      S.depth[n] = S.depth[p] + 1;
-      if (((acc >> p) & 1ull) && S.x[n] == S.g[p]) {
-        acc |= 1ull << n;
-        if (S.depth[n] > S.depth[best]) best = n;
-      }
-    }
-    const int len = S.depth[best];
-    int n = best;
-    for (int pos = len - 1; pos >= 0; --pos) {
-      S.path[pos] = S.x[n];
-      n = A.parent[n];
-    }
-    S.path[len] = S.g[best];
-    S.depth[SV_MAX_TREE_NODES - 1] = len;       // hand the length to the other lanes
     A.out_len[b] = len + 1;
     if (A.out_aux) A.out_aux[b] = best;
   }
-  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
-  const int len = S.depth[SV_MAX_TREE_NODES - 1];
-  if (lane < N) A.out_tokens[(int64_t)b * A.out_cols + lane] = lane <= len ? S.path[lane] : -1;
 }
 
 // ------------------------------------------------------------ row pass ---
@@ -955,7 +998,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.out_p = nullptr; A.out_q = nullptr; A.out_aux = nullptr;
   A.temperature = nullptr; A.seeds = nullptr; A.offset = 0;
   A.n_nodes = 0;
-  for (int i = 0; i < SV_MAX_TREE_NODES; ++i) A.parent[i] = -1;
+  for (int i = 0; i < SV_MAX_TREE_NODES; ++i) { A.parent[i] = -1; A.depth[i] = 0; }
 }
 
 #define SV_LAUNCH(KERNEL, grid, st, A) \
@@ -1142,7 +1185,10 @@ int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
   A.out_len = out_accept_len;
   A.out_aux = out_best_node;
   A.n_nodes = N;
-  for (int n = 0; n < N; ++n) A.parent[n] = (int8_t)parents[n];
+  for (int n = 0; n < N; ++n) {
+    A.parent[n] = (int8_t)parents[n];
+    A.depth[n] = (int8_t)(n == 0 ? 0 : A.depth[parents[n]] + 1);   // parents[n] < n
+  }
   const int64_t wgs = (int64_t)B * N * A.wpr;
   if ((st = check_grid(wgs))) return st;
   launch_rows<kTree>(A, target->dtype, aligned16(target), (unsigned)wgs,

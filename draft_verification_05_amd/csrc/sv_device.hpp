@@ -224,6 +224,15 @@ __device__ inline int lane_i(int v, int l) { return __builtin_amdgcn_readlane(v,
 __device__ inline void am_step(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
+__device__ inline void seg_reduce_am(int S, float& v, int& i) {
+  if (S >= 2) am_step(v, i, dpp_f<kDppXor1>(v), dpp_i<kDppXor1>(i));
+  if (S >= 4) am_step(v, i, dpp_f<kDppXor2>(v), dpp_i<kDppXor2>(i));
+  if (S >= 8) am_step(v, i, dpp_f<kDppHalfMirror>(v), dpp_i<kDppHalfMirror>(i));
+  if (S >= 16) am_step(v, i, dpp_f<kDppMirror>(v), dpp_i<kDppMirror>(i));
+  if (S >= 32) am_step(v, i, __shfl_xor(v, 16), __shfl_xor(i, 16));
+  if (S >= 64) am_step(v, i, __shfl_xor(v, 32), __shfl_xor(i, 32));
+}
+
 template <int kCtrl>
 __device__ inline void am_dpp(float& v, int& i) {
   const float v2 = dpp_f<kCtrl>(v);
@@ -251,6 +260,21 @@ __device__ inline void ms_merge(float& m, float& s, float m2, float s2) {
   if (mn == kNegInf) { m = mn; s = 0.f; return; }
   s = s * fast_exp2(m - mn) + s2 * fast_exp2(m2 - mn);
   m = mn;
+}
+
+// Segmented reductions over aligned groups of S consecutive lanes (S a
+// power of two, uniform): every lane of a group ends with its group's
+// result. Within a row of 16 lanes the butterfly runs on DPP (quad
+// permutes, half-row mirror, row mirror); wider groups add lane shuffles.
+// Every lane of the wave must be active.
+__device__ inline void seg_reduce_ms(int S, float& m, float& s) {
+  float m2, s2;
+  if (S >= 2) { m2 = dpp_f<kDppXor1>(m); s2 = dpp_f<kDppXor1>(s); ms_merge(m, s, m2, s2); }
+  if (S >= 4) { m2 = dpp_f<kDppXor2>(m); s2 = dpp_f<kDppXor2>(s); ms_merge(m, s, m2, s2); }
+  if (S >= 8) { m2 = dpp_f<kDppHalfMirror>(m); s2 = dpp_f<kDppHalfMirror>(s); ms_merge(m, s, m2, s2); }
+  if (S >= 16) { m2 = dpp_f<kDppMirror>(m); s2 = dpp_f<kDppMirror>(s); ms_merge(m, s, m2, s2); }
+  if (S >= 32) { m2 = __shfl_xor(m, 16); s2 = __shfl_xor(s, 16); ms_merge(m, s, m2, s2); }
+  if (S >= 64) { m2 = __shfl_xor(m, 32); s2 = __shfl_xor(s, 32); ms_merge(m, s, m2, s2); }
 }
 
 __device__ inline void wave_reduce_ms(float& m, float& s) {

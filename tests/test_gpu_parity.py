@@ -261,3 +261,104 @@ def test_chain_tree_equals_greedy_on_gpu():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(t_len.cpu().numpy(), g_len.cpu().numpy())
     np.testing.assert_array_equal(t_tok.cpu().numpy(), g_tok.cpu().numpy())
+
+
+# ------------------------------------------- numerical stress, merge paths ---
+def test_sample_low_temperature_recounts():
+    """T = 0.05 turns N(0, 2) logits into scaled logits that span about +-170
+    (log2 units): most chunks hold logits more than 64 above a lane's first
+    vector, so the row pass recounts them against a raised reference."""
+    wl = make("c3_onehot", data_seed=30, B=16, V=2 * 8192 + 1232)
+    T = np.full(16, 0.05, np.float32)
+    T[::3] = 0.02
+    check_sample(dict(wl, temperature=T), "c3 T=0.05")
+    # explicit drafts are redrawn from q at the new temperature (Gumbel-max),
+    # as the method assumes: x ~ q
+    wl2 = make("c2_stoch", data_seed=31, B=12, V=20001)
+    T2 = np.full(12, 0.05, np.float32)
+    y = oracle.logits_f64(wl2["draft"].reshape(-1), "f32").reshape(wl2["draft"].shape) / 0.05
+    tok2 = np.argmax(y + np.random.default_rng(39).gumbel(size=y.shape), -1).astype(np.int32)
+    check_sample(dict(wl2, temperature=T2, draft_tokens=tok2), "c2 T=0.05 explicit")
+
+
+def test_sample_explicit_underflowing_probabilities():
+    """Drafts whose target and draft probabilities both lie far below the
+    fp32 range (e^-100, e^-110): the acceptance must follow the ratio p / q
+    (e^10: always accept; e^-0.5: accept when u < 0.61), not the underflowed
+    values."""
+    B, K, V = 8, 2, 3000
+    wl = make("c2_stoch", data_seed=40, B=B, K=K, V=V)
+    rng = np.random.default_rng(41)
+    tgt = rng.normal(0, 1, (B, K + 1, V)).astype(np.float32)
+    drf = rng.normal(0, 1, (B, K, V)).astype(np.float32)
+    tok = rng.integers(0, V, (B, K)).astype(np.int32)
+    for b in range(B):
+        for i in range(K):
+            tgt[b, i, tok[b, i]] = -100.0
+            drf[b, i, tok[b, i]] = -110.0 if b % 2 == 0 else -99.5
+    wl = dict(wl, target=tgt, draft=drf, draft_tokens=tok, temperature=np.ones(B, np.float32))
+    rep = check_sample(wl, "explicit underflow")
+    g_tok, g_len, _, _ = run_sample(wl)
+    assert np.all(g_len[0::2] == K + 1)            # ratio e^10: every draft accepted
+
+
+def test_sample_huge_logit_spreads():
+    """Rows built to break a running reference: ramps over +-300, isolated
+    spikes 150 above the rest, whole -inf vectors before finite logits, a
+    row offset by -1000, and -200 / +200 blocks inside and across lanes."""
+    B, V = 8, 9000
+    wl = make("c3_onehot", data_seed=32, B=B, V=V)
+    rng = np.random.default_rng(33)
+    x = rng.normal(0, 2, (B, 6, V))
+    x[0] = -300.0 + 600.0 * np.arange(V) / V
+    spikes = rng.integers(0, V, (6, 5))
+    for r in range(6):
+        x[1, r, spikes[r]] = 150.0
+    x[2, :, :2048] = -np.inf
+    x[3, :, :512] = -np.inf
+    x[3, :, 600] = 100.0
+    x[4] = -1000.0 + rng.normal(0, 2, (6, V))
+    # 512-logit blocks: a lane's first vector is -200 and its second +200
+    x[5] = np.where((np.arange(V) // 512) % 2 == 0, -200.0, 200.0) + rng.normal(0, 1, (6, V))
+    x[6, :, : V // 2] = -np.inf
+    # 8-logit blocks: neighbouring lanes alternate -200 / +200
+    x[7] = np.where((np.arange(V) // 8) % 2 == 0, -200.0, 200.0) + rng.normal(0, 1, (6, V))
+    bits = f32_to_bf16_bits(x.astype(np.float32))
+    tok = wl["draft_tokens"].copy()
+    tok[1, :] = spikes[:5, 0]                      # drafts on the spikes: p near 1
+    tok[5, :] = 600                                # inside a +200 block
+    check_sample(dict(wl, target=bits, draft_tokens=tok, temperature=np.ones(B, np.float32)),
+                 "c3 huge spreads")
+
+
+def test_merge_serial_fallback_many_rows():
+    """33 rows with 32 workgroups each need 17 staged loads per lane, more
+    than the tail's 8: the row merges take the serial path."""
+    check_greedy(make("c4_greedy", data_seed=34, B=2, K=32, V=131072), "greedy K=32 V=131072")
+    wl = make("c3_onehot", data_seed=35, B=2, K=32, V=262144)
+    check_sample(wl, "c3 K=32 V=262144")
+
+
+def test_merge_serial_fallback_wide_rows():
+    """A 2^20-logit vocabulary: more than 64 workgroups per row."""
+    wl = make("c3_onehot", data_seed=36, B=2, K=0, V=1 << 20)
+    check_sample(wl, "c3 K=0 V=2^20")
+    check_greedy(make("c4_greedy", data_seed=37, B=2, K=1, V=1 << 20), "greedy K=1 V=2^20")
+
+
+def test_tree_deep_chain():
+    """A 64-node chain: acceptance settles over 63 depth levels."""
+    N, B, V = 64, 8, 5000
+    rng = np.random.default_rng(38)
+    parents = np.arange(-1, N - 1, dtype=np.int32)
+    tgt = rng.normal(0, 1, (B, N, V)).astype(np.float32)
+    g = tgt.argmax(-1)
+    tok = np.empty((B, N), np.int32)
+    tok[:, 0] = -1
+    tok[:, 1:] = g[:, :-1]                          # every node accepted ...
+    for b in range(B):                              # ... up to a per-request break
+        cut = int(rng.integers(1, N + 8))
+        if cut < N:
+            tok[b, cut] = (g[b, cut - 1] + 1) % V
+    wl = dict(target=tgt, draft_tokens=tok, B=B, V=V, dtype="f32", seeds=np.zeros(B, np.uint64))
+    check_tree(wl, parents, "tree chain N=64")
