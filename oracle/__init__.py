@@ -14,6 +14,9 @@ Parity pins (each checked by ``tests/test_oracle_*.py`` without a GPU):
     the target's (the pages' exactness guarantee), chi-square at 10^6 trials.
   * greedy: argmax-prefix properties, and the sampling rule's T -> 0 limit.
   * tree: a chain tree equals greedy; brute-force path enumeration.
+  * ragged batches: every request equals the dense rule on its own rows with
+    the same uniforms, whatever the mix of draft counts; bad offsets refuse
+    only their own request.
 Parity unpinned: individual draws whose uniform lies within 1e-5 of an
 acceptance threshold or CDF boundary (the GPU works in fp32); they are
 counted by the parity tests, not matched.

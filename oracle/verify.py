@@ -63,6 +63,7 @@ __all__ = [
     "logits_f64", "softmax_t", "onehot", "accept_length", "residual_weights",
     "inverse_cdf", "verify_request", "spec_verify_sample", "argmax_lowest",
     "spec_verify_greedy", "tree_depths", "spec_verify_tree",
+    "ragged_draft_count", "spec_verify_sample_ragged", "spec_verify_greedy_ragged",
 ]
 
 
@@ -193,6 +194,99 @@ def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0
         if keep_trace:
             traces[b] = res
     return tokens, accept_len, p_draft, q_draft, traces
+
+
+# ----------------------------------------------------- ragged batches ---
+# Requests with their own draft counts K_b ([FD] "高效投机解码框架设计": one
+# forward verifies variable-length queries, and virtual padding maps each
+# output row back to its request; [VA] suffix decoding proposes an adaptive
+# number of tokens per request; [SD] §10.2 adjusts K per request). Rows are
+# packed: with cu[b] = K_0 + ... + K_{b-1}, request b's K_b + 1 target rows
+# are rows cu[b] + b ... cu[b] + b + K_b, its draft rows and tokens start at
+# cu[b]. The rule per request is the dense one.
+
+def ragged_draft_count(cu, b, total_k, k_max):
+    """K_b of request b, or None when its offsets are out of order or range."""
+    c0, c1 = int(cu[b]), int(cu[b + 1])
+    if not (0 <= c0 <= c1 <= total_k and c1 - c0 <= k_max):
+        return None
+    return c1 - c0
+
+
+def spec_verify_sample_ragged(target_rows, draft_rows, cu, draft_tokens, temperature, seeds,
+                              offset=0, k_max=None, target_dtype="f32", draft_dtype="f32",
+                              keep_trace=False):
+    """Stochastic verification of a ragged batch.
+
+    target_rows [total_k + B, V], draft_rows [total_k, V] or None (one-hot q),
+    cu [B + 1] prefix sums of the draft counts, draft_tokens [total_k].
+    Uniforms are keyed by (seed_b, b, position) exactly as in the dense case.
+    Returns (tokens [B, k_max + 1], accept_len [B], p_draft [total_k],
+    q_draft [total_k], traces). A request with bad offsets or a temperature
+    that is not finite and positive is refused (accept_len 0, tokens -1).
+    """
+    B = len(cu) - 1
+    total_k = len(draft_tokens)
+    if k_max is None:
+        k_max = max([0] + [int(cu[b + 1]) - int(cu[b]) for b in range(B)])
+    V = target_rows.shape[1]
+    tokens = np.full((B, k_max + 1), -1, dtype=np.int32)
+    accept_len = np.zeros(B, dtype=np.int32)
+    p_draft = np.zeros(total_k, dtype=np.float64)
+    q_draft = np.zeros(total_k, dtype=np.float64)
+    traces = {}
+    for b in range(B):
+        K = ragged_draft_count(cu, b, total_k, k_max)
+        T = float(temperature[b])
+        if K is None or not (math.isfinite(T) and T > 0):
+            continue
+        c0 = int(cu[b])
+        p_rows = [softmax_t(logits_f64(target_rows[c0 + b + i], target_dtype), T).tolist()
+                  for i in range(K + 1)]
+        x = [int(v) for v in draft_tokens[c0:c0 + K]]
+        if draft_rows is not None:
+            q_rows = [softmax_t(logits_f64(draft_rows[c0 + i], draft_dtype), T).tolist()
+                      for i in range(K)]
+        else:
+            q_rows = [onehot(V, x[i]) for i in range(K)]
+        pairs = [request_uniforms(int(seeds[b]), b, i, int(offset)) for i in range(K + 1)]
+        res = verify_request(p_rows, q_rows, x, [u for u, _ in pairs], [u for _, u in pairs])
+        tokens[b, :res["accept_len"]] = res["tokens"]
+        accept_len[b] = res["accept_len"]
+        p_draft[c0:c0 + K] = res["p_x"]
+        q_draft[c0:c0 + K] = res["q_x"]
+        if keep_trace:
+            traces[b] = res
+    return tokens, accept_len, p_draft, q_draft, traces
+
+
+def spec_verify_greedy_ragged(target_rows, cu, draft_tokens, k_max=None, dtype="f32"):
+    """Greedy verification of a ragged batch (layout as above).
+
+    Returns (tokens [B, k_max + 1], accept_len [B], argmax [total_k + B]);
+    argmax rows of refused requests stay -1.
+    """
+    B = len(cu) - 1
+    total_k = len(draft_tokens)
+    if k_max is None:
+        k_max = max([0] + [int(cu[b + 1]) - int(cu[b]) for b in range(B)])
+    tokens = np.full((B, k_max + 1), -1, dtype=np.int32)
+    accept_len = np.zeros(B, dtype=np.int32)
+    g_all = np.full(total_k + B, -1, dtype=np.int32)
+    for b in range(B):
+        K = ragged_draft_count(cu, b, total_k, k_max)
+        if K is None:
+            continue
+        c0 = int(cu[b])
+        g = [argmax_lowest(logits_f64(target_rows[c0 + b + i], dtype)) for i in range(K + 1)]
+        g_all[c0 + b:c0 + b + K + 1] = g
+        a = 0
+        while a < K and int(draft_tokens[c0 + a]) == g[a]:
+            a += 1
+        tokens[b, :a] = draft_tokens[c0:c0 + a]
+        tokens[b, a] = g[a]
+        accept_len[b] = a + 1
+    return tokens, accept_len, g_all
 
 
 # ------------------------------------------------------- greedy and tree ---
