@@ -39,22 +39,27 @@ def source_digest() -> str:
 
 
 CHUNK_BYTES = 4096        # the draw re-reads one 4 KiB chunk of logits per request
+RAGGED_BASE = {"c3_ragged": "c3_onehot"}   # ragged workloads: base workload cut to K_b per request
 
 
 def algorithmic_bytes(wl, rejected=None) -> int:
     """Bytes one call must read: every logits row the rule consults once
-    (B*(K+1) target rows, plus B*K draft rows when q is explicit), plus the
-    draw's one chunk per request, plus (explicit drafts only) the stop rows
-    of target and draft again for each request that rejected (`rejected`
-    requests; all B when unknown). Greedy and tree draw nothing."""
+    (B*(K+1) target rows, plus B*K draft rows when q is explicit; a ragged
+    batch consults sum(K_b + 1) and sum(K_b)), plus the draw's one chunk per
+    request, plus (explicit drafts only) the stop rows of target and draft
+    again for each request that rejected (`rejected` requests; all B when
+    unknown). Greedy and tree draw nothing."""
     es = 2 if wl["dtype"] == "bf16" else 4
     B, V = wl["B"], wl["V"]
     if wl["mode"] == "tree":
         return B * len(wl["parents"]) * V * es
     K = wl["K"]
     explicit = wl.get("draft") is not None
-    rows = K + 1 + (K if explicit else 0)
-    total = B * rows * V * es
+    if wl.get("ragged") is not None:
+        nk = int(wl["ragged"]["ks"].sum())
+        total = (nk + B + (nk if explicit else 0)) * V * es
+    else:
+        total = B * (K + 1 + (K if explicit else 0)) * V * es
     if wl["mode"] == "sample":
         total += B * min(CHUNK_BYTES, V * es)
         if explicit:
@@ -76,18 +81,29 @@ def traffic_record(workload: str):
 
 
 def cpu_baseline(wl, seconds: float):
+    import numpy as np
     import oracle
     B = wl["B"]
+    rg = wl.get("ragged")
     t0 = time.perf_counter()
     n = 0
     while n < B and (time.perf_counter() - t0) < seconds:
-        oracle.spec_verify_sample(wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"],
-                                  wl["seeds"], wl["offset"], target_dtype=wl["dtype"], requests=[n])
+        if rg is None:
+            oracle.spec_verify_sample(wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"],
+                                      wl["seeds"], wl["offset"], target_dtype=wl["dtype"], requests=[n])
+        else:                                       # request n alone, as a one-request ragged batch
+            c0, c1 = int(rg["cu"][n]), int(rg["cu"][n + 1])
+            oracle.spec_verify_sample_ragged(
+                rg["target_rows"][c0 + n: c1 + n + 1], None,
+                np.array([0, c1 - c0], np.int32), rg["draft_tokens"][c0:c1],
+                wl["temperature"][n:n + 1], wl["seeds"][n:n + 1], wl["offset"], k_max=wl["K"],
+                target_dtype=wl["dtype"])
         n += 1
     dt = time.perf_counter() - t0
     sample_bytes = algorithmic_bytes(wl) * n / B
     return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} of {B} requests of {wl['name']} ({n * (wl['K'] + 1)} logits rows), "
+            "sample": f"{n} of {B} requests of {wl['name']} "
+                      f"({int(rg['ks'][:n].sum()) + n if rg is not None else n * (wl['K'] + 1)} logits rows), "
                       f"{dt:.1f} s, single thread",
             "us_per_step_equiv": round(dt / n * B * 1e6, 1)}
 
@@ -110,7 +126,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c3_onehot")
+    ap.add_argument("--workload", default="c3_onehot",
+                    help="c1_tiny, c2_stoch, c3_onehot, c4_greedy, c5_tree, or c3_ragged "
+                         "(C3 with per-request draft counts K_b ~ uniform{0..5})")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -132,21 +150,30 @@ def main():
     from workloads import make
 
     dev = torch.device("cuda:0")
-    wl = make(args.workload, data_seed=0)
+    ragged = args.workload in RAGGED_BASE
+    if ragged:
+        from workloads import make_ragged
+        wl = make_ragged(RAGGED_BASE[args.workload], data_seed=0)
+    else:
+        wl = make(args.workload, data_seed=0)
     lib = sv.load_library()
     B, K, V = wl["B"], wl["K"], wl["V"]
     mode = wl["mode"]
 
+    host_t = wl["ragged"]["target_rows"] if ragged else wl["target"]
     if wl["dtype"] == "bf16":
-        tgt0 = torch.from_numpy(wl["target"].view(np.int16)).to(dev).view(torch.bfloat16)
+        tgt0 = torch.from_numpy(host_t.view(np.int16)).to(dev).view(torch.bfloat16)
     else:
-        tgt0 = torch.from_numpy(wl["target"]).to(dev)
+        tgt0 = torch.from_numpy(host_t).to(dev)
     copies = [tgt0] + [tgt0.clone() for _ in range(max(args.copies, 1) - 1)]
     draft = None
     if wl.get("draft") is not None:
         d0 = torch.from_numpy(wl["draft"]).to(dev)
         draft = [d0] + [d0.clone() for _ in range(max(args.copies, 1) - 1)]
-    tokens = torch.from_numpy(wl["draft_tokens"]).to(dev)
+    tokens = torch.from_numpy(wl["ragged"]["draft_tokens"] if ragged else wl["draft_tokens"]).to(dev)
+    if ragged:
+        cu = torch.from_numpy(wl["ragged"]["cu"]).to(dev)
+        total_k = int(wl["ragged"]["ks"].sum())
     out_tok = torch.empty((B, tokens.shape[1] if mode == "tree" else K + 1), dtype=torch.int32, device=dev)
     out_len = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -154,8 +181,8 @@ def main():
     if mode == "sample":
         temp = torch.from_numpy(wl["temperature"]).to(dev)
         seeds = torch.from_numpy(wl["seeds"].view(np.int64)).to(dev)
-        out_p = torch.empty((B, K), dtype=torch.float32, device=dev)
-        out_q = torch.empty((B, K), dtype=torch.float32, device=dev)
+        out_p = torch.empty((total_k if ragged else B * K,), dtype=torch.float32, device=dev)
+        out_q = torch.empty((total_k if ragged else B * K,), dtype=torch.float32, device=dev)
         ws_bytes = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, B, K, V, draft is not None)
     elif mode == "greedy":
         out_g = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
@@ -168,12 +195,18 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     sv.spec_verify_workspace_init(ws)
 
-    descs = [sv._desc(t, "target") for t in copies]
+    descs = [sv._rows_desc(t, "target") if ragged else sv._desc(t, "target") for t in copies]
     ddescs = [sv._desc(t, "draft") for t in draft] if draft is not None else None
 
     def step(i):
         c = i % len(copies)
-        if mode == "sample":
+        if ragged:
+            rc = lib.spec_verify_sample_ragged(ctypes.byref(descs[c]), None, cu.data_ptr(), total_k,
+                                               tokens.data_ptr(), temp.data_ptr(), seeds.data_ptr(), i,
+                                               B, K, V, out_tok.data_ptr(), out_len.data_ptr(),
+                                               out_p.data_ptr(), out_q.data_ptr(), ws.data_ptr(),
+                                               ws_bytes, stream)
+        elif mode == "sample":
             rc = lib.spec_verify_sample(ctypes.byref(descs[c]),
                                         ctypes.byref(ddescs[c]) if ddescs else None,
                                         tokens.data_ptr(), temp.data_ptr(), seeds.data_ptr(), i, B, K, V,
@@ -248,7 +281,10 @@ def main():
                    "logits_dtype": wl["dtype"], "draft": "explicit" if draft is not None else
                    ("one-hot" if mode == "sample" else "tokens"),
                    "temperature": None if wl["temperature"] is None else float(wl["temperature"][0]),
-                   "algorithmic_bytes_per_step": nbytes, "input_copies": len(copies)},
+                   "algorithmic_bytes_per_step": nbytes, "input_copies": len(copies),
+                   **({"ragged": {"rows_consulted": int(wl["ragged"]["ks"].sum()) + B,
+                                  "k_mean": round(float(wl["ragged"]["ks"].mean()), 3),
+                                  "K_max": K}} if ragged else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_record(wl["name"]),

@@ -54,6 +54,11 @@ _SIGNATURES = {
                                           _vp, _c_size, _vp]),
     "spec_verify_tree": (ctypes.c_int, [_PSV, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
                                         _vp, _c_size, _vp]),
+    "spec_verify_sample_ragged": (ctypes.c_int, [_PSV, _PSV, _vp, _c_i32, _vp, _vp, _vp, _c_u64,
+                                                 _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp,
+                                                 _c_size, _vp]),
+    "spec_verify_greedy_ragged": (ctypes.c_int, [_PSV, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32,
+                                                 _vp, _vp, _vp, _vp, _c_size, _vp]),
     "spec_verify_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -137,6 +142,23 @@ def _desc(t: torch.Tensor, name: str) -> SVLogits:
     return SVLogits(t.data_ptr(), dt, 0, t.stride(0), t.stride(1))
 
 
+def _rows_desc(t: torch.Tensor, name: str) -> SVLogits:
+    """Descriptor of packed rows [rows, V] (ragged calls: rows stride(0) apart)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be [rows, V]")
+    if t.dtype == torch.float32:
+        dt = SV_DTYPE_F32
+    elif t.dtype == torch.bfloat16:
+        dt = SV_DTYPE_BF16
+    else:
+        raise ValueError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have a contiguous vocabulary dimension")
+    return SVLogits(t.data_ptr(), dt, 0, 0, t.stride(0))
+
+
 def _check(t: torch.Tensor, name: str, dtype, shape, device):
     if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
             or t.device != device:
@@ -208,6 +230,78 @@ def spec_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, want
                                 ws.data_ptr(), ws.numel(), _stream_ptr(dev))
     if rc:
         raise SpecVerifyError(rc, "spec_verify_greedy")
+    return tokens, alen, g
+
+
+def spec_verify_sample_ragged(target_rows: torch.Tensor, draft_rows: torch.Tensor | None,
+                              cu_draft: torch.Tensor, draft_tokens: torch.Tensor,
+                              temperature: torch.Tensor, seeds: torch.Tensor, offset: int = 0,
+                              *, k_max: int, want_probs: bool = True):
+    """Ragged batch: request b has K_b = cu_draft[b+1] - cu_draft[b] drafts.
+
+    target_rows [total_k + B, V] (request b's rows from cu_draft[b] + b),
+    draft_rows [total_k, V] or None, cu_draft int32 [B + 1], draft_tokens
+    int32 [total_k]. Returns (tokens [B, k_max+1], accept_len [B],
+    p_draft [total_k], q_draft [total_k]).
+    """
+    lib = load_library()
+    dev = target_rows.device
+    B = cu_draft.numel() - 1
+    total_k = draft_tokens.numel()
+    V = target_rows.shape[-1]
+    tdesc = _rows_desc(target_rows, "target_rows")
+    if target_rows.shape[0] != total_k + B:
+        raise ValueError("target_rows must hold total_k + B rows")
+    ddesc = None
+    if draft_rows is not None:
+        ddesc = _rows_desc(draft_rows, "draft_rows")
+        if draft_rows.shape != (total_k, V) or draft_rows.device != dev:
+            raise ValueError("draft_rows must be [total_k, V] on the target's device")
+    _check(cu_draft, "cu_draft", torch.int32, (B + 1,), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (total_k,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    seeds = _seeds_u64(seeds)
+    _check(seeds, "seeds", torch.int64, (B,), dev)
+    tokens = torch.empty((B, k_max + 1), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    p = torch.empty((total_k,), dtype=torch.float32, device=dev) if want_probs else None
+    q = torch.empty((total_k,), dtype=torch.float32, device=dev) if want_probs else None
+    ws = _workspace(dev, spec_verify_workspace_size(SV_OP_SAMPLE, B, k_max, V, draft_rows is not None))
+    rc = lib.spec_verify_sample_ragged(ctypes.byref(tdesc), ctypes.byref(ddesc) if ddesc else None,
+                                       cu_draft.data_ptr(), total_k,
+                                       draft_tokens.data_ptr() if total_k else None,
+                                       temperature.data_ptr(), seeds.data_ptr(),
+                                       int(offset) & (2**64 - 1), B, int(k_max), V,
+                                       tokens.data_ptr(), alen.data_ptr(), _ptr(p), _ptr(q),
+                                       ws.data_ptr(), ws.numel(), _stream_ptr(dev))
+    if rc:
+        raise SpecVerifyError(rc, "spec_verify_sample_ragged")
+    return tokens, alen, p, q
+
+
+def spec_verify_greedy_ragged(target_rows: torch.Tensor, cu_draft: torch.Tensor,
+                              draft_tokens: torch.Tensor, *, k_max: int, want_argmax: bool = True):
+    """Ragged greedy verification. Returns (tokens [B, k_max+1], accept_len [B], argmax [total_k + B])."""
+    lib = load_library()
+    dev = target_rows.device
+    B = cu_draft.numel() - 1
+    total_k = draft_tokens.numel()
+    V = target_rows.shape[-1]
+    tdesc = _rows_desc(target_rows, "target_rows")
+    if target_rows.shape[0] != total_k + B:
+        raise ValueError("target_rows must hold total_k + B rows")
+    _check(cu_draft, "cu_draft", torch.int32, (B + 1,), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (total_k,), dev)
+    tokens = torch.empty((B, k_max + 1), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    g = torch.full((total_k + B,), -1, dtype=torch.int32, device=dev) if want_argmax else None
+    ws = _workspace(dev, spec_verify_workspace_size(SV_OP_GREEDY, B, k_max, V))
+    rc = lib.spec_verify_greedy_ragged(ctypes.byref(tdesc), cu_draft.data_ptr(), total_k,
+                                       draft_tokens.data_ptr() if total_k else None, B,
+                                       int(k_max), V, tokens.data_ptr(), alen.data_ptr(), _ptr(g),
+                                       ws.data_ptr(), ws.numel(), _stream_ptr(dev))
+    if rc:
+        raise SpecVerifyError(rc, "spec_verify_greedy_ragged")
     return tokens, alen, g
 
 

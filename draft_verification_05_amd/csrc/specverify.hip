@@ -54,7 +54,9 @@ struct Record {
 struct Args {
   const char* tgt; int64_t t_sb, t_sk;     // byte strides
   const char* drf; int64_t d_sb, d_sk;
-  const int32_t* tokens;                   // [B, K] drafts or [B, N] node tokens
+  const int32_t* tokens;                   // [B, K] drafts or [B, N] node tokens; ragged: [total_k]
+  const int32_t* cu;                       // ragged: [B + 1] prefix sums of the draft counts; else null
+  int total_k;                             // ragged: number of packed drafts
   const float* temperature;                // [B]
   const uint64_t* seeds;                   // [B]
   uint64_t offset;
@@ -90,13 +92,52 @@ struct TailLds {
   int depth[SV_MAX_TREE_NODES];
 };
 
-// Row r of request b: target rows first, then draft rows. Written as
+// Where request b's rows, tokens and outputs are. Dense batches: K drafts
+// each, rows by the two strides, tokens and p/q outputs at b * K. Ragged
+// batches: K_b = cu[b + 1] - cu[b] drafts; target row i is packed row
+// cu[b] + b + i and draft row i is packed row cu[b] + i (rows by stride_k),
+// tokens and p/q outputs start at cu[b]. A ragged request whose offsets are
+// out of order or out of range is refused and nothing of it is read.
+struct Req {
+  int k;          // draft count
+  bool ok;
+  int64_t tb;     // byte offset of target row 0
+  int64_t db;     // byte offset of draft row 0
+  int64_t x0;     // first draft token / p, q output
+  int64_t g0;     // first argmax output (greedy)
+};
+
+__device__ inline Req request(const Args& A, int b) {
+  Req q;
+  if (!A.cu) {
+    q.k = A.K; q.ok = true;
+    q.tb = (int64_t)b * A.t_sb;
+    q.db = (int64_t)b * A.d_sb;
+    q.x0 = (int64_t)b * A.K;
+    q.g0 = (int64_t)b * (A.K + 1);
+    return q;
+  }
+  const int c0 = A.cu[b], c1 = A.cu[b + 1];
+  q.ok = 0 <= c0 && c0 <= c1 && c1 <= A.total_k && c1 - c0 <= A.K;
+  q.k = q.ok ? c1 - c0 : 0;
+  const int64_t c = q.ok ? c0 : 0;
+  q.tb = (c + b) * A.t_sk;
+  q.db = c * A.d_sk;
+  q.x0 = c;
+  q.g0 = c + b;
+  return q;
+}
+
+// Row r of a request: target rows first, then draft rows. Written as
 // selects so that both descriptors load in one batch of scalar loads.
-__device__ inline const char* row_ptr(const Args& A, int b, int r) {
+__device__ inline const char* row_ptr(const Args& A, const Req& q, int r) {
   const bool t = r < A.R;
-  const char* base = t ? A.tgt : A.drf;
-  const int64_t sb = t ? A.t_sb : A.d_sb, sk = t ? A.t_sk : A.d_sk;
-  return base + (int64_t)b * sb + (int64_t)(t ? r : r - A.R) * sk;
+  return t ? A.tgt + q.tb + (int64_t)r * A.t_sk : A.drf + q.db + (int64_t)(r - A.R) * A.d_sk;
+}
+
+// Whether row r of a request holds data: target rows 0..k, draft rows 0..k-1.
+__device__ inline bool row_live(const Args& A, const Req& q, int r) {
+  return q.ok && (r < A.R ? r <= q.k : r - A.R < q.k);
 }
 
 // ------------------------------------------------ in-launch hand-off ---
@@ -249,8 +290,8 @@ __device__ inline float2 partial(const Args& A, int b, int rr, int s, const Tail
 // `xe`) using that row's row-pass partials; used for the one-hot residual
 // and the bonus token. Returns -1 when the weights have no mass.
 template <int DT, bool kVec>
-__device__ int draw_softmax_row(const Args& A, int b, int r, float c, float M, int xe, float u,
-                                const TailLds& S, bool cached) {
+__device__ int draw_softmax_row(const Args& A, int b, const Req& rq, int r, float c, float M, int xe,
+                                float u, const TailLds& S, bool cached) {
   constexpr int E = Chunk<DT>::kElems / 64;
   auto W = [&](int s) {
     const float2 v = partial(A, b, r, s, S, cached);
@@ -262,7 +303,7 @@ __device__ int draw_softmax_row(const Args& A, int b, int r, float c, float M, i
   if (!(Z > 0.f) || found < 0) return -1;
   const int64_t c0 = (int64_t)found * Chunk<DT>::kElems;
   float x[E], w[E];
-  load_lane_run<DT, kVec, E>(row_ptr(A, b, r), c0, A.V, x);
+  load_lane_run<DT, kVec, E>(row_ptr(A, rq, r), c0, A.V, x);
   const int64_t e0 = c0 + (int64_t)(threadIdx.x & 63) * E;
 #pragma unroll
   for (int k = 0; k < E; ++k) {
@@ -407,13 +448,14 @@ __device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, 
 template <int DT, bool kVec, int MODE>
 __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63;
-  const int K = A.K, V = A.V, R = A.R;
+  const Req rq = request(A, b);
+  const int K = rq.k, V = A.V, R = A.R;
   const int64_t rowg0 = (int64_t)b * A.rows;
   // independent loads first: draft tokens, gathered logits, partials
   int x = -1;
   float lx = kNegInf, ld = kNegInf;
   if (lane < K) {
-    x = A.tokens[(int64_t)b * K + lane];
+    x = A.tokens[rq.x0 + lane];
     lx = A.gath[rowg0 + lane];
     if (MODE == kExplicit) ld = A.gath[rowg0 + R + lane];
   }
@@ -428,10 +470,11 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   merge_softmax_rows(A, b, S, ws);
   const bool cached = stage_commit(A, b, S, st);
   int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
-  if (!(T > 0.f && T < __builtin_inff())) {      // refused request
+  for (int j = K + 1 + lane; j < A.out_cols; j += 64) otok[j] = -1;   // columns past this request's drafts
+  if (!rq.ok || !(T > 0.f && T < __builtin_inff())) {      // refused request
     if (lane <= K) otok[lane] = -1;
-    if (lane < K && A.out_p) A.out_p[(int64_t)b * K + lane] = 0.f;
-    if (lane < K && A.out_q) A.out_q[(int64_t)b * K + lane] = 0.f;
+    if (lane < K && A.out_p) A.out_p[rq.x0 + lane] = 0.f;
+    if (lane < K && A.out_q) A.out_q[rq.x0 + lane] = 0.f;
     if (lane == 0) {
       A.out_len[b] = 0;
       if (MODE == kExplicit) A.rec[b].pending = 0;
@@ -463,8 +506,8 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
       lp = (valid && Sp > 0.f) ? dp - __log2f(Sp) : kNegInf;
       lq = (valid && Sq > 0.f) ? dq - __log2f(Sq) : kNegInf;
     }
-    if (A.out_p) A.out_p[(int64_t)b * K + lane] = p;
-    if (A.out_q) A.out_q[(int64_t)b * K + lane] = q;
+    if (A.out_p) A.out_p[rq.x0 + lane] = p;
+    if (A.out_q) A.out_q[rq.x0 + lane] = q;
   }
   // the first position whose draft is rejected (u q >= p), K if none; with
   // draft logits the test is log2 u + log2 q < log2 p (log2 0 = -inf)
@@ -490,23 +533,32 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   const bool resid = (MODE == kOneHot && a < K);
   const float M = resid ? lane_f(Mx, a) : S.rowM[a];
   const int xe = resid ? lane_i(x, a) : -1;
-  int y = draw_softmax_row<DT, kVec>(A, b, a, c, M, xe, ua, S, cached);
+  int y = draw_softmax_row<DT, kVec>(A, b, rq, a, c, M, xe, ua, S, cached);
   if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
   if (lane == 0) otok[a] = y;
 }
 
 __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
-  const int lane = threadIdx.x & 63, K = A.K;
-  const int x = lane < K ? A.tokens[(int64_t)b * K + lane] : -1;
+  const int lane = threadIdx.x & 63;
+  const Req rq = request(A, b);
+  const int K = rq.k;
+  const int x = lane < K ? A.tokens[rq.x0 + lane] : -1;
   WStaged ws;
   wstage_issue(A, b, A.rows, make_float2(kNegInf, __int_as_float(INT_MAX)), ws);
   merge_argmax_rows(A, b, A.rows, S, ws);
   const int g = lane <= K ? S.g[lane] : -1;
   const int mis = first_lane(lane < K && x != g);
   const int a = mis < 0 ? K : mis;
+  int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
+  for (int j = K + 1 + lane; j < A.out_cols; j += 64) otok[j] = -1;   // columns past this request's drafts
+  if (!rq.ok) {                                    // refused (ragged offsets)
+    if (lane <= K) otok[lane] = -1;
+    if (lane == 0) A.out_len[b] = 0;
+    return;
+  }
   if (lane <= K) {
-    A.out_tokens[(int64_t)b * A.out_cols + lane] = lane < a ? x : (lane == a ? g : -1);
-    if (A.out_aux) A.out_aux[(int64_t)b * (K + 1) + lane] = g;
+    otok[lane] = lane < a ? x : (lane == a ? g : -1);
+    if (A.out_aux) A.out_aux[rq.g0 + lane] = g;
   }
   if (lane == 0) A.out_len[b] = a + 1;
 }
@@ -717,7 +769,9 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   const int wi = (int)(blockIdx.x % (unsigned)A.wpr);
   const int rowg = (int)(blockIdx.x / (unsigned)A.wpr);
   const int b = rowg / A.rows, r = rowg % A.rows;
-  const char* row = row_ptr(A, b, r);
+  const Req rq = request(A, b);
+  if (A.cu && !row_live(A, rq, r)) return;        // a ragged request's padding rows: no work
+  const char* row = row_ptr(A, rq, r);
   const int c_lo = wi * A.cpw;
   const int c_hi = min(c_lo + A.cpw, A.n_chunk);
   // Partials collect in LDS and leave in one store at the end: no global
@@ -740,7 +794,7 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   float c = 0.f;
   if (MODE == kOneHot || MODE == kExplicit) {
     const int i = r < A.R ? r : r - A.R;
-    if (i < A.K) xe = A.tokens[(int64_t)b * A.K + i];
+    if (i < rq.k) xe = A.tokens[rq.x0 + i];
     c = kLog2e / A.temperature[b];
     // The two uniforms of every position i <= K of request b, one lane per
     // position: drawn by one wave of the last (shortest) workgroup of the
@@ -844,8 +898,9 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   const int a = rc.a;
   const float c = rc.c;
   const float ip = 1.f / rc.Sp, iq = 1.f / rc.Sq;
-  const char* rowp = row_ptr(A, b, a);
-  const char* rowq = row_ptr(A, b, A.R + a);
+  const Req rq = request(A, b);
+  const char* rowp = row_ptr(A, rq, a);
+  const char* rowq = row_ptr(A, rq, A.R + a);
   const int c_lo = wi * A.cpw;
   const int c_hi = min(c_lo + A.cpw, A.n_chunk);
 
@@ -892,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   }
   if (y < 0) {
     // p_a and q_a agree everywhere: draw from p_a with the row pass's partials
-    y = draw_softmax_row<DT, kVec>(A, b, a, c, rc.Mp, -1, rc.u, S, false);
+    y = draw_softmax_row<DT, kVec>(A, b, rq, a, c, rc.Mp, -1, rc.u, S, false);
     if (y < 0) y = 0;
   }
   if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + a] = y;
@@ -980,6 +1035,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.t_sb = t->stride_b * es;
   A.t_sk = t->stride_k * es;
   A.drf = nullptr; A.d_sb = 0; A.d_sk = 0;
+  A.cu = nullptr; A.total_k = 0;
   A.B = B; A.K = K; A.V = V; A.R = R; A.rows = rows;
   const int ce = t->dtype == SV_DTYPE_BF16 ? Chunk<kBF16>::kElems : Chunk<kF32>::kElems;
   A.n_chunk = (V + ce - 1) / ce;
@@ -1045,6 +1101,96 @@ int check_grid(int64_t wgs) {
 
 int hip_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
+// Sampling, dense (cu null: [B, K + 1] rows by the two strides) or ragged
+// (cu [B + 1] device prefix sums, packed rows by stride_k, stride_b unused).
+int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* cu, int32_t total_k,
+                const int32_t* draft_tokens, const float* temperature,
+                const uint64_t* seeds, uint64_t offset,
+                int32_t B, int32_t K, int32_t V,
+                int32_t* out_tokens, int32_t* out_accept_len,
+                float* out_p_draft, float* out_q_draft,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(target);
+  if (st) return st;
+  if (draft && (st = check_desc(draft))) return st;
+  if (!temperature || !seeds || !out_tokens || !out_accept_len) return SV_ERR_NULL;
+  if (B < 1 || B > SV_MAX_BATCH || K < 0 || K > SV_MAX_DRAFT || V < 1 || V > SV_MAX_VOCAB)
+    return SV_ERR_SHAPE;
+  if ((cu ? total_k > 0 : K > 0) && !draft_tokens) return SV_ERR_NULL;
+  if (draft && draft->dtype != target->dtype) return SV_ERR_DTYPE;
+  if (!workspace) return SV_ERR_WORKSPACE;
+  const bool explicit_q = draft != nullptr && K > 0;
+  const int R = K + 1;
+  const int rows = R + (explicit_q ? K : 0);
+  if (workspace_bytes < layout(B, rows, V).total) return SV_ERR_WORKSPACE;
+
+  Args A;
+  fill_common(A, target, B, K, V, R, rows, workspace);
+  if (explicit_q) {
+    const int64_t es = elem_bytes(draft->dtype);
+    A.drf = static_cast<const char*>(draft->data);
+    A.d_sb = draft->stride_b * es;
+    A.d_sk = draft->stride_k * es;
+  }
+  A.tokens = draft_tokens;
+  A.cu = cu;
+  A.total_k = total_k;
+  A.temperature = temperature;
+  A.seeds = seeds;
+  A.offset = offset;
+  A.out_cols = K + 1;
+  A.out_tokens = out_tokens;
+  A.out_len = out_accept_len;
+  A.out_p = out_p_draft;
+  A.out_q = out_q_draft;
+  const int64_t wgs = (int64_t)B * rows * A.wpr;
+  if ((st = check_grid(wgs))) return st;
+  const bool vec = aligned16(target) && (!explicit_q || aligned16(draft));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (explicit_q) {
+    launch_rows<kExplicit>(A, target->dtype, vec, (unsigned)wgs, s);
+    if ((st = hip_status())) return st;
+    // the residual pass streams one stop row pair per request
+    Args A2 = A;
+    A2.cpw = chunks_per_wg(B, A.n_chunk);
+    A2.wpr = (A.n_chunk + A2.cpw - 1) / A2.cpw;
+    launch_residual(A2, target->dtype, vec, (unsigned)((int64_t)B * A2.wpr), s);
+  } else {
+    launch_rows<kOneHot>(A, target->dtype, vec, (unsigned)wgs, s);
+  }
+  return hip_status();
+}
+
+// Greedy, dense or ragged (as sample_impl).
+int greedy_impl(const sv_logits* target, const int32_t* cu, int32_t total_k,
+                const int32_t* draft_tokens, int32_t B, int32_t K, int32_t V,
+                int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(target);
+  if (st) return st;
+  if (!out_tokens || !out_accept_len) return SV_ERR_NULL;
+  if (B < 1 || B > SV_MAX_BATCH || K < 0 || K > SV_MAX_DRAFT || V < 1 || V > SV_MAX_VOCAB)
+    return SV_ERR_SHAPE;
+  if ((cu ? total_k > 0 : K > 0) && !draft_tokens) return SV_ERR_NULL;
+  if (!workspace) return SV_ERR_WORKSPACE;
+  const int R = K + 1;
+  if (workspace_bytes < layout(B, R, V).total) return SV_ERR_WORKSPACE;
+  Args A;
+  fill_common(A, target, B, K, V, R, R, workspace);
+  A.tokens = draft_tokens;
+  A.cu = cu;
+  A.total_k = total_k;
+  A.out_cols = K + 1;
+  A.out_tokens = out_tokens;
+  A.out_len = out_accept_len;
+  A.out_aux = out_argmax;
+  const int64_t wgs = (int64_t)B * R * A.wpr;
+  if ((st = check_grid(wgs))) return st;
+  launch_rows<kGreedy>(A, target->dtype, aligned16(target), (unsigned)wgs,
+                       static_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -1087,80 +1233,47 @@ int spec_verify_sample(const sv_logits* target, const sv_logits* draft,
                        int32_t* out_tokens, int32_t* out_accept_len,
                        float* out_p_draft, float* out_q_draft,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_desc(target);
-  if (st) return st;
-  if (draft && (st = check_desc(draft))) return st;
-  if (!temperature || !seeds || !out_tokens || !out_accept_len) return SV_ERR_NULL;
-  if (B < 1 || B > SV_MAX_BATCH || K < 0 || K > SV_MAX_DRAFT || V < 1 || V > SV_MAX_VOCAB)
-    return SV_ERR_SHAPE;
-  if (K > 0 && !draft_tokens) return SV_ERR_NULL;
-  if (draft && draft->dtype != target->dtype) return SV_ERR_DTYPE;
-  if (!workspace) return SV_ERR_WORKSPACE;
-  const bool explicit_q = draft != nullptr && K > 0;
-  const int R = K + 1;
-  const int rows = R + (explicit_q ? K : 0);
-  if (workspace_bytes < layout(B, rows, V).total) return SV_ERR_WORKSPACE;
+  return sample_impl(target, draft, nullptr, 0, draft_tokens, temperature, seeds, offset, B, K, V,
+                     out_tokens, out_accept_len, out_p_draft, out_q_draft, workspace,
+                     workspace_bytes, stream);
+}
 
-  Args A;
-  fill_common(A, target, B, K, V, R, rows, workspace);
-  if (explicit_q) {
-    const int64_t es = elem_bytes(draft->dtype);
-    A.drf = static_cast<const char*>(draft->data);
-    A.d_sb = draft->stride_b * es;
-    A.d_sk = draft->stride_k * es;
-  }
-  A.tokens = draft_tokens;
-  A.temperature = temperature;
-  A.seeds = seeds;
-  A.offset = offset;
-  A.out_cols = K + 1;
-  A.out_tokens = out_tokens;
-  A.out_len = out_accept_len;
-  A.out_p = out_p_draft;
-  A.out_q = out_q_draft;
-  const int64_t wgs = (int64_t)B * rows * A.wpr;
-  if ((st = check_grid(wgs))) return st;
-  const bool vec = aligned16(target) && (!explicit_q || aligned16(draft));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (explicit_q) {
-    launch_rows<kExplicit>(A, target->dtype, vec, (unsigned)wgs, s);
-    if ((st = hip_status())) return st;
-    // the residual pass streams one stop row pair per request
-    Args A2 = A;
-    A2.cpw = chunks_per_wg(B, A.n_chunk);
-    A2.wpr = (A.n_chunk + A2.cpw - 1) / A2.cpw;
-    launch_residual(A2, target->dtype, vec, (unsigned)((int64_t)B * A2.wpr), s);
-  } else {
-    launch_rows<kOneHot>(A, target->dtype, vec, (unsigned)wgs, s);
-  }
-  return hip_status();
+int spec_verify_sample_ragged(const sv_logits* target, const sv_logits* draft,
+                              const int32_t* cu_draft, int32_t total_k,
+                              const int32_t* draft_tokens, const float* temperature,
+                              const uint64_t* seeds, uint64_t offset,
+                              int32_t B, int32_t K_max, int32_t V,
+                              int32_t* out_tokens, int32_t* out_accept_len,
+                              float* out_p_draft, float* out_q_draft,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_draft || !target) return SV_ERR_NULL;
+  if (total_k < 0) return SV_ERR_SHAPE;
+  sv_logits t = *target, d = draft ? *draft : sv_logits{};
+  t.stride_b = 0;                                   // packed rows: stride_k only
+  d.stride_b = 0;
+  return sample_impl(&t, draft ? &d : nullptr, cu_draft, total_k, draft_tokens, temperature,
+                     seeds, offset, B, K_max, V, out_tokens, out_accept_len, out_p_draft,
+                     out_q_draft, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
                        int32_t B, int32_t K, int32_t V,
                        int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_desc(target);
-  if (st) return st;
-  if (!out_tokens || !out_accept_len) return SV_ERR_NULL;
-  if (B < 1 || B > SV_MAX_BATCH || K < 0 || K > SV_MAX_DRAFT || V < 1 || V > SV_MAX_VOCAB)
-    return SV_ERR_SHAPE;
-  if (K > 0 && !draft_tokens) return SV_ERR_NULL;
-  if (!workspace) return SV_ERR_WORKSPACE;
-  const int R = K + 1;
-  if (workspace_bytes < layout(B, R, V).total) return SV_ERR_WORKSPACE;
-  Args A;
-  fill_common(A, target, B, K, V, R, R, workspace);
-  A.tokens = draft_tokens;
-  A.out_cols = K + 1;
-  A.out_tokens = out_tokens;
-  A.out_len = out_accept_len;
-  A.out_aux = out_argmax;
-  const int64_t wgs = (int64_t)B * R * A.wpr;
-  if ((st = check_grid(wgs))) return st;
-  launch_rows<kGreedy>(A, target->dtype, aligned16(target), (unsigned)wgs,
-                       static_cast<hipStream_t>(stream));
-  return hip_status();
+  return greedy_impl(target, nullptr, 0, draft_tokens, B, K, V, out_tokens, out_accept_len,
+                     out_argmax, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_greedy_ragged(const sv_logits* target, const int32_t* cu_draft, int32_t total_k,
+                              const int32_t* draft_tokens, int32_t B, int32_t K_max, int32_t V,
+                              int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_draft || !target) return SV_ERR_NULL;
+  if (total_k < 0) return SV_ERR_SHAPE;
+  sv_logits t = *target;
+  t.stride_b = 0;
+  return greedy_impl(&t, cu_draft, total_k, draft_tokens, B, K_max, V, out_tokens,
+                     out_accept_len, out_argmax, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,

@@ -99,7 +99,10 @@ int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* st
  *   i.e. with probability min(1, p_i(x_i) / q_i(x_i)); the scan stops at
  *   the first rejection a, where one token is drawn from the normalised
  *   residual max(0, p_a - q_a) (p_a if that has no mass); if all K are
- *   accepted the token is drawn from p_K. Draws are inverse-CDF: the
+ *   accepted the token is drawn from p_K. With draft logits the test is
+ *   evaluated as log2 u + log2 q_i(x_i) < log2 p_i(x_i) (the same event;
+ *   it stays exact where both probabilities underflow fp32). Draws are
+ *   inverse-CDF: the
  *   smallest token whose running sum exceeds u times the total.
  *   The two uniforms of (b, i) are the top 24 bits of words 0 and 1 of
  *   Philox4x64-10 (Salmon et al., SC'11) with counter (i, b, offset, 0) and
@@ -147,6 +150,49 @@ int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
                        int32_t B, int32_t K, int32_t V,
                        int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Ragged batches: every request has its own draft count K_b (a verifier
+ * takes variable-length queries from one forward and maps each output row
+ * back to its request: FastDeploy "投机解码", framework design, virtual
+ * padding; adaptive per-request draft counts: vLLM-Ascend "Speculative
+ * Decoding Guide", suffix decoding; "推测解码与 MTP" §10.2).
+ *
+ * Rows are packed. With cu = cu_draft (device, [B + 1] int32 prefix sums,
+ * K_b = cu[b + 1] - cu[b]):
+ *   target rows of request b: packed rows cu[b] + b ... cu[b] + b + K_b of
+ *     `target` ([total_k + B, V]; rows stride_k apart, stride_b unused);
+ *   draft rows (explicit q): packed rows cu[b] ... cu[b] + K_b - 1 of
+ *     `draft` ([total_k, V]), or NULL for one-hot q;
+ *   draft tokens: draft_tokens[cu[b] ... cu[b] + K_b - 1] ([total_k]);
+ *   out_p_draft / out_q_draft: [total_k] at the same positions;
+ *   out_tokens: [B, K_max + 1], columns past K_b are -1;
+ *   out_argmax (greedy): [total_k + B] at the target rows' positions.
+ * The rule per request is the dense one with K = K_b, with the uniforms of
+ * (seeds[b], b, position): a ragged call equals the dense call on each
+ * request's own rows. total_k [host] is the number of packed drafts and
+ * K_max [host] (0..SV_MAX_DRAFT) bounds every K_b; the workspace is sized
+ * as for the dense call with K = K_max.
+ * Device-side checks: a request with cu[b] < 0, cu[b + 1] < cu[b],
+ * cu[b + 1] > total_k or K_b > K_max is refused (accept_len 0, tokens -1)
+ * and none of its rows is read; every row read lies in the ranges above.
+ * Other device values behave as in the dense calls. Host errors: as the
+ * dense calls, plus SV_ERR_NULL for a NULL cu_draft (or NULL draft_tokens
+ * with total_k > 0) and SV_ERR_SHAPE for total_k < 0.
+ */
+int spec_verify_sample_ragged(const sv_logits* target, const sv_logits* draft,
+                              const int32_t* cu_draft, int32_t total_k,
+                              const int32_t* draft_tokens, const float* temperature,
+                              const uint64_t* seeds, uint64_t offset,
+                              int32_t B, int32_t K_max, int32_t V,
+                              int32_t* out_tokens, int32_t* out_accept_len,
+                              float* out_p_draft, float* out_q_draft,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+int spec_verify_greedy_ragged(const sv_logits* target, const int32_t* cu_draft, int32_t total_k,
+                              const int32_t* draft_tokens, int32_t B, int32_t K_max, int32_t V,
+                              int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Greedy verification of a static draft tree (Medusa, "推测解码与 MTP"

@@ -135,3 +135,27 @@ def test_workspace_init_null(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         sv.load_library(str(tmp_path / "nope.so"))
+
+
+def test_ragged_argument_errors(lib):
+    s = lib.spec_verify_sample_ragged
+    t = desc()
+
+    def call(cu=FAKE, total_k=3, tokens=FAKE, B=2, K=2, wsb=BIG_WS, ws=FAKE, d=None):
+        return s(ctypes.byref(t), ctypes.byref(d) if d is not None else None, cu, total_k, tokens,
+                 FAKE, FAKE, 0, B, K, 5, FAKE, FAKE, None, None, ws, wsb, None)
+
+    assert call(cu=None) == sv.SV_ERR_NULL
+    assert call(total_k=-1) == sv.SV_ERR_SHAPE
+    assert call(tokens=None) == sv.SV_ERR_NULL            # drafts exist but no tokens
+    assert call(K=33) == sv.SV_ERR_SHAPE
+    assert call(B=0) == sv.SV_ERR_SHAPE
+    assert call(ws=None) == sv.SV_ERR_WORKSPACE
+    need = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, 2, 2, 5)
+    assert call(wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    assert call(d=desc(dtype=1)) == sv.SV_ERR_DTYPE
+    g = lib.spec_verify_greedy_ragged
+    assert g(ctypes.byref(t), None, 3, FAKE, 2, 2, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert g(ctypes.byref(t), FAKE, -2, FAKE, 2, 2, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+    assert g(ctypes.byref(t), FAKE, 3, None, 2, 2, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert g(None, FAKE, 3, FAKE, 2, 2, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL

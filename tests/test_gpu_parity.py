@@ -13,6 +13,7 @@ import oracle
 from chisq import chisq_pvalue
 from parity import assert_report, classify_sample, new_report, to_device
 from workloads import f32_to_bf16_bits, make, medusa_tree_parents
+from workloads import pack_ragged as workloads_pack_ragged
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -362,3 +363,94 @@ def test_tree_deep_chain():
             tok[b, cut] = (g[b, cut - 1] + 1) % V
     wl = dict(target=tgt, draft_tokens=tok, B=B, V=V, dtype="f32", seeds=np.zeros(B, np.uint64))
     check_tree(wl, parents, "tree chain N=64")
+
+
+# ---------------------------------------------------------------- ragged ---
+def pack_ragged(wl, ks):
+    r = workloads_pack_ragged(wl, ks)
+    return r["target_rows"], r["draft_rows"], r["cu"], r["draft_tokens"]
+
+
+def run_ragged(wl, ks, K, cu=None):
+    t_rows, d_rows, cu0, toks = pack_ragged(wl, ks)
+    cu = cu0 if cu is None else cu
+    bf16 = wl["dtype"] == "bf16"
+    tt = torch.from_numpy(t_rows.view(np.int16) if bf16 else t_rows).to(DEV)
+    tt = tt.view(torch.bfloat16) if bf16 else tt
+    dd = None if d_rows is None else torch.from_numpy(np.ascontiguousarray(d_rows)).to(DEV)
+    out = sv.spec_verify_sample_ragged(
+        tt, dd, torch.from_numpy(cu).to(DEV), torch.from_numpy(toks).to(DEV),
+        torch.from_numpy(wl["temperature"]).to(DEV),
+        torch.from_numpy(wl["seeds"].view(np.int64)).to(DEV), wl["offset"], k_max=K)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in out], cu0
+
+
+@pytest.mark.parametrize("cfg,K,V", [("c3_onehot", 5, 2 * 8192 + 1232), ("c2_stoch", 3, 20001),
+                                     ("c2_stoch", 4, 8192)])
+def test_ragged_sample(cfg, K, V):
+    B = 24
+    wl = make(cfg, data_seed=60, B=B, K=K, V=V, offset=2)
+    ks = np.random.default_rng(61).integers(0, K + 1, B)
+    ks[:3] = [0, K, 0]
+    (g_tok, g_len, g_p, g_q), cu = run_ragged(wl, ks, K)
+    print(f"[case] ragged {cfg} B={B} K_max={K} V={V} ks={ks.tolist()}", flush=True)
+    for b in range(B):
+        assert np.all(g_tok[b, ks[b] + 1:] == -1)
+    rep = new_report()
+    for k in np.unique(ks):
+        reqs = [int(b) for b in np.nonzero(ks == k)[0]]
+        wl_k = dict(wl, K=int(k), target=wl["target"][:, : k + 1],
+                    draft=None if wl["draft"] is None else wl["draft"][:, :k],
+                    draft_tokens=np.ascontiguousarray(wl["draft_tokens"][:, :k]))
+        tok_k = np.full((B, k + 1), -1, np.int32)
+        p_k = np.zeros((B, k), np.float32)
+        q_k = np.zeros((B, k), np.float32)
+        for b in reqs:
+            tok_k[b] = g_tok[b, : k + 1]
+            p_k[b] = g_p[cu[b]:cu[b + 1]]
+            q_k[b] = g_q[cu[b]:cu[b + 1]]
+        classify_sample(wl_k, tok_k, g_len, p_k, q_k, requests=reqs, report=rep)
+    assert_report(rep, f"ragged {cfg} V={V}")
+
+
+def test_ragged_full_counts_equal_dense_bitwise():
+    wl = make("c3_onehot", data_seed=62, B=16, K=5, V=9000)
+    (r_tok, r_len, r_p, r_q), _ = run_ragged(wl, np.full(16, 5), 5)
+    d_tok, d_len, d_p, d_q = run_sample(wl)
+    np.testing.assert_array_equal(r_tok, d_tok)
+    np.testing.assert_array_equal(r_len, d_len)
+    np.testing.assert_array_equal(r_p, d_p.reshape(-1))
+    np.testing.assert_array_equal(r_q, d_q.reshape(-1))
+
+
+def test_ragged_bad_offsets_refuse_only_their_request():
+    K = 3
+    wl = make("c2_stoch", data_seed=63, B=6, K=K, V=5000)
+    ks = np.array([2, 3, 1, 0, 2, 3])
+    (good_tok, good_len, _, _), cu = run_ragged(wl, ks, K)
+    bad = cu.copy()
+    bad[2] = bad[3] + 1                            # request 1: K_b > K_max; request 2: out of order
+    bad[5] = 10**6                                 # requests 4 and 5: beyond total_k
+    (tok, alen, _, _), _ = run_ragged(wl, ks, K, cu=bad)
+    for b in (1, 2, 4, 5):
+        assert alen[b] == 0 and np.all(tok[b] == -1), b
+    for b in (0, 3):
+        assert alen[b] == good_len[b]
+        np.testing.assert_array_equal(tok[b], good_tok[b])
+
+
+def test_ragged_greedy():
+    K = 5
+    wl = make("c4_greedy", data_seed=64, B=20, K=K, V=3 * 8192 + 5)
+    ks = np.random.default_rng(65).integers(0, K + 1, 20)
+    t_rows, _, cu, toks = pack_ragged(wl, ks)
+    tok, alen, g = sv.spec_verify_greedy_ragged(torch.from_numpy(t_rows).to(DEV),
+                                                torch.from_numpy(cu).to(DEV),
+                                                torch.from_numpy(toks).to(DEV), k_max=K)
+    torch.cuda.synchronize()
+    o_tok, o_len, o_g = oracle.spec_verify_greedy_ragged(t_rows, cu, toks, k_max=K)
+    np.testing.assert_array_equal(g.cpu().numpy(), o_g)
+    np.testing.assert_array_equal(alen.cpu().numpy(), o_len)
+    np.testing.assert_array_equal(tok.cpu().numpy(), o_tok)
+    print(f"[parity] ragged greedy: exact, ks={ks.tolist()}", flush=True)

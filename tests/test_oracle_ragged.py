@@ -8,21 +8,12 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make
+from workloads import make, pack_ragged
 
 
 def pack(wl, ks):
-    """Packed rows, prefix sums and tokens of a dense workload cut to per-request counts."""
-    B = wl["B"]
-    cu = np.zeros(B + 1, np.int32)
-    cu[1:] = np.cumsum(ks)
-    t_rows = np.concatenate([wl["target"][b, : ks[b] + 1] for b in range(B)])
-    d_rows = None
-    if wl["draft"] is not None:
-        d_rows = np.concatenate([wl["draft"][b, : ks[b]] for b in range(B)] +
-                                [np.zeros((0, wl["V"]), wl["draft"].dtype)])
-    toks = np.concatenate([wl["draft_tokens"][b, : ks[b]] for b in range(B)] + [np.zeros(0, np.int32)])
-    return t_rows, d_rows, cu, toks.astype(np.int32)
+    r = pack_ragged(wl, ks)
+    return r["target_rows"], r["draft_rows"], r["cu"], r["draft_tokens"]
 
 
 @pytest.mark.parametrize("cfg", ["c2_stoch", "c3_onehot"])

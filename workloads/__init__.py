@@ -44,6 +44,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "CONFIGS", "make", "medusa_tree_parents", "f32_to_bf16_bits",
+    "pack_ragged", "make_ragged",
     "bf16_bits_to_f32",
 ]
 
@@ -211,3 +212,35 @@ def make(name: str, data_seed: int = 0, *, B: int | None = None, K: int | None =
     out.update(target=tgt_store, draft=draft, draft_tokens=np.ascontiguousarray(tokens),
                temperature=temp, seeds=seeds)
     return out
+
+
+def pack_ragged(wl: dict, ks) -> dict:
+    """Cut a dense workload to per-request draft counts ks[b] <= K and pack it.
+
+    Returns dict(ks, cu [B + 1] int32 prefix sums, target_rows [sum ks + B, V]
+    (request b's K_b + 1 rows from cu[b] + b), draft_rows [sum ks, V] or
+    None, draft_tokens [sum ks] int32). Layout only: nothing is computed.
+    """
+    B = wl["B"]
+    ks = np.asarray(ks, dtype=np.int64)
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(ks)
+    rows = np.concatenate([wl["target"][b, : ks[b] + 1] for b in range(B)])
+    drows = None
+    if wl.get("draft") is not None:
+        drows = np.concatenate([wl["draft"][b, : ks[b]] for b in range(B)] +
+                               [np.zeros((0, wl["V"]), wl["draft"].dtype)])
+    toks = np.concatenate([wl["draft_tokens"][b, : ks[b]] for b in range(B)] +
+                          [np.zeros(0, np.int32)]).astype(np.int32)
+    return dict(ks=ks, cu=cu, target_rows=np.ascontiguousarray(rows),
+                draft_rows=None if drows is None else np.ascontiguousarray(drows),
+                draft_tokens=toks)
+
+
+def make_ragged(name: str, data_seed: int = 0, **kw) -> dict:
+    """A named workload with per-request draft counts K_b ~ uniform{0..K}
+    (seeded by data_seed), packed. The dense arrays stay in the dict."""
+    wl = make(name, data_seed, **kw)
+    ks = np.random.default_rng([data_seed, 7]).integers(0, wl["K"] + 1, wl["B"])
+    wl = dict(wl, name=name.split("_")[0] + "_ragged", ragged=pack_ragged(wl, ks))
+    return wl
