@@ -17,6 +17,9 @@ Parity pins (each checked by ``tests/test_oracle_*.py`` without a GPU):
   * ragged batches: every request equals the dense rule on its own rows with
     the same uniforms, whatever the mix of draft counts; bad offsets refuse
     only their own request.
+  * grammar bitmasks: the bit layout against numpy's own bit unpacking; an
+    all-ones mask changes nothing; emitted tokens are always allowed and
+    disallowed drafts are always rejected.
 Parity unpinned: individual draws whose uniform lies within 1e-5 of an
 acceptance threshold or CDF boundary (the GPU works in fp32); they are
 counted by the parity tests, not matched.

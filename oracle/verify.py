@@ -64,6 +64,7 @@ __all__ = [
     "inverse_cdf", "verify_request", "spec_verify_sample", "argmax_lowest",
     "spec_verify_greedy", "tree_depths", "spec_verify_tree",
     "ragged_draft_count", "spec_verify_sample_ragged", "spec_verify_greedy_ragged",
+    "apply_bitmask",
 ]
 
 
@@ -78,6 +79,19 @@ def logits_f64(row, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return a.astype(np.float32).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def apply_bitmask(logits: np.ndarray, mask_row) -> np.ndarray:
+    """Logits of one position with the tokens a grammar bitmask disallows set to
+    -inf (LMDeploy "Speculative Decoding", structured output: the grammar
+    mask is applied to the target's logits at every verified position).
+    Token v is allowed when bit v % 32 of word v // 32 of ``mask_row`` is 1."""
+    V = len(logits)
+    out = np.array(logits, dtype=np.float64)
+    for v in range(V):
+        if not (int(mask_row[v // 32]) >> (v % 32)) & 1:
+            out[v] = -math.inf
+    return out
 
 
 def softmax_t(logits: np.ndarray, T: float) -> np.ndarray:
@@ -152,7 +166,7 @@ def verify_request(p_rows, q_rows, x, u_acc, u_smp) -> dict:
 
 def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0,
                        target_dtype="f32", draft_dtype="f32", requests=None,
-                       keep_trace=False):
+                       keep_trace=False, bitmask=None):
     """Batched stochastic verification.
 
     target [B, K+1, V] (fp32 values or bf16 bit patterns), draft [B, >=K, V]
@@ -164,7 +178,8 @@ def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0
     float64, q_draft [B, K] float64, traces) where traces[b] is the
     per-request record from ``verify_request`` when keep_trace is set.
     A request whose temperature is not a finite positive number is refused:
-    accept_len 0, tokens -1, probabilities 0.
+    accept_len 0, tokens -1, probabilities 0. ``bitmask`` [B, K+1, ceil(V/32)]
+    (optional) masks target row i and, with draft logits, draft row i.
     """
     B, R, V = target.shape
     K = R - 1
@@ -177,11 +192,13 @@ def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0
         T = float(temperature[b])
         if not (math.isfinite(T) and T > 0):
             continue
-        p_rows = [softmax_t(logits_f64(target[b, i], target_dtype), T).tolist()
+        def masked(l, i):
+            return l if bitmask is None else apply_bitmask(l, bitmask[b, i])
+        p_rows = [softmax_t(masked(logits_f64(target[b, i], target_dtype), i), T).tolist()
                   for i in range(K + 1)]
         x = [int(v) for v in draft_tokens[b, :K]]
         if draft is not None:
-            q_rows = [softmax_t(logits_f64(draft[b, i], draft_dtype), T).tolist()
+            q_rows = [softmax_t(masked(logits_f64(draft[b, i], draft_dtype), i), T).tolist()
                       for i in range(K)]
         else:
             q_rows = [onehot(V, x[i]) for i in range(K)]
@@ -296,10 +313,11 @@ def argmax_lowest(row) -> int:
     return int(np.argmax(np.asarray(row, dtype=np.float64)))
 
 
-def spec_verify_greedy(target, draft_tokens, dtype="f32"):
+def spec_verify_greedy(target, draft_tokens, dtype="f32", bitmask=None):
     """Greedy (argmax-match) verification.
 
     Returns (tokens [B, K+1] -1 padded, accept_len [B], argmax [B, K+1]).
+    ``bitmask`` (optional) as in spec_verify_sample: argmax over allowed tokens.
     """
     B, R, V = target.shape
     K = R - 1
@@ -308,7 +326,8 @@ def spec_verify_greedy(target, draft_tokens, dtype="f32"):
     g = np.zeros((B, K + 1), dtype=np.int32)
     for b in range(B):
         for i in range(K + 1):
-            g[b, i] = argmax_lowest(logits_f64(target[b, i], dtype))
+            l = logits_f64(target[b, i], dtype)
+            g[b, i] = argmax_lowest(l if bitmask is None else apply_bitmask(l, bitmask[b, i]))
         a = 0
         while a < K and int(draft_tokens[b, a]) == g[b, a]:
             a += 1
