@@ -40,6 +40,7 @@ def source_digest() -> str:
 
 CHUNK_BYTES = 4096        # the draw re-reads one 4 KiB chunk of logits per request
 RAGGED_BASE = {"c3_ragged": "c3_onehot"}   # ragged workloads: base workload cut to K_b per request
+MASKED_BASE = {"c3_masked": "c3_onehot"}   # grammar-masked workloads: base workload + a bitmask
 
 
 def algorithmic_bytes(wl, rejected=None) -> int:
@@ -60,6 +61,8 @@ def algorithmic_bytes(wl, rejected=None) -> int:
         total = (nk + B + (nk if explicit else 0)) * V * es
     else:
         total = B * (K + 1 + (K if explicit else 0)) * V * es
+    if wl.get("bitmask") is not None:               # one mask row per consulted row
+        total += wl["bitmask"].nbytes // (K + 1) * (K + 1 + (K if explicit else 0))
     if wl["mode"] == "sample":
         total += B * min(CHUNK_BYTES, V * es)
         if explicit:
@@ -90,7 +93,8 @@ def cpu_baseline(wl, seconds: float):
     while n < B and (time.perf_counter() - t0) < seconds:
         if rg is None:
             oracle.spec_verify_sample(wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"],
-                                      wl["seeds"], wl["offset"], target_dtype=wl["dtype"], requests=[n])
+                                      wl["seeds"], wl["offset"], target_dtype=wl["dtype"], requests=[n],
+                                      bitmask=wl.get("bitmask"))
         else:                                       # request n alone, as a one-request ragged batch
             c0, c1 = int(rg["cu"][n]), int(rg["cu"][n + 1])
             oracle.spec_verify_sample_ragged(
@@ -127,8 +131,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3_onehot",
-                    help="c1_tiny, c2_stoch, c3_onehot, c4_greedy, c5_tree, or c3_ragged "
-                         "(C3 with per-request draft counts K_b ~ uniform{0..5})")
+                    help="c1_tiny, c2_stoch, c3_onehot, c4_greedy, c5_tree, c3_ragged "
+                         "(C3 with per-request draft counts K_b ~ uniform{0..5}) or c3_masked "
+                         "(C3 with a grammar bitmask allowing each token w.p. 1/2)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -151,9 +156,13 @@ def main():
 
     dev = torch.device("cuda:0")
     ragged = args.workload in RAGGED_BASE
+    masked = args.workload in MASKED_BASE
     if ragged:
         from workloads import make_ragged
         wl = make_ragged(RAGGED_BASE[args.workload], data_seed=0)
+    elif masked:
+        from workloads import make_masked
+        wl = make_masked(MASKED_BASE[args.workload], data_seed=0)
     else:
         wl = make(args.workload, data_seed=0)
     lib = sv.load_library()
@@ -174,6 +183,8 @@ def main():
     if ragged:
         cu = torch.from_numpy(wl["ragged"]["cu"]).to(dev)
         total_k = int(wl["ragged"]["ks"].sum())
+    if masked:
+        bitmask = torch.from_numpy(wl["bitmask"].view(np.int32)).to(dev)
     out_tok = torch.empty((B, tokens.shape[1] if mode == "tree" else K + 1), dtype=torch.int32, device=dev)
     out_len = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -206,6 +217,13 @@ def main():
                                                B, K, V, out_tok.data_ptr(), out_len.data_ptr(),
                                                out_p.data_ptr(), out_q.data_ptr(), ws.data_ptr(),
                                                ws_bytes, stream)
+        elif masked:
+            rc = lib.spec_verify_sample_masked(ctypes.byref(descs[c]),
+                                               ctypes.byref(ddescs[c]) if ddescs else None,
+                                               tokens.data_ptr(), bitmask.data_ptr(), temp.data_ptr(),
+                                               seeds.data_ptr(), i, B, K, V, out_tok.data_ptr(),
+                                               out_len.data_ptr(), out_p.data_ptr(), out_q.data_ptr(),
+                                               ws.data_ptr(), ws_bytes, stream)
         elif mode == "sample":
             rc = lib.spec_verify_sample(ctypes.byref(descs[c]),
                                         ctypes.byref(ddescs[c]) if ddescs else None,
@@ -284,7 +302,9 @@ def main():
                    "algorithmic_bytes_per_step": nbytes, "input_copies": len(copies),
                    **({"ragged": {"rows_consulted": int(wl["ragged"]["ks"].sum()) + B,
                                   "k_mean": round(float(wl["ragged"]["ks"].mean()), 3),
-                                  "K_max": K}} if ragged else {})},
+                                  "K_max": K}} if ragged else {}),
+                   **({"bitmask": {"allowed_fraction": round(float(wl["mask_allowed"]), 4),
+                                   "bytes": int(wl["bitmask"].nbytes)}} if masked else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_record(wl["name"]),

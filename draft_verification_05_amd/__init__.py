@@ -59,6 +59,11 @@ _SIGNATURES = {
                                                  _c_size, _vp]),
     "spec_verify_greedy_ragged": (ctypes.c_int, [_PSV, _vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32,
                                                  _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "spec_verify_sample_masked": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _vp, _c_u64, _c_i32,
+                                                 _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp, _c_size,
+                                                 _vp]),
+    "spec_verify_greedy_masked": (ctypes.c_int, [_PSV, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp,
+                                                 _vp, _vp, _c_size, _vp]),
     "spec_verify_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -302,6 +307,72 @@ def spec_verify_greedy_ragged(target_rows: torch.Tensor, cu_draft: torch.Tensor,
                                        ws.data_ptr(), ws.numel(), _stream_ptr(dev))
     if rc:
         raise SpecVerifyError(rc, "spec_verify_greedy_ragged")
+    return tokens, alen, g
+
+
+def _bitmask(bitmask: torch.Tensor, B: int, R: int, V: int, dev) -> torch.Tensor:
+    if bitmask.dtype == torch.uint32:
+        bitmask = bitmask.view(torch.int32)
+    _check(bitmask, "bitmask", torch.int32, (B, R, (V + 31) // 32), dev)
+    return bitmask
+
+
+def spec_verify_sample_masked(target: torch.Tensor, draft: torch.Tensor | None,
+                              draft_tokens: torch.Tensor, bitmask: torch.Tensor,
+                              temperature: torch.Tensor, seeds: torch.Tensor, offset: int = 0,
+                              *, want_probs: bool = True):
+    """Grammar-masked stochastic verification; bitmask [B, K+1, ceil(V/32)] int32/uint32
+    (bit v % 32 of word v // 32 set = token v allowed). Returns as spec_verify_sample."""
+    lib = load_library()
+    B, R, V = target.shape
+    K = R - 1
+    dev = target.device
+    tdesc = _desc(target, "target")
+    ddesc = None
+    if draft is not None:
+        ddesc = _desc(draft, "draft")
+        if draft.shape[0] != B or draft.shape[1] < K or draft.shape[2] != V or draft.device != dev:
+            raise ValueError("draft must be [B, >=K, V] on the target's device")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    bitmask = _bitmask(bitmask, B, R, V, dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    seeds = _seeds_u64(seeds)
+    _check(seeds, "seeds", torch.int64, (B,), dev)
+    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    p = torch.empty((B, K), dtype=torch.float32, device=dev) if want_probs else None
+    q = torch.empty((B, K), dtype=torch.float32, device=dev) if want_probs else None
+    ws = _workspace(dev, spec_verify_workspace_size(SV_OP_SAMPLE, B, K, V, draft is not None))
+    rc = lib.spec_verify_sample_masked(ctypes.byref(tdesc), ctypes.byref(ddesc) if ddesc else None,
+                                       draft_tokens.data_ptr() if K else None, bitmask.data_ptr(),
+                                       temperature.data_ptr(), seeds.data_ptr(),
+                                       int(offset) & (2**64 - 1), B, K, V, tokens.data_ptr(),
+                                       alen.data_ptr(), _ptr(p), _ptr(q), ws.data_ptr(), ws.numel(),
+                                       _stream_ptr(dev))
+    if rc:
+        raise SpecVerifyError(rc, "spec_verify_sample_masked")
+    return tokens, alen, p, q
+
+
+def spec_verify_greedy_masked(target: torch.Tensor, draft_tokens: torch.Tensor, bitmask: torch.Tensor,
+                              *, want_argmax: bool = True):
+    """Grammar-masked greedy verification. Returns as spec_verify_greedy."""
+    lib = load_library()
+    B, R, V = target.shape
+    K = R - 1
+    dev = target.device
+    tdesc = _desc(target, "target")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    bitmask = _bitmask(bitmask, B, R, V, dev)
+    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    g = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if want_argmax else None
+    ws = _workspace(dev, spec_verify_workspace_size(SV_OP_GREEDY, B, K, V))
+    rc = lib.spec_verify_greedy_masked(ctypes.byref(tdesc), draft_tokens.data_ptr() if K else None,
+                                       bitmask.data_ptr(), B, K, V, tokens.data_ptr(), alen.data_ptr(),
+                                       _ptr(g), ws.data_ptr(), ws.numel(), _stream_ptr(dev))
+    if rc:
+        raise SpecVerifyError(rc, "spec_verify_greedy_masked")
     return tokens, alen, g
 
 

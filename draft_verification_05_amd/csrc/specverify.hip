@@ -57,6 +57,8 @@ struct Args {
   const int32_t* tokens;                   // [B, K] drafts or [B, N] node tokens; ragged: [total_k]
   const int32_t* cu;                       // ragged: [B + 1] prefix sums of the draft counts; else null
   int total_k;                             // ragged: number of packed drafts
+  const uint32_t* mask;                    // grammar bitmask [B, K+1, mask_words] or null
+  int mask_words;                          // ceil(V / 32)
   const float* temperature;                // [B]
   const uint64_t* seeds;                   // [B]
   uint64_t offset;
@@ -133,6 +135,11 @@ __device__ inline Req request(const Args& A, int b) {
 __device__ inline const char* row_ptr(const Args& A, const Req& q, int r) {
   const bool t = r < A.R;
   return t ? A.tgt + q.tb + (int64_t)r * A.t_sk : A.drf + q.db + (int64_t)(r - A.R) * A.d_sk;
+}
+
+// Bitmask words of position i of request b (target row i and draft row i).
+__device__ inline const uint32_t* mask_row(const Args& A, int b, int i) {
+  return A.mask + ((int64_t)b * A.R + i) * A.mask_words;
 }
 
 // Whether row r of a request holds data: target rows 0..k, draft rows 0..k-1.
@@ -286,10 +293,19 @@ __device__ inline float2 partial(const Args& A, int b, int rr, int s, const Tail
                 : A.part[((int64_t)b * A.rows + rr) * A.n_chunk + s];
 }
 
+// Bitmask bits of lane l's E consecutive logits c0 + l * E ... (E = 32 or
+// 16, so they sit in one word): bit k allows logit c0 + l * E + k.
+template <int E>
+__device__ __forceinline__ uint32_t lane_mask_bits(const uint32_t* mrow, int64_t c0, int n_words) {
+  const int64_t e0 = c0 + (int64_t)(threadIdx.x & 63) * E;
+  const int64_t wi = e0 >> 5;
+  return mrow[wi < n_words ? wi : n_words - 1] >> (e0 & 31);
+}
+
 // Draw from one row's softmax weights 2^(y - M) (optionally without token
 // `xe`) using that row's row-pass partials; used for the one-hot residual
 // and the bonus token. Returns -1 when the weights have no mass.
-template <int DT, bool kVec>
+template <int DT, bool kVec, bool kMask>
 __device__ int draw_softmax_row(const Args& A, int b, const Req& rq, int r, float c, float M, int xe,
                                 float u, const TailLds& S, bool cached) {
   constexpr int E = Chunk<DT>::kElems / 64;
@@ -304,11 +320,12 @@ __device__ int draw_softmax_row(const Args& A, int b, const Req& rq, int r, floa
   const int64_t c0 = (int64_t)found * Chunk<DT>::kElems;
   float x[E], w[E];
   load_lane_run<DT, kVec, E>(row_ptr(A, rq, r), c0, A.V, x);
+  const uint32_t allow = kMask ? lane_mask_bits<E>(mask_row(A, b, r), c0, A.mask_words) : ~0u;
   const int64_t e0 = c0 + (int64_t)(threadIdx.x & 63) * E;
 #pragma unroll
   for (int k = 0; k < E; ++k) {
     const float v = fast_exp2(fmaf(x[k], c, -M));
-    w[k] = (e0 + k == xe) ? 0.f : v;
+    w[k] = (e0 + k == xe || !((allow >> k) & 1u)) ? 0.f : v;
   }
   return wave_pick<E>(w, c0, t_in);
 }
@@ -445,7 +462,7 @@ __device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, 
 
 // ---------------------------------------------------------- row tails ---
 // One wave per request.
-template <int DT, bool kVec, int MODE>
+template <int DT, bool kVec, int MODE, bool kMask>
 __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   const int lane = threadIdx.x & 63;
   const Req rq = request(A, b);
@@ -533,7 +550,7 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   const bool resid = (MODE == kOneHot && a < K);
   const float M = resid ? lane_f(Mx, a) : S.rowM[a];
   const int xe = resid ? lane_i(x, a) : -1;
-  int y = draw_softmax_row<DT, kVec>(A, b, rq, a, c, M, xe, ua, S, cached);
+  int y = draw_softmax_row<DT, kVec, kMask>(A, b, rq, a, c, M, xe, ua, S, cached);
   if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
   if (lane == 0) otok[a] = y;
 }
@@ -648,17 +665,19 @@ struct RefState {
   bool first = true;     // wave-uniform: no chunk seen yet
 };
 
-// One chunk's partial from one wave: (M, sum 2^(y - M)) for sampling, where
+// One chunk's partial from one wave (after the grammar bitmask, if any, has
+// turned disallowed logits into -inf): (M, sum 2^(y - M)) for sampling, where
 // M is a reference no larger than the row's maximum scaled logit (and, for
 // a chunk with finite logits, no smaller than any of them minus 64);
 // (max logit, lowest index of it) for greedy/tree. With a draft token xe in
 // this chunk, its logit goes to `gath` and, for one-hot drafts, it is left
 // out of the sums. `r` holds the lane's four 16-byte vectors.
-template <int MODE, int DT>
-__device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, int c0, int xe, float c, float* gath,
-                                                RefState& st) {
+template <int MODE, int DT, bool kMask>
+__device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, const MaskRaw& mk, int c0, int xe, float c,
+                                                float* gath, RefState& st) {
   constexpr int kPer = Elem<DT>::kPerVec;
   const int lane0 = (threadIdx.x & 63) * kPer;   // first logit of the lane's vector 0
+  if constexpr (kMask) apply_mask<DT>(r, mk);     // disallowed logits read as -inf from here on
   if constexpr (MODE == kOneHot || MODE == kExplicit) {
     const int dx = xe - c0;                       // the draft token's offset in this chunk
     if (xe >= 0 && (unsigned)dx < (unsigned)Chunk<DT>::kElems) {
@@ -761,7 +780,7 @@ __device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, int c0, int xe, flo
 // streams chunks c_lo + v, c_lo + v + 4, ... Full chunks go through a
 // two-deep pipeline of raw 16-byte loads; a row's last, partial chunk and
 // rows that are not 16-byte aligned take the checked element path.
-template <int MODE, int DT, bool kVec>
+template <int MODE, int DT, bool kVec, bool kMask>
 __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   constexpr int kCE = Chunk<DT>::kElems;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -772,6 +791,7 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   const Req rq = request(A, b);
   if (A.cu && !row_live(A, rq, r)) return;        // a ragged request's padding rows: no work
   const char* row = row_ptr(A, rq, r);
+  const uint32_t* mrow = kMask ? mask_row(A, b, r < A.R ? r : r - A.R) : nullptr;
   const int c_lo = wi * A.cpw;
   const int c_hi = min(c_lo + A.cpw, A.n_chunk);
   // Partials collect in LDS and leave in one store at the end: no global
@@ -785,7 +805,11 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   RefState rs;
   const bool piped = ch < ch_end;
   ChunkRaw ra, rb;
-  if (piped) issue_chunk<DT>(row, (int64_t)ch * kCE, ra);   // first loads before anything else
+  MaskRaw ma, mb;
+  if (piped) {                                     // first loads before anything else
+    issue_chunk<DT>(row, (int64_t)ch * kCE, ra);
+    if (kMask) issue_mask<DT>(mrow, (int64_t)ch * kCE, A.mask_words, ma);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // The draft token of this row (if any): its logit is kept for the tail,
@@ -814,9 +838,10 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
       int nx = ch + kWaves;
       bool more = nx < ch_end;
       issue_chunk<DT>(row, (int64_t)(more ? nx : ch) * kCE, rb);
+      if (kMask) issue_mask<DT>(mrow, (int64_t)(more ? nx : ch) * kCE, A.mask_words, mb);
       __builtin_amdgcn_sched_barrier(0);           // keep the prefetch ahead of the math
       {
-        const float2 res = chunk_partial<MODE, DT>(ra, ch * kCE, xe, c, gath, rs);
+        const float2 res = chunk_partial<MODE, DT, kMask>(ra, ma, ch * kCE, xe, c, gath, rs);
         if (lane == 0) s_part[ch - c_lo] = res;
       }
       ch = nx;
@@ -824,9 +849,10 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
       nx = ch + kWaves;
       more = nx < ch_end;
       issue_chunk<DT>(row, (int64_t)(more ? nx : ch) * kCE, ra);
+      if (kMask) issue_mask<DT>(mrow, (int64_t)(more ? nx : ch) * kCE, A.mask_words, ma);
       __builtin_amdgcn_sched_barrier(0);
       {
-        const float2 res = chunk_partial<MODE, DT>(rb, ch * kCE, xe, c, gath, rs);
+        const float2 res = chunk_partial<MODE, DT, kMask>(rb, mb, ch * kCE, xe, c, gath, rs);
         if (lane == 0) s_part[ch - c_lo] = res;
       }
       ch = nx;
@@ -835,8 +861,10 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   }
   for (; ch < c_hi; ch += kWaves) {               // checked path
     ChunkRaw rr;
+    MaskRaw mr;
     load_chunk_checked<DT, kVec>(row, (int64_t)ch * kCE, A.V, rr);
-    const float2 res = chunk_partial<MODE, DT>(rr, ch * kCE, xe, c, gath, rs);
+    if (kMask) issue_mask<DT>(mrow, (int64_t)ch * kCE, A.mask_words, mr);
+    const float2 res = chunk_partial<MODE, DT, kMask>(rr, mr, ch * kCE, xe, c, gath, rs);
     if (lane == 0) s_part[ch - c_lo] = res;
   }
   __syncthreads();
@@ -868,12 +896,12 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
 
 // One wave per request: the rule on the merged partials. The launch
 // boundary after the row pass is the only synchronisation the tail needs.
-template <int MODE, int DT, bool kVec>
+template <int MODE, int DT, bool kVec, bool kMask>
 __global__ __launch_bounds__(64) void sv_tail_kernel(Args A) {
   __shared__ TailLds S;
   const int b = blockIdx.x;
   if constexpr (MODE == kOneHot || MODE == kExplicit) {
-    sample_tail<DT, kVec, MODE>(A, b, S);
+    sample_tail<DT, kVec, MODE, kMask>(A, b, S);
   } else if constexpr (MODE == kGreedy) {
     greedy_tail(A, b, S);
   } else {
@@ -884,7 +912,7 @@ __global__ __launch_bounds__(64) void sv_tail_kernel(Args A) {
 // ------------------------------------------------------ residual pass ---
 // Explicit draft logits: for requests that stopped at a < K, chunk sums of
 // max(0, p_a - q_a); the last workgroup of the request draws the token.
-template <int DT, bool kVec>
+template <int DT, bool kVec, bool kMask>
 __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   constexpr int kCE = Chunk<DT>::kElems;
   __shared__ TailLds S;
@@ -898,9 +926,10 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   const int a = rc.a;
   const float c = rc.c;
   const float ip = 1.f / rc.Sp, iq = 1.f / rc.Sq;
-  const Req rq = request(A, b);
-  const char* rowp = row_ptr(A, rq, a);
-  const char* rowq = row_ptr(A, rq, A.R + a);
+  const Req req = request(A, b);
+  const char* rowp = row_ptr(A, req, a);
+  const char* rowq = row_ptr(A, req, A.R + a);
+  const uint32_t* mrow = kMask ? mask_row(A, b, a) : nullptr;
   const int c_lo = wi * A.cpw;
   const int c_hi = min(c_lo + A.cpw, A.n_chunk);
 
@@ -914,6 +943,12 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
     } else {
       load_chunk_checked<DT, kVec>(rowp, c0, A.V, rp);
       load_chunk_checked<DT, kVec>(rowq, c0, A.V, rq);
+    }
+    if constexpr (kMask) {                         // disallowed: p = q = 0, no residual
+      MaskRaw mr;
+      issue_mask<DT>(mrow, c0, A.mask_words, mr);
+      apply_mask<DT>(rp, mr);
+      apply_mask<DT>(rq, mr);
     }
     float s = 0.f;
 #pragma unroll
@@ -940,14 +975,17 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
     float xp[E], xq[E], w[E];
     load_lane_run<DT, kVec, E>(rowp, c0, A.V, xp);
     load_lane_run<DT, kVec, E>(rowq, c0, A.V, xq);
+    const uint32_t allow = kMask ? lane_mask_bits<E>(mrow, c0, A.mask_words) : ~0u;
 #pragma unroll
     for (int k = 0; k < E; ++k)
-      w[k] = fmaxf(fast_exp2(fmaf(xp[k], c, -rc.Mp)) * ip - fast_exp2(fmaf(xq[k], c, -rc.Mq)) * iq, 0.f);
+      w[k] = ((allow >> k) & 1u)
+                 ? fmaxf(fast_exp2(fmaf(xp[k], c, -rc.Mp)) * ip - fast_exp2(fmaf(xq[k], c, -rc.Mq)) * iq, 0.f)
+                 : 0.f;
     y = wave_pick<E>(w, c0, t_in);
   }
   if (y < 0) {
     // p_a and q_a agree everywhere: draw from p_a with the row pass's partials
-    y = draw_softmax_row<DT, kVec>(A, b, rq, a, c, rc.Mp, -1, rc.u, S, false);
+    y = draw_softmax_row<DT, kVec, kMask>(A, b, req, a, c, rc.Mp, -1, rc.u, S, false);
     if (y < 0) y = 0;
   }
   if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + a] = y;
@@ -1036,6 +1074,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.t_sk = t->stride_k * es;
   A.drf = nullptr; A.d_sb = 0; A.d_sk = 0;
   A.cu = nullptr; A.total_k = 0;
+  A.mask = nullptr; A.mask_words = (V + 31) / 32;
   A.B = B; A.K = K; A.V = V; A.R = R; A.rows = rows;
   const int ce = t->dtype == SV_DTYPE_BF16 ? Chunk<kBF16>::kElems : Chunk<kF32>::kElems;
   A.n_chunk = (V + ce - 1) / ce;
@@ -1062,36 +1101,50 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
 
 // Row pass over every (request, row, chunk run), then one tail wave per
 // request, back to back on the caller's stream.
-template <int MODE>
-void launch_rows(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
-  const dim3 tails((unsigned)A.B), wave(64);
-  if (dtype == SV_DTYPE_BF16) {
-    if (vec) {
-      SV_LAUNCH((sv_rows_kernel<MODE, kBF16, true>), grid, st, A);
-      hipLaunchKernelGGL((sv_tail_kernel<MODE, kBF16, true>), tails, wave, 0, st, A);
-    } else {
-      SV_LAUNCH((sv_rows_kernel<MODE, kBF16, false>), grid, st, A);
-      hipLaunchKernelGGL((sv_tail_kernel<MODE, kBF16, false>), tails, wave, 0, st, A);
-    }
+template <int MODE, int DT, bool kVec, bool kMask>
+void launch_pair(const Args& A, unsigned grid, hipStream_t st) {
+  SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask>), grid, st, A);
+  hipLaunchKernelGGL((sv_tail_kernel<MODE, DT, kVec, kMask>), dim3((unsigned)A.B), dim3(64), 0, st, A);
+}
+
+template <int MODE, int DT>
+void launch_rows_dt(const Args& A, bool vec, bool mask, unsigned grid, hipStream_t st) {
+  if constexpr (MODE == kTree) {                   // trees take no bitmask
+    if (vec) launch_pair<MODE, DT, true, false>(A, grid, st);
+    else     launch_pair<MODE, DT, false, false>(A, grid, st);
   } else {
     if (vec) {
-      SV_LAUNCH((sv_rows_kernel<MODE, kF32, true>), grid, st, A);
-      hipLaunchKernelGGL((sv_tail_kernel<MODE, kF32, true>), tails, wave, 0, st, A);
+      if (mask) launch_pair<MODE, DT, true, true>(A, grid, st);
+      else      launch_pair<MODE, DT, true, false>(A, grid, st);
     } else {
-      SV_LAUNCH((sv_rows_kernel<MODE, kF32, false>), grid, st, A);
-      hipLaunchKernelGGL((sv_tail_kernel<MODE, kF32, false>), tails, wave, 0, st, A);
+      if (mask) launch_pair<MODE, DT, false, true>(A, grid, st);
+      else      launch_pair<MODE, DT, false, false>(A, grid, st);
     }
   }
 }
 
-void launch_residual(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
-  if (dtype == SV_DTYPE_BF16) {
-    if (vec) SV_LAUNCH((sv_residual_kernel<kBF16, true>), grid, st, A);
-    else     SV_LAUNCH((sv_residual_kernel<kBF16, false>), grid, st, A);
+template <int MODE>
+void launch_rows(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
+  const bool mask = A.mask != nullptr;
+  if (dtype == SV_DTYPE_BF16) launch_rows_dt<MODE, kBF16>(A, vec, mask, grid, st);
+  else                        launch_rows_dt<MODE, kF32>(A, vec, mask, grid, st);
+}
+
+template <int DT>
+void launch_residual_dt(const Args& A, bool vec, unsigned grid, hipStream_t st) {
+  const bool mask = A.mask != nullptr;
+  if (vec) {
+    if (mask) SV_LAUNCH((sv_residual_kernel<DT, true, true>), grid, st, A);
+    else      SV_LAUNCH((sv_residual_kernel<DT, true, false>), grid, st, A);
   } else {
-    if (vec) SV_LAUNCH((sv_residual_kernel<kF32, true>), grid, st, A);
-    else     SV_LAUNCH((sv_residual_kernel<kF32, false>), grid, st, A);
+    if (mask) SV_LAUNCH((sv_residual_kernel<DT, false, true>), grid, st, A);
+    else      SV_LAUNCH((sv_residual_kernel<DT, false, false>), grid, st, A);
   }
+}
+
+void launch_residual(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
+  if (dtype == SV_DTYPE_BF16) launch_residual_dt<kBF16>(A, vec, grid, st);
+  else                        launch_residual_dt<kF32>(A, vec, grid, st);
 }
 
 // A dispatch counts work-items in 32 bits per dimension.
@@ -1104,7 +1157,7 @@ int hip_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; 
 // Sampling, dense (cu null: [B, K + 1] rows by the two strides) or ragged
 // (cu [B + 1] device prefix sums, packed rows by stride_k, stride_b unused).
 int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* cu, int32_t total_k,
-                const int32_t* draft_tokens, const float* temperature,
+                const uint32_t* mask, const int32_t* draft_tokens, const float* temperature,
                 const uint64_t* seeds, uint64_t offset,
                 int32_t B, int32_t K, int32_t V,
                 int32_t* out_tokens, int32_t* out_accept_len,
@@ -1135,6 +1188,7 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
   A.tokens = draft_tokens;
   A.cu = cu;
   A.total_k = total_k;
+  A.mask = mask;
   A.temperature = temperature;
   A.seeds = seeds;
   A.offset = offset;
@@ -1162,7 +1216,7 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
 }
 
 // Greedy, dense or ragged (as sample_impl).
-int greedy_impl(const sv_logits* target, const int32_t* cu, int32_t total_k,
+int greedy_impl(const sv_logits* target, const int32_t* cu, int32_t total_k, const uint32_t* mask,
                 const int32_t* draft_tokens, int32_t B, int32_t K, int32_t V,
                 int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
                 void* workspace, size_t workspace_bytes, void* stream) {
@@ -1180,6 +1234,7 @@ int greedy_impl(const sv_logits* target, const int32_t* cu, int32_t total_k,
   A.tokens = draft_tokens;
   A.cu = cu;
   A.total_k = total_k;
+  A.mask = mask;
   A.out_cols = K + 1;
   A.out_tokens = out_tokens;
   A.out_len = out_accept_len;
@@ -1233,8 +1288,21 @@ int spec_verify_sample(const sv_logits* target, const sv_logits* draft,
                        int32_t* out_tokens, int32_t* out_accept_len,
                        float* out_p_draft, float* out_q_draft,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return sample_impl(target, draft, nullptr, 0, draft_tokens, temperature, seeds, offset, B, K, V,
-                     out_tokens, out_accept_len, out_p_draft, out_q_draft, workspace,
+  return sample_impl(target, draft, nullptr, 0, nullptr, draft_tokens, temperature, seeds, offset, B,
+                     K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft, workspace,
+                     workspace_bytes, stream);
+}
+
+int spec_verify_sample_masked(const sv_logits* target, const sv_logits* draft,
+                              const int32_t* draft_tokens, const uint32_t* bitmask,
+                              const float* temperature, const uint64_t* seeds, uint64_t offset,
+                              int32_t B, int32_t K, int32_t V,
+                              int32_t* out_tokens, int32_t* out_accept_len,
+                              float* out_p_draft, float* out_q_draft,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!bitmask) return SV_ERR_NULL;
+  return sample_impl(target, draft, nullptr, 0, bitmask, draft_tokens, temperature, seeds, offset, B,
+                     K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft, workspace,
                      workspace_bytes, stream);
 }
 
@@ -1251,7 +1319,7 @@ int spec_verify_sample_ragged(const sv_logits* target, const sv_logits* draft,
   sv_logits t = *target, d = draft ? *draft : sv_logits{};
   t.stride_b = 0;                                   // packed rows: stride_k only
   d.stride_b = 0;
-  return sample_impl(&t, draft ? &d : nullptr, cu_draft, total_k, draft_tokens, temperature,
+  return sample_impl(&t, draft ? &d : nullptr, cu_draft, total_k, nullptr, draft_tokens, temperature,
                      seeds, offset, B, K_max, V, out_tokens, out_accept_len, out_p_draft,
                      out_q_draft, workspace, workspace_bytes, stream);
 }
@@ -1260,7 +1328,16 @@ int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
                        int32_t B, int32_t K, int32_t V,
                        int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return greedy_impl(target, nullptr, 0, draft_tokens, B, K, V, out_tokens, out_accept_len,
+  return greedy_impl(target, nullptr, 0, nullptr, draft_tokens, B, K, V, out_tokens, out_accept_len,
+                     out_argmax, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_greedy_masked(const sv_logits* target, const int32_t* draft_tokens,
+                              const uint32_t* bitmask, int32_t B, int32_t K, int32_t V,
+                              int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!bitmask) return SV_ERR_NULL;
+  return greedy_impl(target, nullptr, 0, bitmask, draft_tokens, B, K, V, out_tokens, out_accept_len,
                      out_argmax, workspace, workspace_bytes, stream);
 }
 
@@ -1272,7 +1349,7 @@ int spec_verify_greedy_ragged(const sv_logits* target, const int32_t* cu_draft, 
   if (total_k < 0) return SV_ERR_SHAPE;
   sv_logits t = *target;
   t.stride_b = 0;
-  return greedy_impl(&t, cu_draft, total_k, draft_tokens, B, K_max, V, out_tokens,
+  return greedy_impl(&t, cu_draft, total_k, nullptr, draft_tokens, B, K_max, V, out_tokens,
                      out_accept_len, out_argmax, workspace, workspace_bytes, stream);
 }
 

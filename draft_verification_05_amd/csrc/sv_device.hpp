@@ -101,6 +101,51 @@ __device__ __forceinline__ void issue_chunk(const char* row, int64_t c0, ChunkRa
     r.v[j] = *reinterpret_cast<const uint4*>(p + j * 64 * 16);
 }
 
+// Grammar bitmask words of one chunk: vector j of the lane (logits
+// c0 + (j * 64 + lane) * kPer ...) has its kPer bits in word
+// (c0 + (j * 64 + lane) * kPer) / 32 (a chunk starts on a word, a vector
+// never straddles one). Word indices past the row's last word are clamped
+// (those logits read as -inf anyway).
+struct MaskRaw { uint32_t w[kLoadsPerLane]; };
+
+template <int DT>
+__device__ __forceinline__ void issue_mask(const uint32_t* mrow, int64_t c0, int n_words, MaskRaw& m) {
+  constexpr int kPer = Elem<DT>::kPerVec;
+#pragma unroll
+  for (int j = 0; j < kLoadsPerLane; ++j) {
+    const int64_t wi = (c0 + (int64_t)(j * 64 + (threadIdx.x & 63)) * kPer) >> 5;
+    m.w[j] = mrow[wi < n_words ? wi : n_words - 1];
+  }
+}
+
+// Disallowed logits of a chunk become -inf in the packed words: bit k of
+// the lane's vector j (after the shift below) allows logit k of it. Per
+// 32-bit word one bitfield insert against the -inf pattern.
+template <int DT>
+__device__ __forceinline__ void apply_mask(ChunkRaw& r, const MaskRaw& m) {
+  constexpr int kPer = Elem<DT>::kPerVec;
+  const uint32_t shift = ((threadIdx.x & 63) * kPer) & 31;
+#pragma unroll
+  for (int j = 0; j < kLoadsPerLane; ++j) {
+    const uint32_t bits = m.w[j] >> shift;
+    auto blend = [bits](uint32_t& w, int q) {
+      uint32_t keep;
+      if constexpr (DT == kF32) {
+        keep = 0u - ((bits >> q) & 1u);                               // 0 or all ones
+      } else {
+        keep = ((0u - ((bits >> (2 * q)) & 1u)) & 0x0000FFFFu) |
+               ((0u - ((bits >> (2 * q + 1)) & 1u)) & 0xFFFF0000u);
+      }
+      const uint32_t inf = DT == kF32 ? 0xFF800000u : 0xFF80FF80u;
+      w = (w & keep) | (inf & ~keep);
+    };
+    blend(r.v[j].x, 0);
+    blend(r.v[j].y, 1);
+    blend(r.v[j].z, 2);
+    blend(r.v[j].w, 3);
+  }
+}
+
 // Same layout as issue_chunk with bounds checks: a row's last, partial
 // chunk (16-byte loads for the vectors inside the row when kVec) and rows
 // that are not 16-byte aligned (element loads). Logits at or past V read as

@@ -152,6 +152,36 @@ int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Grammar-constrained verification (LMDeploy "Speculative Decoding",
+ * structured output: the grammar mask is applied to the target's logits at
+ * every verified position before rejection sampling; drafts were proposed
+ * under the same masks).
+ *
+ * bitmask       [B, K+1, ceil(V/32)] uint32, row-major: token v is allowed at
+ *               position i of request b when bit v % 32 of word
+ *               bitmask[b, i, v / 32] is 1. Disallowed logits of target row i
+ *               and, with draft logits, draft row i count as -inf; the rule
+ *               is then exactly spec_verify_sample / spec_verify_greedy on the
+ *               masked logits. A draft token that is disallowed has p = 0 and
+ *               is rejected; drawn tokens are always allowed.
+ * Every other argument as in spec_verify_sample / spec_verify_greedy; a
+ * position with no allowed token is a caller error (results unspecified,
+ * never an out-of-bounds access). SV_ERR_NULL for a NULL bitmask.
+ */
+int spec_verify_sample_masked(const sv_logits* target, const sv_logits* draft,
+                              const int32_t* draft_tokens, const uint32_t* bitmask,
+                              const float* temperature, const uint64_t* seeds, uint64_t offset,
+                              int32_t B, int32_t K, int32_t V,
+                              int32_t* out_tokens, int32_t* out_accept_len,
+                              float* out_p_draft, float* out_q_draft,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+int spec_verify_greedy_masked(const sv_logits* target, const int32_t* draft_tokens,
+                              const uint32_t* bitmask, int32_t B, int32_t K, int32_t V,
+                              int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_argmax,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Ragged batches: every request has its own draft count K_b (a verifier
  * takes variable-length queries from one forward and maps each output row
  * back to its request: FastDeploy "投机解码", framework design, virtual

@@ -47,7 +47,8 @@ def new_report():
                 max_p_err=0.0, max_q_err=0.0)
 
 
-def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32", report=None):
+def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32", report=None,
+                    bitmask=None):
     """Run the oracle on `requests` and fold the comparison into a report dict."""
     rep = new_report() if report is None else report
     B, K, V = wl["B"], wl["K"], wl["V"]
@@ -55,7 +56,7 @@ def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32"
     o_tok, o_len, o_p, o_q, traces = oracle.spec_verify_sample(
         wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"], wl["seeds"],
         wl["offset"], target_dtype=wl["dtype"], draft_dtype=draft_dtype, requests=reqs,
-        keep_trace=True)
+        keep_trace=True, bitmask=bitmask)
     for b in reqs:
         rep["requests"] += 1
         if b not in traces:                               # refused by the oracle

@@ -159,3 +159,17 @@ def test_ragged_argument_errors(lib):
     assert g(ctypes.byref(t), FAKE, -2, FAKE, 2, 2, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
     assert g(ctypes.byref(t), FAKE, 3, None, 2, 2, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
     assert g(None, FAKE, 3, FAKE, 2, 2, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+
+
+def test_masked_argument_errors(lib):
+    s = lib.spec_verify_sample_masked
+    t = desc()
+    assert s(ctypes.byref(t), None, FAKE, None, FAKE, FAKE, 0, 2, 1, 5, FAKE, FAKE, None, None,
+             FAKE, BIG_WS, None) == sv.SV_ERR_NULL                       # no bitmask
+    assert s(ctypes.byref(t), None, FAKE, FAKE, FAKE, FAKE, 0, 2, 33, 5, FAKE, FAKE, None, None,
+             FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+    assert s(ctypes.byref(t), None, FAKE, FAKE, FAKE, FAKE, 0, 2, 1, 5, FAKE, FAKE, None, None,
+             None, BIG_WS, None) == sv.SV_ERR_WORKSPACE
+    g = lib.spec_verify_greedy_masked
+    assert g(ctypes.byref(t), FAKE, None, 2, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert g(ctypes.byref(t), FAKE, FAKE, 2, 40, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE

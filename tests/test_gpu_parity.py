@@ -454,3 +454,95 @@ def test_ragged_greedy():
     np.testing.assert_array_equal(alen.cpu().numpy(), o_len)
     np.testing.assert_array_equal(tok.cpu().numpy(), o_tok)
     print(f"[parity] ragged greedy: exact, ks={ks.tolist()}", flush=True)
+
+
+# --------------------------------------------------------- grammar masks ---
+def pack_bits(allowed):
+    """uint32 words (bit v % 32 of word v // 32) from a boolean [B, R, V] array."""
+    B, R, V = allowed.shape
+    W = (V + 31) // 32
+    pad = np.zeros((B, R, W * 32), bool)
+    pad[..., :V] = allowed
+    by = np.packbits(pad.reshape(B, R, W, 4, 8), axis=-1, bitorder="little")[..., 0]
+    return np.ascontiguousarray(by).view("<u4").reshape(B, R, W).astype(np.uint32)
+
+
+def grammar_mask(rng, B, R, V, kind):
+    if kind == "dense":
+        allowed = rng.random((B, R, V)) < 0.3
+    else:                                          # a few hundred allowed tokens, clustered
+        allowed = np.zeros((B, R, V), bool)
+        for b in range(B):
+            for r in range(R):
+                starts = rng.integers(0, V, 6)
+                for s in starts:
+                    allowed[b, r, s: s + rng.integers(10, 60)] = True
+    allowed[..., rng.integers(0, V)] = True
+    return allowed
+
+
+def run_masked(wl, mask):
+    d = to_device(wl, DEV)
+    out = sv.spec_verify_sample_masked(d["target"], d["draft"], d["tokens"],
+                                       torch.from_numpy(mask.view(np.int32)).to(DEV),
+                                       d["temperature"], d["seeds"], wl["offset"])
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in out]
+
+
+@pytest.mark.parametrize("cfg,V,kind", [("c3_onehot", 2 * 8192 + 1232, "dense"),
+                                        ("c3_onehot", 20001, "sparse"),
+                                        ("c2_stoch", 3 * 8192 + 1234, "dense"),
+                                        ("c2_stoch", 20001, "sparse")])
+def test_masked_sample(cfg, V, kind):
+    rng = np.random.default_rng(80)
+    wl = make(cfg, data_seed=81, B=16, V=V)
+    R = wl["K"] + 1
+    allowed = grammar_mask(rng, 16, R, V, kind)
+    tok = wl["draft_tokens"].copy()
+    for b in range(16):                            # drafts on allowed tokens, a few on disallowed ones
+        for i in range(wl["K"]):
+            ok = np.nonzero(allowed[b, i])[0]
+            tok[b, i] = ok[rng.integers(0, len(ok))] if b % 4 else tok[b, i]
+    wl = dict(wl, draft_tokens=tok)
+    mask = pack_bits(allowed)
+    print(f"[case] masked {cfg} V={V} {kind}", flush=True)
+    g = run_masked(wl, mask)
+    for b in range(16):
+        for i in range(g[1][b]):
+            assert allowed[b, i, g[0][b, i]]
+    rep = classify_sample(wl, *g, bitmask=mask)
+    assert_report(rep, f"masked {cfg} V={V} {kind}")
+
+
+def test_masked_all_ones_equals_unmasked_bitwise():
+    wl = make("c2_stoch", data_seed=82, B=12, V=9000)
+    ones = np.full((12, 4, (9000 + 31) // 32), 0xFFFFFFFF, np.uint32)
+    for a, b in zip(run_masked(wl, ones), run_sample(wl)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_masked_greedy():
+    rng = np.random.default_rng(83)
+    wl = make("c4_greedy", data_seed=84, B=16, V=3 * 8192 + 5)
+    allowed = grammar_mask(rng, 16, wl["K"] + 1, wl["V"], "sparse")
+    mask = pack_bits(allowed)
+    d = to_device(wl, DEV)
+    tok, alen, g = sv.spec_verify_greedy_masked(d["target"], d["tokens"],
+                                                torch.from_numpy(mask.view(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    o_tok, o_len, o_g = oracle.spec_verify_greedy(wl["target"], wl["draft_tokens"], bitmask=mask)
+    np.testing.assert_array_equal(g.cpu().numpy(), o_g)
+    np.testing.assert_array_equal(alen.cpu().numpy(), o_len)
+    np.testing.assert_array_equal(tok.cpu().numpy(), o_tok)
+
+
+def test_masked_full_size_c3():
+    rng = np.random.default_rng(85)
+    wl = make("c3_onehot", data_seed=2)
+    allowed = rng.random((wl["B"], wl["K"] + 1, wl["V"])) < 0.5
+    mask = pack_bits(allowed)
+    g = run_masked(wl, mask)
+    reqs = list(rng.choice(wl["B"], 32, replace=False))
+    rep = classify_sample(wl, *g, requests=reqs, bitmask=mask)
+    assert_report(rep, "masked c3 full size (32 sampled requests)")

@@ -44,7 +44,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "CONFIGS", "make", "medusa_tree_parents", "f32_to_bf16_bits",
-    "pack_ragged", "make_ragged",
+    "pack_ragged", "make_ragged", "make_masked",
     "bf16_bits_to_f32",
 ]
 
@@ -244,3 +244,22 @@ def make_ragged(name: str, data_seed: int = 0, **kw) -> dict:
     ks = np.random.default_rng([data_seed, 7]).integers(0, wl["K"] + 1, wl["B"])
     wl = dict(wl, name=name.split("_")[0] + "_ragged", ragged=pack_ragged(wl, ks))
     return wl
+
+
+def make_masked(name: str, data_seed: int = 0, allow: float = 0.5, **kw) -> dict:
+    """A named workload plus a grammar bitmask [B, K+1, ceil(V/32)] uint32 that
+    allows each token of each position independently with probability
+    ``allow`` (bit v % 32 of word v // 32 set = allowed; token 0 always
+    allowed so no position is empty). Layout only: nothing is computed."""
+    wl = make(name, data_seed, **kw)
+    B, R, V = wl["B"], wl["K"] + 1, wl["V"]
+    rng = np.random.default_rng([data_seed, 11])
+    allowed = rng.random((B, R, V)) < allow
+    allowed[..., 0] = True
+    W = (V + 31) // 32
+    pad = np.zeros((B, R, W * 32), bool)
+    pad[..., :V] = allowed
+    by = np.packbits(pad.reshape(B, R, W, 4, 8), axis=-1, bitorder="little")[..., 0]
+    mask = np.ascontiguousarray(by).view("<u4").reshape(B, R, W).astype(np.uint32)
+    return dict(wl, name=name.split("_")[0] + "_masked", bitmask=mask,
+                mask_allowed=float(allowed.mean()))
