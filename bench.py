@@ -41,6 +41,7 @@ def source_digest() -> str:
 CHUNK_BYTES = 4096        # the draw re-reads one 4 KiB chunk of logits per request
 RAGGED_BASE = {"c3_ragged": "c3_onehot"}   # ragged workloads: base workload cut to K_b per request
 MASKED_BASE = {"c3_masked": "c3_onehot"}   # grammar-masked workloads: base workload + a bitmask
+LAZY_BASE = {"c3_lazy": "c3_onehot", "c2_lazy": "c2_stoch"}   # early-exit verification of a workload
 
 
 def algorithmic_bytes(wl, rejected=None) -> int:
@@ -67,6 +68,23 @@ def algorithmic_bytes(wl, rejected=None) -> int:
         total += B * min(CHUNK_BYTES, V * es)
         if explicit:
             total += (B if rejected is None else rejected) * 2 * V * es
+    return total
+
+
+def lazy_bytes(wl, accept) -> int:
+    """Bytes early-exit verification must read: for a request that stopped at
+    position a (accept length a + 1), target rows 0..a and draft rows
+    0..min(a, K - 1), plus the draw's chunk, plus (explicit drafts) the stop
+    rows again for the residual when a < K."""
+    import numpy as np
+    es = 2 if wl["dtype"] == "bf16" else 4
+    K, V = wl["K"], wl["V"]
+    explicit = wl.get("draft") is not None
+    a = accept.astype(np.int64) - 1
+    rows = (a + 1) + (np.minimum(a + 1, K) if explicit else 0)
+    total = int(rows.sum()) * V * es + len(a) * min(CHUNK_BYTES, V * es)
+    if explicit:
+        total += int((a < K).sum()) * 2 * V * es
     return total
 
 
@@ -133,7 +151,8 @@ def main():
     ap.add_argument("--workload", default="c3_onehot",
                     help="c1_tiny, c2_stoch, c3_onehot, c4_greedy, c5_tree, c3_ragged "
                          "(C3 with per-request draft counts K_b ~ uniform{0..5}) or c3_masked "
-                         "(C3 with a grammar bitmask allowing each token w.p. 1/2)")
+                         "(C3 with a grammar bitmask allowing each token w.p. 1/2); c3_lazy / c2_lazy "
+                         "run C3 / C2 through early-exit verification")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -157,7 +176,10 @@ def main():
     dev = torch.device("cuda:0")
     ragged = args.workload in RAGGED_BASE
     masked = args.workload in MASKED_BASE
-    if ragged:
+    lazy = args.workload in LAZY_BASE
+    if lazy:
+        wl = dict(make(LAZY_BASE[args.workload], data_seed=0), name=args.workload)
+    elif ragged:
         from workloads import make_ragged
         wl = make_ragged(RAGGED_BASE[args.workload], data_seed=0)
     elif masked:
@@ -217,6 +239,13 @@ def main():
                                                B, K, V, out_tok.data_ptr(), out_len.data_ptr(),
                                                out_p.data_ptr(), out_q.data_ptr(), ws.data_ptr(),
                                                ws_bytes, stream)
+        elif lazy:
+            rc = lib.spec_verify_sample_lazy(ctypes.byref(descs[c]),
+                                             ctypes.byref(ddescs[c]) if ddescs else None,
+                                             tokens.data_ptr(), temp.data_ptr(), seeds.data_ptr(), i,
+                                             B, K, V, out_tok.data_ptr(), out_len.data_ptr(),
+                                             out_p.data_ptr(), out_q.data_ptr(), ws.data_ptr(),
+                                             ws_bytes, stream)
         elif masked:
             rc = lib.spec_verify_sample_masked(ctypes.byref(descs[c]),
                                                ctypes.byref(ddescs[c]) if ddescs else None,
@@ -275,7 +304,9 @@ def main():
     ms_per_step = region_ms / args.steps
     accept = out_len.cpu().numpy()
     rejected = int((accept < K + 1).sum()) if mode == "sample" else None
-    nbytes = algorithmic_bytes(wl, rejected)
+    # the last step's accept lengths stand for every step's (the offset changes
+    # the uniforms, not the drafts' odds)
+    nbytes = lazy_bytes(wl, accept) if lazy else algorithmic_bytes(wl, rejected)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
 
@@ -303,12 +334,18 @@ def main():
                    **({"ragged": {"rows_consulted": int(wl["ragged"]["ks"].sum()) + B,
                                   "k_mean": round(float(wl["ragged"]["ks"].mean()), 3),
                                   "K_max": K}} if ragged else {}),
+                   **({"lazy": {"rows_read_bytes": nbytes,
+                                "dense_bytes": algorithmic_bytes(wl, rejected),
+                                "dense_equivalent_gbps": round(algorithmic_bytes(wl, rejected)
+                                                               / (ms_per_step * 1e-3) / 1e9, 1)}}
+                      if lazy else {}),
                    **({"bitmask": {"allowed_fraction": round(float(wl["mask_allowed"]), 4),
                                    "bytes": int(wl["bitmask"].nbytes)}} if masked else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_record(wl["name"]),
-                     "kernel": "one verification call: row pass + tail" +
+                     "kernel": (f"one verification call: {K + 1} rounds of row pass + decision"
+                                if lazy else "one verification call: row pass + tail") +
                                (" + residual pass" if mode == "sample" and draft is not None else ""),
                      "launch_us_mean": round(mean_launch_ms * 1e3, 2),
                      "launch_us_p10": round(per_launch_ms[len(per_launch_ms) // 10] * 1e3, 2),

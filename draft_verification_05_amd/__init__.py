@@ -9,6 +9,9 @@ Entry points (same names as the C ABI):
   spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset)
   spec_verify_greedy(target, draft_tokens)
   spec_verify_tree(target, node_tokens, parents)
+  spec_verify_sample_ragged / spec_verify_greedy_ragged   (per-request draft counts)
+  spec_verify_sample_masked / spec_verify_greedy_masked   (grammar bitmasks)
+  spec_verify_sample_lazy                                 (early exit at the first rejection)
 """
 from __future__ import annotations
 
@@ -20,7 +23,9 @@ import torch
 
 __all__ = [
     "LIB_PATH", "SpecVerifyError", "load_library", "spec_verify_sample", "spec_verify_greedy",
-    "spec_verify_tree", "spec_verify_workspace_size", "spec_verify_workspace_init",
+    "spec_verify_tree", "spec_verify_sample_ragged", "spec_verify_greedy_ragged",
+    "spec_verify_sample_masked", "spec_verify_greedy_masked", "spec_verify_sample_lazy",
+    "spec_verify_workspace_size", "spec_verify_workspace_init",
     "spec_verify_status_string", "SV_OK", "SV_ERR_NULL", "SV_ERR_SHAPE", "SV_ERR_DTYPE",
     "SV_ERR_STRIDE", "SV_ERR_WORKSPACE", "SV_ERR_TREE", "SV_ERR_HIP", "SV_OP_SAMPLE",
     "SV_OP_GREEDY", "SV_OP_TREE", "SVLogits",
@@ -50,6 +55,8 @@ _SIGNATURES = {
     "spec_verify_workspace_init": (ctypes.c_int, [_vp, _c_size, _vp]),
     "spec_verify_sample": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _c_u64, _c_i32, _c_i32,
                                           _c_i32, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "spec_verify_sample_lazy": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _c_u64, _c_i32, _c_i32,
+                                               _c_i32, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "spec_verify_greedy": (ctypes.c_int, [_PSV, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
                                           _vp, _c_size, _vp]),
     "spec_verify_tree": (ctypes.c_int, [_PSV, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
@@ -188,6 +195,22 @@ def spec_verify_sample(target: torch.Tensor, draft: torch.Tensor | None, draft_t
                        temperature: torch.Tensor, seeds: torch.Tensor, offset: int = 0,
                        *, want_probs: bool = True):
     """Stochastic verification. Returns (tokens [B,K+1], accept_len [B], p_draft [B,K], q_draft [B,K])."""
+    return _sample("spec_verify_sample", target, draft, draft_tokens, temperature, seeds, offset,
+                   want_probs)
+
+
+def spec_verify_sample_lazy(target: torch.Tensor, draft: torch.Tensor | None,
+                            draft_tokens: torch.Tensor, temperature: torch.Tensor,
+                            seeds: torch.Tensor, offset: int = 0, *, want_probs: bool = True):
+    """Early-exit stochastic verification: rows after a request's first rejection are not read.
+
+    Same results as spec_verify_sample (tokens, accept_len); p_draft / q_draft are 0 after
+    the position where the request stopped."""
+    return _sample("spec_verify_sample_lazy", target, draft, draft_tokens, temperature, seeds,
+                   offset, want_probs)
+
+
+def _sample(entry, target, draft, draft_tokens, temperature, seeds, offset, want_probs):
     lib = load_library()
     B, R, V = target.shape
     K = R - 1
@@ -208,13 +231,13 @@ def spec_verify_sample(target: torch.Tensor, draft: torch.Tensor | None, draft_t
     q = torch.empty((B, K), dtype=torch.float32, device=dev) if want_probs else None
     nbytes = spec_verify_workspace_size(SV_OP_SAMPLE, B, K, V, draft is not None)
     ws = _workspace(dev, nbytes)
-    rc = lib.spec_verify_sample(ctypes.byref(tdesc), ctypes.byref(ddesc) if ddesc else None,
-                                draft_tokens.data_ptr() if K else None, temperature.data_ptr(),
-                                seeds.data_ptr(), int(offset) & (2**64 - 1), B, K, V,
-                                tokens.data_ptr(), alen.data_ptr(), _ptr(p), _ptr(q),
-                                ws.data_ptr(), ws.numel(), _stream_ptr(dev))
+    rc = getattr(lib, entry)(ctypes.byref(tdesc), ctypes.byref(ddesc) if ddesc else None,
+                             draft_tokens.data_ptr() if K else None, temperature.data_ptr(),
+                             seeds.data_ptr(), int(offset) & (2**64 - 1), B, K, V,
+                             tokens.data_ptr(), alen.data_ptr(), _ptr(p), _ptr(q),
+                             ws.data_ptr(), ws.numel(), _stream_ptr(dev))
     if rc:
-        raise SpecVerifyError(rc, "spec_verify_sample")
+        raise SpecVerifyError(rc, entry)
     return tokens, alen, p, q
 
 

@@ -59,6 +59,9 @@ struct Args {
   int total_k;                             // ragged: number of packed drafts
   const uint32_t* mask;                    // grammar bitmask [B, K+1, mask_words] or null
   int mask_words;                          // ceil(V / 32)
+  int round;                               // early-exit rounds: position of this round, else -1
+  int round_rows;                          // rows per request in a round (1, or 2 with draft logits)
+  int* alive;                              // [B]: request still open after the previous round
   const float* temperature;                // [B]
   const uint64_t* seeds;                   // [B]
   uint64_t offset;
@@ -305,12 +308,13 @@ __device__ __forceinline__ uint32_t lane_mask_bits(const uint32_t* mrow, int64_t
 // Draw from one row's softmax weights 2^(y - M) (optionally without token
 // `xe`) using that row's row-pass partials; used for the one-hot residual
 // and the bonus token. Returns -1 when the weights have no mass.
-template <int DT, bool kVec, bool kMask>
-__device__ int draw_softmax_row(const Args& A, int b, const Req& rq, int r, float c, float M, int xe,
-                                float u, const TailLds& S, bool cached) {
+// part_of(s) returns the row's chunk partial s.
+template <int DT, bool kVec, bool kMask, class PartOf>
+__device__ int draw_from_partials(const Args& A, int b, const Req& rq, int r, float c, float M, int xe,
+                                  float u, PartOf part_of) {
   constexpr int E = Chunk<DT>::kElems / 64;
   auto W = [&](int s) {
-    const float2 v = partial(A, b, r, s, S, cached);
+    const float2 v = part_of(s);
     return v.x == kNegInf ? 0.f : v.y * fast_exp2(v.x - M);
   };
   int found;
@@ -328,6 +332,13 @@ __device__ int draw_softmax_row(const Args& A, int b, const Req& rq, int r, floa
     w[k] = (e0 + k == xe || !((allow >> k) & 1u)) ? 0.f : v;
   }
   return wave_pick<E>(w, c0, t_in);
+}
+
+template <int DT, bool kVec, bool kMask>
+__device__ int draw_softmax_row(const Args& A, int b, const Req& rq, int r, float c, float M, int xe,
+                                float u, const TailLds& S, bool cached) {
+  return draw_from_partials<DT, kVec, kMask>(A, b, rq, r, c, M, xe, u,
+                                              [&](int s) { return partial(A, b, r, s, S, cached); });
 }
 
 // Copying a request's partials to LDS when they fit: stage_issue starts the
@@ -618,6 +629,124 @@ __device__ void tree_tail(const Args& A, int b, TailLds& S) {
   }
 }
 
+// ------------------------------------------------- early-exit rounds ---
+// The rule stops at the first rejection ("推测解码与 MTP" §2.1), so rows
+// after it are never needed. Round i reads target row i (and draft row i)
+// of the requests still open; the last workgroup of a request to finish
+// its share then decides position i with one wave: accepted -> open for
+// round i + 1; rejected -> draw (or hand the residual to the residual
+// pass) and close; position K -> bonus draw. Everything the decision reads
+// from other workgroups (partials, the gathered logits, the uniforms) is
+// published with agent-scope stores and fetched with agent-scope loads.
+
+// (M, S) of one row from its row-pass workgroup partials.
+__device__ float2 merge_row(const Args& A, int b, int r) {
+  const int lane = threadIdx.x & 63;
+  const float2* wp = A.wpart + ((int64_t)b * A.rows + r) * A.wpr;
+  float m = kNegInf, s = 0.f;
+  for (int w = lane; w < A.wpr; w += 64) {
+    const float2 v = fetch(wp + w);
+    ms_merge(m, s, v.x, v.y);
+  }
+  const float M = wave_max_all(m);
+  s = wave_sum_all((m == kNegInf) ? 0.f : s * fast_exp2(m - M));
+  return make_float2(M, s);
+}
+
+template <int MODE, int DT, bool kVec>
+__device__ void round_decide(const Args& A, int b) {
+  const int lane = threadIdx.x & 63;
+  const int i = A.round, K = A.K, R = A.R, V = A.V;
+  const Req rq = request(A, b);
+  int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
+  const float T = A.temperature[b];
+  if (!(T > 0.f && T < __builtin_inff())) {        // refused request (round 0 only)
+    if (lane <= K) otok[lane] = -1;
+    if (lane < K && A.out_p) A.out_p[(int64_t)b * K + lane] = 0.f;
+    if (lane < K && A.out_q) A.out_q[(int64_t)b * K + lane] = 0.f;
+    if (lane == 0) {
+      A.out_len[b] = 0;
+      A.alive[b] = 0;
+      if (MODE == kExplicit) A.rec[b].pending = 0;
+    }
+    return;
+  }
+  const float c = kLog2e / T;
+  const float2 un = fetch(A.unif + (int64_t)b * R + i);
+  const float2 mp = merge_row(A, b, i);
+  const int64_t rowg0 = (int64_t)b * A.rows;
+  int y;
+  if (i < K) {
+    const int x = A.tokens[(int64_t)b * K + i];
+    const bool valid = (unsigned)x < (unsigned)V;
+    const float lx = valid ? fetch(A.gath + rowg0 + i) : kNegInf;
+    float p, q, Mx = mp.x;
+    bool accept;
+    if (MODE == kOneHot) {
+      // the row's sums leave x out: add its own term back for p(x)
+      Mx = fmaxf(mp.x, lx * c);
+      const float Sx = (mp.x == kNegInf) ? 0.f : mp.y * fast_exp2(mp.x - Mx);
+      const float e = (valid && Mx != kNegInf) ? fast_exp2(fmaf(lx, c, -Mx)) : 0.f;
+      const float St = Sx + e;
+      p = St > 0.f ? e / St : 0.f;
+      q = valid ? 1.f : 0.f;
+      accept = un.x * q < p;
+    } else {
+      const float2 mq = merge_row(A, b, R + i);
+      const float ld = valid ? fetch(A.gath + rowg0 + R + i) : kNegInf;
+      const float dp = fmaf(lx, c, -mp.x), dq = fmaf(ld, c, -mq.x);
+      p = (valid && mp.y > 0.f) ? fast_exp2(dp) / mp.y : 0.f;
+      q = (valid && mq.y > 0.f) ? fast_exp2(dq) / mq.y : 0.f;
+      const float lp = (valid && mp.y > 0.f) ? dp - __log2f(mp.y) : kNegInf;
+      const float lq = (valid && mq.y > 0.f) ? dq - __log2f(mq.y) : kNegInf;
+      accept = __log2f(un.x) + lq < lp;
+      if (!accept && lane == 0) {                  // the residual pass draws this one
+        Record rc;
+        rc.a = i; rc.pending = 1; rc.c = c; rc.u = un.y;
+        rc.Mp = mp.x; rc.Sp = mp.y; rc.Mq = mq.x; rc.Sq = mq.y;
+        A.rec[b] = rc;
+      }
+    }
+    if (lane == 0) {
+      if (A.out_p) A.out_p[(int64_t)b * K + i] = p;
+      if (A.out_q) A.out_q[(int64_t)b * K + i] = q;
+    }
+    if (accept) {
+      if (lane == 0) {
+        otok[i] = x;
+        A.alive[b] = 1;
+      }
+      return;
+    }
+    // stop at a = i: positions after it are padding, their p and q unread
+    if (lane > i && lane <= K) otok[lane] = -1;
+    if (lane > i && lane < K) {
+      if (A.out_p) A.out_p[(int64_t)b * K + lane] = 0.f;
+      if (A.out_q) A.out_q[(int64_t)b * K + lane] = 0.f;
+    }
+    if (lane == 0) {
+      A.out_len[b] = i + 1;
+      A.alive[b] = 0;
+    }
+    if (MODE == kExplicit) return;
+    y = draw_from_partials<DT, kVec, false>(A, b, rq, i, c, Mx, x, un.y, [&](int s) {
+      return fetch(A.part + (rowg0 + i) * A.n_chunk + s);
+    });
+    if (y < 0) y = valid ? x : 0;                  // residual without mass: p's mode
+  } else {                                         // all K accepted: the bonus token from p_K
+    y = draw_from_partials<DT, kVec, false>(A, b, rq, K, c, mp.x, -1, un.y, [&](int s) {
+      return fetch(A.part + (rowg0 + K) * A.n_chunk + s);
+    });
+    if (y < 0) y = 0;
+    if (lane == 0) {
+      A.out_len[b] = K + 1;
+      A.alive[b] = 0;
+      if (MODE == kExplicit) A.rec[b].pending = 0;
+    }
+  }
+  if (lane == 0) otok[i] = y;
+}
+
 // ------------------------------------------------------------ row pass ---
 // Logit (j, k) of a lane's chunk: word k / kPerWord of vector j, widened.
 template <int DT>
@@ -671,8 +800,9 @@ struct RefState {
 // a chunk with finite logits, no smaller than any of them minus 64);
 // (max logit, lowest index of it) for greedy/tree. With a draft token xe in
 // this chunk, its logit goes to `gath` and, for one-hot drafts, it is left
-// out of the sums. `r` holds the lane's four 16-byte vectors.
-template <int MODE, int DT, bool kMask>
+// out of the sums (kPub: stored with an agent-scope store, for readers in
+// the same launch). `r` holds the lane's four 16-byte vectors.
+template <int MODE, int DT, bool kMask, bool kPub>
 __device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, const MaskRaw& mk, int c0, int xe, float c,
                                                 float* gath, RefState& st) {
   constexpr int kPer = Elem<DT>::kPerVec;
@@ -697,7 +827,8 @@ __device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, const MaskRaw& mk, 
         float lx;
         if constexpr (DT == kF32) lx = __uint_as_float(w);
         else lx = half ? bf16_hi(w) : bf16_lo(w);
-        *gath = lx;                               // once per row
+        if constexpr (kPub) publish(gath, lx);    // once per row
+        else *gath = lx;
       }
       if (MODE == kOneHot) {
         uint32_t masked;
@@ -780,14 +911,25 @@ __device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, const MaskRaw& mk, 
 // streams chunks c_lo + v, c_lo + v + 4, ... Full chunks go through a
 // two-deep pipeline of raw 16-byte loads; a row's last, partial chunk and
 // rows that are not 16-byte aligned take the checked element path.
-template <int MODE, int DT, bool kVec, bool kMask>
+// kRound: one early-exit round (rows `round` of the open requests), the
+// decision taken at the end by the request's last workgroup.
+template <int MODE, int DT, bool kVec, bool kMask, bool kRound>
 __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   constexpr int kCE = Chunk<DT>::kElems;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   const int wi = (int)(blockIdx.x % (unsigned)A.wpr);
-  const int rowg = (int)(blockIdx.x / (unsigned)A.wpr);
-  const int b = rowg / A.rows, r = rowg % A.rows;
+  const int slot = (int)(blockIdx.x / (unsigned)A.wpr);
+  int b, r;
+  if constexpr (!kRound) {                        // every row of every request
+    b = slot / A.rows;
+    r = slot % A.rows;
+  } else {                                        // target (and draft) row `round`
+    b = slot / A.round_rows;
+    r = (slot % A.round_rows == 0) ? A.round : A.R + A.round;
+    if (A.round > 0 && !A.alive[b]) return;       // the request stopped in an earlier round
+  }
+  const int rowg = b * A.rows + r;
   const Req rq = request(A, b);
   if (A.cu && !row_live(A, rq, r)) return;        // a ragged request's padding rows: no work
   const char* row = row_ptr(A, rq, r);
@@ -841,7 +983,7 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
       if (kMask) issue_mask<DT>(mrow, (int64_t)(more ? nx : ch) * kCE, A.mask_words, mb);
       __builtin_amdgcn_sched_barrier(0);           // keep the prefetch ahead of the math
       {
-        const float2 res = chunk_partial<MODE, DT, kMask>(ra, ma, ch * kCE, xe, c, gath, rs);
+        const float2 res = chunk_partial<MODE, DT, kMask, kRound>(ra, ma, ch * kCE, xe, c, gath, rs);
         if (lane == 0) s_part[ch - c_lo] = res;
       }
       ch = nx;
@@ -852,7 +994,7 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
       if (kMask) issue_mask<DT>(mrow, (int64_t)(more ? nx : ch) * kCE, A.mask_words, ma);
       __builtin_amdgcn_sched_barrier(0);
       {
-        const float2 res = chunk_partial<MODE, DT, kMask>(rb, mb, ch * kCE, xe, c, gath, rs);
+        const float2 res = chunk_partial<MODE, DT, kMask, kRound>(rb, mb, ch * kCE, xe, c, gath, rs);
         if (lane == 0) s_part[ch - c_lo] = res;
       }
       ch = nx;
@@ -864,14 +1006,20 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
     MaskRaw mr;
     load_chunk_checked<DT, kVec>(row, (int64_t)ch * kCE, A.V, rr);
     if (kMask) issue_mask<DT>(mrow, (int64_t)ch * kCE, A.mask_words, mr);
-    const float2 res = chunk_partial<MODE, DT, kMask>(rr, mr, ch * kCE, xe, c, gath, rs);
+    const float2 res = chunk_partial<MODE, DT, kMask, kRound>(rr, mr, ch * kCE, xe, c, gath, rs);
     if (lane == 0) s_part[ch - c_lo] = res;
   }
   __syncthreads();
   float2* part = A.part + (int64_t)rowg * A.n_chunk;
-  for (int i = tid; i < c_hi - c_lo; i += kThreads) part[c_lo + i] = s_part[i];
+  for (int i = tid; i < c_hi - c_lo; i += kThreads) {
+    if constexpr (kRound) publish(part + c_lo + i, s_part[i]);
+    else part[c_lo + i] = s_part[i];
+  }
   if (MODE == kOneHot || MODE == kExplicit) {
-    if (r == 0 && wi == A.wpr - 1 && tid < A.R) A.unif[(int64_t)b * A.R + tid] = s_unif[tid];
+    if (r == 0 && wi == A.wpr - 1 && tid < A.R) {
+      if constexpr (kRound) publish(A.unif + (int64_t)b * A.R + tid, s_unif[tid]);
+      else A.unif[(int64_t)b * A.R + tid] = s_unif[tid];
+    }
   }
   // wave 0 also folds the workgroup's partials into one, so the tail merges
   // wpr values per row instead of n_chunk
@@ -890,7 +1038,15 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
       wave_argmax_all(v, idx);
       acc = make_float2(v, __int_as_float(idx));
     }
-    if (lane == 0) A.wpart[(int64_t)rowg * A.wpr + wi] = acc;
+    if (lane == 0) {
+      if constexpr (kRound) publish(A.wpart + (int64_t)rowg * A.wpr + wi, acc);
+      else A.wpart[(int64_t)rowg * A.wpr + wi] = acc;
+    }
+  }
+  if constexpr (kRound && (MODE == kOneHot || MODE == kExplicit)) {
+    __shared__ int s_last;
+    if (!last_of_request(A.counters + b, (unsigned)(A.round_rows * A.wpr), &s_last)) return;
+    if (wave == 0) round_decide<MODE, DT, kVec>(A, b);
   }
 }
 
@@ -1014,12 +1170,12 @@ using namespace sv;
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t part, wpart, gath, rec, res, unif, total;
+  size_t part, wpart, gath, rec, res, unif, alive, total;
 };
 
 // Workspace: [counters: 4 * SV_MAX_BATCH][chunk partials][workgroup
 //            partials][gathered logits][records][residual partials]
-//            [uniforms]
+//            [uniforms][alive flags]
 Layout layout(int64_t B, int64_t rows, int64_t V) {
   const int64_t ce = Chunk<kF32>::kElems;          // the smaller chunk: a bound for both dtypes
   const int64_t nch = (V + ce - 1) / ce;
@@ -1030,7 +1186,8 @@ Layout layout(int64_t B, int64_t rows, int64_t V) {
   L.rec = align_up(L.gath + (size_t)(B * rows) * sizeof(float), 256);
   L.res = align_up(L.rec + (size_t)B * sizeof(Record), 256);
   L.unif = align_up(L.res + (size_t)(B * nch) * sizeof(float), 256);
-  L.total = align_up(L.unif + (size_t)(B * rows) * sizeof(float2), 256);   // R <= rows
+  L.alive = align_up(L.unif + (size_t)(B * rows) * sizeof(float2), 256);   // R <= rows
+  L.total = align_up(L.alive + (size_t)B * sizeof(int), 256);
   return L;
 }
 
@@ -1075,6 +1232,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.drf = nullptr; A.d_sb = 0; A.d_sk = 0;
   A.cu = nullptr; A.total_k = 0;
   A.mask = nullptr; A.mask_words = (V + 31) / 32;
+  A.round = -1; A.round_rows = 0;
   A.B = B; A.K = K; A.V = V; A.R = R; A.rows = rows;
   const int ce = t->dtype == SV_DTYPE_BF16 ? Chunk<kBF16>::kElems : Chunk<kF32>::kElems;
   A.n_chunk = (V + ce - 1) / ce;
@@ -1090,6 +1248,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.rec = reinterpret_cast<Record*>(base + L.rec);
   A.res_part = reinterpret_cast<float*>(base + L.res);
   A.unif = reinterpret_cast<float2*>(base + L.unif);
+  A.alive = reinterpret_cast<int*>(base + L.alive);
   A.out_p = nullptr; A.out_q = nullptr; A.out_aux = nullptr;
   A.temperature = nullptr; A.seeds = nullptr; A.offset = 0;
   A.n_nodes = 0;
@@ -1103,7 +1262,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
 // request, back to back on the caller's stream.
 template <int MODE, int DT, bool kVec, bool kMask>
 void launch_pair(const Args& A, unsigned grid, hipStream_t st) {
-  SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask>), grid, st, A);
+  SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask, false>), grid, st, A);
   hipLaunchKernelGGL((sv_tail_kernel<MODE, DT, kVec, kMask>), dim3((unsigned)A.B), dim3(64), 0, st, A);
 }
 
@@ -1147,6 +1306,19 @@ void launch_residual(const Args& A, int dtype, bool vec, unsigned grid, hipStrea
   else                        launch_residual_dt<kF32>(A, vec, grid, st);
 }
 
+// One early-exit round: the row pass over this round's rows, which ends in
+// the per-request decision.
+template <int MODE>
+void launch_round(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
+  if (dtype == SV_DTYPE_BF16) {
+    if (vec) SV_LAUNCH((sv_rows_kernel<MODE, kBF16, true, false, true>), grid, st, A);
+    else     SV_LAUNCH((sv_rows_kernel<MODE, kBF16, false, false, true>), grid, st, A);
+  } else {
+    if (vec) SV_LAUNCH((sv_rows_kernel<MODE, kF32, true, false, true>), grid, st, A);
+    else     SV_LAUNCH((sv_rows_kernel<MODE, kF32, false, false, true>), grid, st, A);
+  }
+}
+
 // A dispatch counts work-items in 32 bits per dimension.
 int check_grid(int64_t wgs) {
   return (wgs >= 1 && wgs <= (int64_t)(UINT32_MAX / kThreads)) ? SV_OK : SV_ERR_SHAPE;
@@ -1157,7 +1329,7 @@ int hip_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; 
 // Sampling, dense (cu null: [B, K + 1] rows by the two strides) or ragged
 // (cu [B + 1] device prefix sums, packed rows by stride_k, stride_b unused).
 int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* cu, int32_t total_k,
-                const uint32_t* mask, const int32_t* draft_tokens, const float* temperature,
+                const uint32_t* mask, bool lazy, const int32_t* draft_tokens, const float* temperature,
                 const uint64_t* seeds, uint64_t offset,
                 int32_t B, int32_t K, int32_t V,
                 int32_t* out_tokens, int32_t* out_accept_len,
@@ -1197,10 +1369,31 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
   A.out_len = out_accept_len;
   A.out_p = out_p_draft;
   A.out_q = out_q_draft;
-  const int64_t wgs = (int64_t)B * rows * A.wpr;
-  if ((st = check_grid(wgs))) return st;
   const bool vec = aligned16(target) && (!explicit_q || aligned16(draft));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (lazy) {                                      // early-exit rounds, one position at a time
+    for (int i = 0; i <= K; ++i) {
+      Args Ai = A;
+      Ai.round = i;
+      Ai.round_rows = (explicit_q && i < K) ? 2 : 1;
+      Ai.cpw = chunks_per_wg((int64_t)B * Ai.round_rows, A.n_chunk);
+      Ai.wpr = (A.n_chunk + Ai.cpw - 1) / Ai.cpw;
+      const int64_t g = (int64_t)B * Ai.round_rows * Ai.wpr;
+      if ((st = check_grid(g))) return st;
+      if (explicit_q) launch_round<kExplicit>(Ai, target->dtype, vec, (unsigned)g, s);
+      else            launch_round<kOneHot>(Ai, target->dtype, vec, (unsigned)g, s);
+      if ((st = hip_status())) return st;
+    }
+    if (explicit_q) {
+      Args A2 = A;
+      A2.cpw = chunks_per_wg(B, A.n_chunk);
+      A2.wpr = (A.n_chunk + A2.cpw - 1) / A2.cpw;
+      launch_residual(A2, target->dtype, vec, (unsigned)((int64_t)B * A2.wpr), s);
+    }
+    return hip_status();
+  }
+  const int64_t wgs = (int64_t)B * rows * A.wpr;
+  if ((st = check_grid(wgs))) return st;
   if (explicit_q) {
     launch_rows<kExplicit>(A, target->dtype, vec, (unsigned)wgs, s);
     if ((st = hip_status())) return st;
@@ -1288,9 +1481,21 @@ int spec_verify_sample(const sv_logits* target, const sv_logits* draft,
                        int32_t* out_tokens, int32_t* out_accept_len,
                        float* out_p_draft, float* out_q_draft,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return sample_impl(target, draft, nullptr, 0, nullptr, draft_tokens, temperature, seeds, offset, B,
-                     K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft, workspace,
-                     workspace_bytes, stream);
+  return sample_impl(target, draft, nullptr, 0, nullptr, false, draft_tokens, temperature, seeds,
+                     offset, B, K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft,
+                     workspace, workspace_bytes, stream);
+}
+
+int spec_verify_sample_lazy(const sv_logits* target, const sv_logits* draft,
+                            const int32_t* draft_tokens, const float* temperature,
+                            const uint64_t* seeds, uint64_t offset,
+                            int32_t B, int32_t K, int32_t V,
+                            int32_t* out_tokens, int32_t* out_accept_len,
+                            float* out_p_draft, float* out_q_draft,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return sample_impl(target, draft, nullptr, 0, nullptr, true, draft_tokens, temperature, seeds,
+                     offset, B, K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft,
+                     workspace, workspace_bytes, stream);
 }
 
 int spec_verify_sample_masked(const sv_logits* target, const sv_logits* draft,
@@ -1301,9 +1506,9 @@ int spec_verify_sample_masked(const sv_logits* target, const sv_logits* draft,
                               float* out_p_draft, float* out_q_draft,
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!bitmask) return SV_ERR_NULL;
-  return sample_impl(target, draft, nullptr, 0, bitmask, draft_tokens, temperature, seeds, offset, B,
-                     K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft, workspace,
-                     workspace_bytes, stream);
+  return sample_impl(target, draft, nullptr, 0, bitmask, false, draft_tokens, temperature, seeds,
+                     offset, B, K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft,
+                     workspace, workspace_bytes, stream);
 }
 
 int spec_verify_sample_ragged(const sv_logits* target, const sv_logits* draft,
@@ -1319,7 +1524,7 @@ int spec_verify_sample_ragged(const sv_logits* target, const sv_logits* draft,
   sv_logits t = *target, d = draft ? *draft : sv_logits{};
   t.stride_b = 0;                                   // packed rows: stride_k only
   d.stride_b = 0;
-  return sample_impl(&t, draft ? &d : nullptr, cu_draft, total_k, nullptr, draft_tokens, temperature,
+  return sample_impl(&t, draft ? &d : nullptr, cu_draft, total_k, nullptr, false, draft_tokens, temperature,
                      seeds, offset, B, K_max, V, out_tokens, out_accept_len, out_p_draft,
                      out_q_draft, workspace, workspace_bytes, stream);
 }

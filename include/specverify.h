@@ -152,6 +152,26 @@ int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Early-exit ("lazy") stochastic verification. The rule stops at the first
+ * rejection ("推测解码与 MTP" §2.1), so the rows after it are never needed:
+ * this call reads position by position (round i reads target row i, and
+ * draft row i, only of the requests still open after round i - 1) instead
+ * of every row at once. It costs K + 1 dependent rounds and pays off when
+ * drafts are rejected early. Tokens, accept lengths and the uniforms used
+ * are those of spec_verify_sample; out_p_draft / out_q_draft hold p_i(x_i) /
+ * q_i(x_i) up to the stop position and 0 after it (those rows are not
+ * read). Arguments, limits and errors as spec_verify_sample; the workspace
+ * is sized as for it.
+ */
+int spec_verify_sample_lazy(const sv_logits* target, const sv_logits* draft,
+                            const int32_t* draft_tokens, const float* temperature,
+                            const uint64_t* seeds, uint64_t offset,
+                            int32_t B, int32_t K, int32_t V,
+                            int32_t* out_tokens, int32_t* out_accept_len,
+                            float* out_p_draft, float* out_q_draft,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Grammar-constrained verification (LMDeploy "Speculative Decoding",
  * structured output: the grammar mask is applied to the target's logits at
  * every verified position before rejection sampling; drafts were proposed

@@ -48,8 +48,11 @@ def new_report():
 
 
 def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32", report=None,
-                    bitmask=None):
-    """Run the oracle on `requests` and fold the comparison into a report dict."""
+                    bitmask=None, lazy=False):
+    """Run the oracle on `requests` and fold the comparison into a report dict.
+
+    lazy: the outputs of early-exit verification, which computes p and q only
+    up to the position where a request stopped and leaves 0 after it."""
     rep = new_report() if report is None else report
     B, K, V = wl["B"], wl["K"], wl["V"]
     reqs = list(range(B)) if requests is None else list(requests)
@@ -66,9 +69,13 @@ def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32"
                 rep["mismatches"].append((b, "refusal", int(g_len[b])))
             continue
         tr = traces[b]
-        if K:
-            rep["max_p_err"] = max(rep["max_p_err"], float(np.max(np.abs(g_p[b] - o_p[b]))))
-            rep["max_q_err"] = max(rep["max_q_err"], float(np.max(np.abs(g_q[b] - o_q[b]))))
+        n = min(max(int(g_len[b]), 0), K) if lazy else K
+        if n:
+            rep["max_p_err"] = max(rep["max_p_err"], float(np.max(np.abs(g_p[b, :n] - o_p[b, :n]))))
+            rep["max_q_err"] = max(rep["max_q_err"], float(np.max(np.abs(g_q[b, :n] - o_q[b, :n]))))
+        if n < K and (np.any(g_p[b, n:] != 0) or np.any(g_q[b, n:] != 0)):
+            rep["mismatches"].append((b, "p/q after the stop", g_p[b, n:].tolist(), g_q[b, n:].tolist()))
+            continue
         a_o, a_g = int(o_len[b]) - 1, int(g_len[b]) - 1
         if not 0 <= a_g <= K:
             rep["mismatches"].append((b, "accept_len", a_g + 1))

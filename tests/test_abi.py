@@ -173,3 +173,21 @@ def test_masked_argument_errors(lib):
     g = lib.spec_verify_greedy_masked
     assert g(ctypes.byref(t), FAKE, None, 2, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
     assert g(ctypes.byref(t), FAKE, FAKE, 2, 40, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+
+
+def test_lazy_argument_errors(lib):
+    s = lib.spec_verify_sample_lazy
+    t = desc()
+
+    def call(t=t, d=None, B=2, K=1, V=5, temp=FAKE, seeds=FAKE, ws=FAKE, wsb=BIG_WS):
+        return s(ctypes.byref(t) if t is not None else None, ctypes.byref(d) if d is not None else None,
+                 FAKE, temp, seeds, 0, B, K, V, FAKE, FAKE, None, None, ws, wsb, None)
+
+    assert call(t=None) == sv.SV_ERR_NULL
+    assert call(temp=None) == sv.SV_ERR_NULL
+    assert call(B=0) == sv.SV_ERR_SHAPE
+    assert call(K=33) == sv.SV_ERR_SHAPE
+    assert call(ws=None) == sv.SV_ERR_WORKSPACE
+    need = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, 2, 1, 5)
+    assert call(wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    assert call(d=desc(dtype=1)) == sv.SV_ERR_DTYPE

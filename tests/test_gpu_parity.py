@@ -546,3 +546,89 @@ def test_masked_full_size_c3():
     reqs = list(rng.choice(wl["B"], 32, replace=False))
     rep = classify_sample(wl, *g, requests=reqs, bitmask=mask)
     assert_report(rep, "masked c3 full size (32 sampled requests)")
+
+
+# ------------------------------------------------------------ early exit ---
+def run_lazy(wl, offset=None):
+    d = to_device(wl, DEV)
+    off = wl["offset"] if offset is None else offset
+    out = sv.spec_verify_sample_lazy(d["target"], d["draft"], d["tokens"], d["temperature"],
+                                     d["seeds"], off)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+LAZY_REDUCED = [
+    ("c3-ragged-aligned", "c3_onehot", dict(B=32, V=2 * 8192 + 1232)),
+    ("c3-odd-V-scalar-path", "c3_onehot", dict(B=24, V=2 * 8192 + 777)),
+    ("c3-K1", "c3_onehot", dict(B=40, K=1, V=9000)),
+    ("c3-K0", "c3_onehot", dict(B=16, K=0, V=5000)),
+    ("c2-ragged", "c2_stoch", dict(B=16, V=3 * 8192 + 1234)),
+    ("c2-odd-V-scalar-path", "c2_stoch", dict(B=12, V=20001)),
+    ("c1-full", "c1_tiny", {}),
+]
+
+
+@pytest.mark.parametrize("name,cfg,kw", LAZY_REDUCED, ids=[c[0] for c in LAZY_REDUCED])
+def test_lazy_sample(name, cfg, kw):
+    for offset in range(3):
+        wl = make(cfg, data_seed=300 + offset, offset=offset, **kw)
+        print(f"[case] lazy {name}/off{offset} B={wl['B']} K={wl['K']} V={wl['V']}", flush=True)
+        g = run_lazy(wl)
+        assert_report(classify_sample(wl, *g, lazy=True), f"lazy {name}/off{offset}")
+
+
+def test_lazy_edge_device_values():
+    """Refused temperatures and out-of-range drafts stop a request in the first rounds."""
+    wl = make("c3_onehot", data_seed=310, B=16, V=9000)
+    T = wl["temperature"].copy()
+    T[[1, 2, 3, 4]] = [0.0, -1.0, np.nan, np.inf]
+    tok = wl["draft_tokens"].copy()
+    tok[5, 0] = -1
+    tok[6, 3] = 9000
+    wl = dict(wl, temperature=T, draft_tokens=tok)
+    print("[case] lazy edge values", flush=True)
+    assert_report(classify_sample(wl, *run_lazy(wl), lazy=True), "lazy edge values")
+
+
+def test_lazy_all_accepted_and_first_rejected():
+    """Drafts equal to the target's mode at low temperature run every round; drafts the
+    target gives no mass stop in round 0."""
+    wl = make("c3_onehot", data_seed=311, B=24, V=9000)
+    tgt = wl["target"].copy()
+    tok = wl["draft_tokens"].copy()
+    hi = f32_to_bf16_bits(np.array([60.0], np.float32))[0]
+    for b in range(12):                             # mode = draft token, sharp target
+        tgt[b, np.arange(wl["K"]), tok[b]] = hi
+    for b in range(12, 24):                         # draft token masked out of the target
+        tgt[b, 0, tok[b, 0]] = 0xFF80
+    wl = dict(wl, target=tgt, temperature=np.full(24, 0.25, np.float32))
+    g = run_lazy(wl)
+    print("[case] lazy all-accepted / first-rejected", flush=True)
+    assert_report(classify_sample(wl, *g, lazy=True), "lazy extremes")
+    assert np.all(g[1][:12] == wl["K"] + 1) and np.all(g[1][12:] == 1)
+
+
+@pytest.mark.parametrize("cfg", ["c2_stoch", "c3_onehot"])
+def test_lazy_full_size(cfg):
+    wl = make(cfg, data_seed=1)
+    print(f"[case] lazy {cfg} full", flush=True)
+    assert_report(classify_sample(wl, *run_lazy(wl), lazy=True), f"lazy {cfg} full")
+
+
+def test_lazy_agrees_with_dense_and_reuses_workspace():
+    """Same uniforms as the dense rule: tokens agree with it wherever neither side sits at a
+    decision boundary, and interleaved dense / lazy calls do not disturb one another."""
+    wl = make("c3_onehot", data_seed=312, B=64, V=20000)
+    d1 = run_sample(wl)
+    l1 = run_lazy(wl)
+    d2 = run_sample(wl)
+    l2 = run_lazy(wl)
+    for a, b in zip(d1, d2):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(l1, l2):
+        np.testing.assert_array_equal(a, b)
+    rep = classify_sample(wl, *l1, lazy=True)
+    assert_report(rep, "lazy vs oracle")
+    differ = int(np.sum(np.any(d1[0] != l1[0], axis=1)))
+    assert differ <= rep["near_accept"][1e-5] + rep["near_select"][1e-5]
