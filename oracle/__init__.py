@@ -20,6 +20,11 @@ Parity pins (each checked by ``tests/test_oracle_*.py`` without a GPU):
   * grammar bitmasks: the bit layout against numpy's own bit unpacking; an
     all-ones mask changes nothing; emitted tokens are always allowed and
     disallowed drafts are always rejected.
+  * top-k / top-p filters: brute force over every upper set of a row
+    (top-k: the largest cut holding at least k tokens; top-p: the largest
+    cut holding at least top_p of the mass), hand-computed small rows, the
+    switched-off and single-token limits, and the exact law of the filtered
+    rule (it emits the filtered target distribution).
 Parity unpinned: individual draws whose uniform lies within 1e-5 of an
 acceptance threshold or CDF boundary (the GPU works in fp32); they are
 counted by the parity tests, not matched.

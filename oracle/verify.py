@@ -64,7 +64,7 @@ __all__ = [
     "inverse_cdf", "verify_request", "spec_verify_sample", "argmax_lowest",
     "spec_verify_greedy", "tree_depths", "spec_verify_tree",
     "ragged_draft_count", "spec_verify_sample_ragged", "spec_verify_greedy_ragged",
-    "apply_bitmask",
+    "apply_bitmask", "filter_keep", "filtered_row",
 ]
 
 
@@ -92,6 +92,60 @@ def apply_bitmask(logits: np.ndarray, mask_row) -> np.ndarray:
         if not (int(mask_row[v // 32]) >> (v % 32)) & 1:
             out[v] = -math.inf
     return out
+
+
+# ------------------------------------------------ top-k / top-p filters ---
+# The pages run speculative decoding with the sampling parameters
+# temperature 0.8 and top_p 0.95 ([VA] "Speculative Decoding Guide", the
+# offline-inference examples). Reading: p and q are the distributions the
+# sampler would draw from, so both are filtered with the request's (top_k,
+# top_p) after the temperature. top-k keeps the tokens whose logit is at
+# least the k-th largest logit (ties at the cut are kept). top-p then keeps,
+# of those, the tokens whose logit is at least t, where t is the largest
+# logit value whose upper set {v : l_v >= t} holds at least top_p of the
+# top-k set's mass. The kept set is renormalised. top_k <= 0 or >= V, and
+# top_p >= 1 or NaN, switch the filter off.
+
+def filter_keep(logits, T: float, top_k: int = 0, top_p: float = 1.0):
+    """Kept tokens of one row under (top_k, top_p), and the top-p decision's
+    margin: the distance, as a fraction of the top-k mass, from top_p to the
+    nearer of the two cumulative masses that bracket it (inf when top-p is
+    off). A computation that rounds its masses by less than the margin
+    keeps the same set."""
+    l = np.asarray(logits, dtype=np.float64)
+    V = len(l)
+    keep = np.ones(V, dtype=bool)
+    if 0 < int(top_k) < V:
+        kth = np.sort(l)[::-1][int(top_k) - 1]
+        keep = l >= kth
+    margin = math.inf
+    if float(top_p) < 1.0:                          # NaN compares false: off
+        w = softmax_t(l, T) * keep
+        Z = math.fsum(w.tolist())
+        values = np.unique(l[keep])[::-1]            # distinct kept values, largest first
+        above = 0.0                                  # mass strictly above the current value
+        t = values[-1]
+        for v in values:
+            upper = above + math.fsum(w[l == v].tolist()) / Z
+            if upper >= float(top_p):
+                t = v
+                # nothing lies above the largest value: that side is exact
+                margin = upper - float(top_p) if v == values[0] else min(float(top_p) - above,
+                                                                         upper - float(top_p))
+                break
+            above = upper
+        keep = keep & (l >= t)
+    return keep, margin
+
+
+def filtered_row(logits, T: float, top_k: int = 0, top_p: float = 1.0):
+    """softmax(logits / T) restricted to the kept set and renormalised; and the margin."""
+    keep, margin = filter_keep(logits, T, top_k, top_p)
+    p = softmax_t(logits, T)
+    if keep.all():
+        return p, margin
+    w = p * keep
+    return w / math.fsum(w.tolist()), margin
 
 
 def softmax_t(logits: np.ndarray, T: float) -> np.ndarray:
@@ -166,7 +220,7 @@ def verify_request(p_rows, q_rows, x, u_acc, u_smp) -> dict:
 
 def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0,
                        target_dtype="f32", draft_dtype="f32", requests=None,
-                       keep_trace=False, bitmask=None):
+                       keep_trace=False, bitmask=None, top_k=None, top_p=None):
     """Batched stochastic verification.
 
     target [B, K+1, V] (fp32 values or bf16 bit patterns), draft [B, >=K, V]
@@ -180,6 +234,9 @@ def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0
     A request whose temperature is not a finite positive number is refused:
     accept_len 0, tokens -1, probabilities 0. ``bitmask`` [B, K+1, ceil(V/32)]
     (optional) masks target row i and, with draft logits, draft row i.
+    ``top_k`` [B] and ``top_p`` [B] (optional) filter every target row and,
+    with draft logits, every draft row (``filter_keep``); the trace then
+    holds the smallest top-p margin of the request's rows.
     """
     B, R, V = target.shape
     K = R - 1
@@ -194,12 +251,20 @@ def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0
             continue
         def masked(l, i):
             return l if bitmask is None else apply_bitmask(l, bitmask[b, i])
-        p_rows = [softmax_t(masked(logits_f64(target[b, i], target_dtype), i), T).tolist()
-                  for i in range(K + 1)]
+        tk = 0 if top_k is None else int(top_k[b])
+        tp = 1.0 if top_p is None else float(top_p[b])
+        margins = []
+
+        def dist(l):
+            if top_k is None and top_p is None:
+                return softmax_t(l, T).tolist()
+            row, m = filtered_row(l, T, tk, tp)
+            margins.append(m)
+            return row.tolist()
+        p_rows = [dist(masked(logits_f64(target[b, i], target_dtype), i)) for i in range(K + 1)]
         x = [int(v) for v in draft_tokens[b, :K]]
         if draft is not None:
-            q_rows = [softmax_t(masked(logits_f64(draft[b, i], draft_dtype), i), T).tolist()
-                      for i in range(K)]
+            q_rows = [dist(masked(logits_f64(draft[b, i], draft_dtype), i)) for i in range(K)]
         else:
             q_rows = [onehot(V, x[i]) for i in range(K)]
         pairs = [request_uniforms(int(seeds[b]), b, i, int(offset)) for i in range(K + 1)]
@@ -209,6 +274,7 @@ def spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset=0
         p_draft[b, :] = res["p_x"]
         q_draft[b, :] = res["q_x"]
         if keep_trace:
+            res["filter_margin"] = min(margins) if margins else math.inf
             traces[b] = res
     return tokens, accept_len, p_draft, q_draft, traces
 
