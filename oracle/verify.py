@@ -122,18 +122,18 @@ def filter_keep(logits, T: float, top_k: int = 0, top_p: float = 1.0):
     if float(top_p) < 1.0:                          # NaN compares false: off
         w = softmax_t(l, T) * keep
         Z = math.fsum(w.tolist())
-        values = np.unique(l[keep])[::-1]            # distinct kept values, largest first
-        above = 0.0                                  # mass strictly above the current value
-        t = values[-1]
-        for v in values:
-            upper = above + math.fsum(w[l == v].tolist()) / Z
-            if upper >= float(top_p):
-                t = v
-                # nothing lies above the largest value: that side is exact
-                margin = upper - float(top_p) if v == values[0] else min(float(top_p) - above,
-                                                                         upper - float(top_p))
-                break
-            above = upper
+        # distinct kept values, largest first, with the mass of each
+        vals, inv = np.unique(l[keep], return_inverse=True)
+        group = np.bincount(inv, weights=w[keep])[::-1] / Z
+        vals = vals[::-1]
+        upper = np.cumsum(group)                     # mass of {l >= vals[j]}
+        hit = np.nonzero(upper >= float(top_p))[0]
+        j = int(hit[0]) if len(hit) else len(vals) - 1
+        t = vals[j]
+        above = upper[j - 1] if j > 0 else 0.0
+        # nothing lies above the largest value: that side is exact
+        margin = upper[j] - float(top_p) if j == 0 else min(float(top_p) - above,
+                                                            upper[j] - float(top_p))
         keep = keep & (l >= t)
     return keep, margin
 
