@@ -42,6 +42,8 @@ CHUNK_BYTES = 4096        # the draw re-reads one 4 KiB chunk of logits per requ
 RAGGED_BASE = {"c3_ragged": "c3_onehot"}   # ragged workloads: base workload cut to K_b per request
 MASKED_BASE = {"c3_masked": "c3_onehot"}   # grammar-masked workloads: base workload + a bitmask
 LAZY_BASE = {"c3_lazy": "c3_onehot", "c2_lazy": "c2_stoch"}   # early-exit verification of a workload
+# top-k / top-p filtered verification: base workload, top_k, top_p (the pages' top_p 0.95)
+FILTER_BASE = {"c3_topp": ("c3_onehot", 0, 0.95), "c2_topp": ("c2_stoch", 0, 0.95)}
 
 
 def algorithmic_bytes(wl, rejected=None) -> int:
@@ -112,7 +114,8 @@ def cpu_baseline(wl, seconds: float):
         if rg is None:
             oracle.spec_verify_sample(wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"],
                                       wl["seeds"], wl["offset"], target_dtype=wl["dtype"], requests=[n],
-                                      bitmask=wl.get("bitmask"))
+                                      bitmask=wl.get("bitmask"), top_k=wl.get("top_k"),
+                                      top_p=wl.get("top_p"))
         else:                                       # request n alone, as a one-request ragged batch
             c0, c1 = int(rg["cu"][n]), int(rg["cu"][n + 1])
             oracle.spec_verify_sample_ragged(
@@ -152,7 +155,8 @@ def main():
                     help="c1_tiny, c2_stoch, c3_onehot, c4_greedy, c5_tree, c3_ragged "
                          "(C3 with per-request draft counts K_b ~ uniform{0..5}) or c3_masked "
                          "(C3 with a grammar bitmask allowing each token w.p. 1/2); c3_lazy / c2_lazy "
-                         "run C3 / C2 through early-exit verification")
+                         "run C3 / C2 through early-exit verification; c3_topp / c2_topp "
+                         "add a top_p 0.95 filter")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -177,7 +181,13 @@ def main():
     ragged = args.workload in RAGGED_BASE
     masked = args.workload in MASKED_BASE
     lazy = args.workload in LAZY_BASE
-    if lazy:
+    filt = args.workload in FILTER_BASE
+    if filt:
+        base, f_k, f_p = FILTER_BASE[args.workload]
+        wl = dict(make(base, data_seed=0), name=args.workload)
+        wl["top_k"] = np.full(wl["B"], f_k, np.int32)
+        wl["top_p"] = np.full(wl["B"], f_p, np.float32)
+    elif lazy:
         wl = dict(make(LAZY_BASE[args.workload], data_seed=0), name=args.workload)
     elif ragged:
         from workloads import make_ragged
@@ -217,6 +227,9 @@ def main():
         out_p = torch.empty((total_k if ragged else B * K,), dtype=torch.float32, device=dev)
         out_q = torch.empty((total_k if ragged else B * K,), dtype=torch.float32, device=dev)
         ws_bytes = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, B, K, V, draft is not None)
+        if filt:
+            top_k = torch.full((B,), f_k, dtype=torch.int32, device=dev)
+            top_p = torch.full((B,), f_p, dtype=torch.float32, device=dev)
     elif mode == "greedy":
         out_g = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
         ws_bytes = sv.spec_verify_workspace_size(sv.SV_OP_GREEDY, B, K, V)
@@ -239,6 +252,14 @@ def main():
                                                B, K, V, out_tok.data_ptr(), out_len.data_ptr(),
                                                out_p.data_ptr(), out_q.data_ptr(), ws.data_ptr(),
                                                ws_bytes, stream)
+        elif filt:
+            rc = lib.spec_verify_sample_filtered(ctypes.byref(descs[c]),
+                                                 ctypes.byref(ddescs[c]) if ddescs else None,
+                                                 tokens.data_ptr(), temp.data_ptr(), top_k.data_ptr(),
+                                                 top_p.data_ptr(), seeds.data_ptr(), i, B, K, V,
+                                                 out_tok.data_ptr(), out_len.data_ptr(),
+                                                 out_p.data_ptr(), out_q.data_ptr(), ws.data_ptr(),
+                                                 ws_bytes, stream)
         elif lazy:
             rc = lib.spec_verify_sample_lazy(ctypes.byref(descs[c]),
                                              ctypes.byref(ddescs[c]) if ddescs else None,
@@ -339,13 +360,15 @@ def main():
                                 "dense_equivalent_gbps": round(algorithmic_bytes(wl, rejected)
                                                                / (ms_per_step * 1e-3) / 1e9, 1)}}
                       if lazy else {}),
+                   **({"filter": {"top_k": f_k, "top_p": f_p}} if filt else {}),
                    **({"bitmask": {"allowed_fraction": round(float(wl["mask_allowed"]), 4),
                                    "bytes": int(wl["bitmask"].nbytes)}} if masked else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_record(wl["name"]),
                      "kernel": (f"one verification call: {K + 1} rounds of row pass + decision"
-                                if lazy else "one verification call: row pass + tail") +
+                                if lazy else "one verification call: row pass + select pass + tail"
+                                if filt else "one verification call: row pass + tail") +
                                (" + residual pass" if mode == "sample" and draft is not None else ""),
                      "launch_us_mean": round(mean_launch_ms * 1e3, 2),
                      "launch_us_p10": round(per_launch_ms[len(per_launch_ms) // 10] * 1e3, 2),

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   spec_verify_sample_ragged / spec_verify_greedy_ragged   (per-request draft counts)
   spec_verify_sample_masked / spec_verify_greedy_masked   (grammar bitmasks)
   spec_verify_sample_lazy                                 (early exit at the first rejection)
+  spec_verify_sample_filtered                             (top-k / top-p filtered p and q)
 """
 from __future__ import annotations
 
@@ -25,6 +26,7 @@ __all__ = [
     "LIB_PATH", "SpecVerifyError", "load_library", "spec_verify_sample", "spec_verify_greedy",
     "spec_verify_tree", "spec_verify_sample_ragged", "spec_verify_greedy_ragged",
     "spec_verify_sample_masked", "spec_verify_greedy_masked", "spec_verify_sample_lazy",
+    "spec_verify_sample_filtered",
     "spec_verify_workspace_size", "spec_verify_workspace_init",
     "spec_verify_status_string", "SV_OK", "SV_ERR_NULL", "SV_ERR_SHAPE", "SV_ERR_DTYPE",
     "SV_ERR_STRIDE", "SV_ERR_WORKSPACE", "SV_ERR_TREE", "SV_ERR_HIP", "SV_OP_SAMPLE",
@@ -57,6 +59,9 @@ _SIGNATURES = {
                                           _c_i32, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "spec_verify_sample_lazy": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _c_u64, _c_i32, _c_i32,
                                                _c_i32, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "spec_verify_sample_filtered": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _vp, _vp, _c_u64,
+                                                   _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp,
+                                                   _c_size, _vp]),
     "spec_verify_greedy": (ctypes.c_int, [_PSV, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
                                           _vp, _c_size, _vp]),
     "spec_verify_tree": (ctypes.c_int, [_PSV, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
@@ -210,7 +215,23 @@ def spec_verify_sample_lazy(target: torch.Tensor, draft: torch.Tensor | None,
                    offset, want_probs)
 
 
-def _sample(entry, target, draft, draft_tokens, temperature, seeds, offset, want_probs):
+def spec_verify_sample_filtered(target: torch.Tensor, draft: torch.Tensor | None,
+                                draft_tokens: torch.Tensor, temperature: torch.Tensor,
+                                top_k: torch.Tensor | None, top_p: torch.Tensor | None,
+                                seeds: torch.Tensor, offset: int = 0, *, want_probs: bool = True):
+    """Stochastic verification on top-k / top-p filtered p (and q): top_k int32 [B] and
+    top_p float32 [B] device tensors, either may be None. Returns as spec_verify_sample."""
+    B = target.shape[0]
+    if top_k is not None:
+        _check(top_k, "top_k", torch.int32, (B,), target.device)
+    if top_p is not None:
+        _check(top_p, "top_p", torch.float32, (B,), target.device)
+    return _sample("spec_verify_sample_filtered", target, draft, draft_tokens, temperature, seeds,
+                   offset, want_probs, filters=(_ptr(top_k), _ptr(top_p)))
+
+
+def _sample(entry, target, draft, draft_tokens, temperature, seeds, offset, want_probs,
+            filters=None):
     lib = load_library()
     B, R, V = target.shape
     K = R - 1
@@ -231,9 +252,11 @@ def _sample(entry, target, draft, draft_tokens, temperature, seeds, offset, want
     q = torch.empty((B, K), dtype=torch.float32, device=dev) if want_probs else None
     nbytes = spec_verify_workspace_size(SV_OP_SAMPLE, B, K, V, draft is not None)
     ws = _workspace(dev, nbytes)
-    rc = getattr(lib, entry)(ctypes.byref(tdesc), ctypes.byref(ddesc) if ddesc else None,
-                             draft_tokens.data_ptr() if K else None, temperature.data_ptr(),
-                             seeds.data_ptr(), int(offset) & (2**64 - 1), B, K, V,
+    head = [ctypes.byref(tdesc), ctypes.byref(ddesc) if ddesc else None,
+            draft_tokens.data_ptr() if K else None, temperature.data_ptr()]
+    if filters is not None:
+        head += list(filters)
+    rc = getattr(lib, entry)(*head, seeds.data_ptr(), int(offset) & (2**64 - 1), B, K, V,
                              tokens.data_ptr(), alen.data_ptr(), _ptr(p), _ptr(q),
                              ws.data_ptr(), ws.numel(), _stream_ptr(dev))
     if rc:

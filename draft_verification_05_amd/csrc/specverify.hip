@@ -49,7 +49,12 @@ struct Record {
   float u;        // sampling uniform of position a
   float Mp, Sp;   // target row a: max and sum in units of 2^(y - Mp)
   float Mq, Sq;   // draft row a
+  float tp, tq;   // top-k / top-p cuts of the two rows (filtered verification)
 };
+
+// A row's top-k / top-p cut: kept logits l >= thr, weights 2^(l c - mref),
+// s = their sum (without a one-hot draft token).
+struct RowFilter { float mref, thr, s, pad; };
 
 struct Args {
   const char* tgt; int64_t t_sb, t_sk;     // byte strides
@@ -81,6 +86,11 @@ struct Args {
   Record* rec;          // [B]
   float* res_part;      // [B * n_chunk]
   float2* unif;         // [B * R]: (u_accept, u_sample) of each position
+  int filtered;         // 1: top-k / top-p filtered verification
+  const int32_t* top_k; // [B] or null (no top-k)
+  const float* top_p;   // [B] or null (no top-p)
+  RowFilter* rf;        // [B * rows]
+  float* fpart;         // [B * rows * n_chunk]: kept weight per chunk
   int n_nodes;
   int8_t parent[SV_MAX_TREE_NODES];
   int8_t depth[SV_MAX_TREE_NODES];   // depth of each node (root 0)
@@ -308,10 +318,11 @@ __device__ __forceinline__ uint32_t lane_mask_bits(const uint32_t* mrow, int64_t
 // Draw from one row's softmax weights 2^(y - M) (optionally without token
 // `xe`) using that row's row-pass partials; used for the one-hot residual
 // and the bonus token. Returns -1 when the weights have no mass.
-// part_of(s) returns the row's chunk partial s.
-template <int DT, bool kVec, bool kMask, class PartOf>
+// part_of(s) returns the row's chunk partial s. kThr: logits below thr
+// weigh nothing (a top-k / top-p cut).
+template <int DT, bool kVec, bool kMask, bool kThr, class PartOf>
 __device__ int draw_from_partials(const Args& A, int b, const Req& rq, int r, float c, float M, int xe,
-                                  float u, PartOf part_of) {
+                                  float u, float thr, PartOf part_of) {
   constexpr int E = Chunk<DT>::kElems / 64;
   auto W = [&](int s) {
     const float2 v = part_of(s);
@@ -329,7 +340,7 @@ __device__ int draw_from_partials(const Args& A, int b, const Req& rq, int r, fl
 #pragma unroll
   for (int k = 0; k < E; ++k) {
     const float v = fast_exp2(fmaf(x[k], c, -M));
-    w[k] = (e0 + k == xe || !((allow >> k) & 1u)) ? 0.f : v;
+    w[k] = (e0 + k == xe || !((allow >> k) & 1u) || (kThr && !(x[k] >= thr))) ? 0.f : v;
   }
   return wave_pick<E>(w, c0, t_in);
 }
@@ -337,8 +348,8 @@ __device__ int draw_from_partials(const Args& A, int b, const Req& rq, int r, fl
 template <int DT, bool kVec, bool kMask>
 __device__ int draw_softmax_row(const Args& A, int b, const Req& rq, int r, float c, float M, int xe,
                                 float u, const TailLds& S, bool cached) {
-  return draw_from_partials<DT, kVec, kMask>(A, b, rq, r, c, M, xe, u,
-                                              [&](int s) { return partial(A, b, r, s, S, cached); });
+  return draw_from_partials<DT, kVec, kMask, false>(A, b, rq, r, c, M, xe, u, kNegInf,
+                                                     [&](int s) { return partial(A, b, r, s, S, cached); });
 }
 
 // Copying a request's partials to LDS when they fit: stage_issue starts the
@@ -729,12 +740,12 @@ __device__ void round_decide(const Args& A, int b) {
       A.alive[b] = 0;
     }
     if (MODE == kExplicit) return;
-    y = draw_from_partials<DT, kVec, false>(A, b, rq, i, c, Mx, x, un.y, [&](int s) {
+    y = draw_from_partials<DT, kVec, false, false>(A, b, rq, i, c, Mx, x, un.y, kNegInf, [&](int s) {
       return fetch(A.part + (rowg0 + i) * A.n_chunk + s);
     });
     if (y < 0) y = valid ? x : 0;                  // residual without mass: p's mode
   } else {                                         // all K accepted: the bonus token from p_K
-    y = draw_from_partials<DT, kVec, false>(A, b, rq, K, c, mp.x, -1, un.y, [&](int s) {
+    y = draw_from_partials<DT, kVec, false, false>(A, b, rq, K, c, mp.x, -1, un.y, kNegInf, [&](int s) {
       return fetch(A.part + (rowg0 + K) * A.n_chunk + s);
     });
     if (y < 0) y = 0;
@@ -1065,10 +1076,415 @@ __global__ __launch_bounds__(64) void sv_tail_kernel(Args A) {
   }
 }
 
+// ------------------------------------------------- top-k / top-p filters ---
+// The sampler's filters, applied to p and, with draft logits, to q (the
+// sampling parameters used with speculation in "Speculative Decoding
+// Guide", vLLM-Ascend): top-k keeps the logits at least the k-th largest;
+// top-p then keeps the largest cut whose upper set holds top_p of the
+// remaining mass; ties at a cut are kept. One workgroup per row finds each
+// cut as a logit value by descent over histograms of the log2 weight
+//   D = l * log2(e) / T - Mref   (fp64; Mref = the row's largest l * log2(e) / T)
+// in 256 buckets of width 1/4 over [0, 64), refined 256-fold per level (at
+// most three levels) until the bucket holding the cut has at most kSelCap
+// logits. Those are sorted by value and scanned exactly. A cut more than
+// 64 below the largest log2 weight keeps the whole row (the weights it
+// would drop are below 2^-64 of the largest).
+
+constexpr int kSelBuckets = 256;
+constexpr int kSelCap = 2048;
+constexpr int kSelLevels = 3;
+
+struct SelLds {
+  unsigned cnt[kWaves][kSelBuckets];
+  double mass[kWaves][kSelBuckets];
+  uint32_t key[kSelCap];
+  double w[kSelCap];
+  double scan[kThreads];
+  double tab[64];                                  // 2^(j / 64)
+  float wsum[kWaves];
+  int n, sel;
+  uint32_t kfloor;
+};
+
+// Total order of logit values as unsigned keys (-0 sorts with +0).
+__device__ __forceinline__ uint32_t order_key(float l) {
+  uint32_t u = __float_as_uint(l);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// 2^D in fp64 (relative error ~1e-15): 2^n * 2^(j/64) (table) * e^r with
+// r = (f - j/64) ln 2 in [0, ln2/64) by its Taylor series to r^5.
+__device__ __forceinline__ double exp2_weight(double D, const double* tab) {
+  if (!(D > -1000.0)) return 0.0;
+  const double n = floor(D), f = D - n;
+  const int j = min((int)(f * 64.0), 63);
+  const double r = (f - j * (1.0 / 64.0)) * 0.69314718055994530942;
+  double e = 1.0 / 120.0;
+  e = fma(e, r, 1.0 / 24.0);
+  e = fma(e, r, 1.0 / 6.0);
+  e = fma(e, r, 0.5);
+  e = fma(e, r, 1.0);
+  e = fma(e, r, 1.0);
+  return ldexp(tab[j] * e, (int)n);
+}
+
+// Bucket of a logit at `level` inside bucket `parent` (its global index at
+// level - 1), or -1 outside it. Non-increasing in the logit.
+__device__ __forceinline__ int sel_bucket(double D, int level, int64_t parent) {
+  if (level == 0) {
+    const double t = -4.0 * D;
+    if (!(t < 255.0)) return kSelBuckets - 1;      // also -inf logits and NaN
+    return t > 0.0 ? (int)t : 0;
+  }
+  const double scale = level == 1 ? 1024.0 : 262144.0;
+  const double lo = (double)parent * kSelBuckets;
+  const double t = fmax(-D, 0.0) * scale;
+  if (!(t >= lo && t < lo + kSelBuckets)) return -1;
+  return (int)(t - lo);
+}
+
+// Inclusive scan of one value per thread; buf keeps the result.
+__device__ double block_scan(double v, double* buf) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const double t = tid >= off ? buf[tid - off] : 0.0;
+    __syncthreads();
+    buf[tid] += t;
+    __syncthreads();
+  }
+  return buf[tid];
+}
+
+// Every logit of a row once (f(l, index)), four chunks in flight.
+template <int DT, bool kVec, class F>
+__device__ void for_each_logit(const char* row, int n_chunk, int V, F f) {
+  constexpr int kCE = Chunk<DT>::kElems, kPT = Chunk<DT>::kPerThread, kU = 2;
+  for (int ch = 0; ch < n_chunk; ch += kU) {
+    float x[kU][kPT];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (ch + u < n_chunk) {
+        load_chunk_wg<DT, kVec>(row, (int64_t)(ch + u) * kCE, V, x[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kPT; ++k) x[u][k] = kNegInf;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int k = 0; k < kPT; ++k) {
+        const int64_t e = (int64_t)(ch + u) * kCE + (int64_t)threadIdx.x * kPT + k;
+        if (ch + u < n_chunk && e < V) f(x[u][k], e);
+      }
+  }
+}
+
+// Descending bitonic sort of the first n collected entries (padded to a
+// power of two with key 0, below every logit's key).
+__device__ void sort_collected(SelLds& L, int n) {
+  int np = 2;
+  while (np < n) np <<= 1;
+  for (int i = n + threadIdx.x; i < np; i += kThreads) {
+    L.key[i] = 0u;
+    L.w[i] = 0.0;
+  }
+  __syncthreads();
+  for (int size = 2; size <= np; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (np >> 1); i += kThreads) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint32_t a = L.key[lo], c = L.key[hi];
+        if (desc ? (a < c) : (a > c)) {
+          L.key[lo] = c;
+          L.key[hi] = a;
+          const double t = L.w[lo];
+          L.w[lo] = L.w[hi];
+          L.w[hi] = t;
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// The cut for one criterion among the logits with key >= kfloor: the
+// largest logit value t whose upper set holds at least `want` logits
+// (by_mass false) or `want` of their mass (by_mass true). Returns the key
+// of t, or 0 to keep them all.
+template <int DT, bool kVec>
+__device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, double cd, float mref,
+                               bool by_mass, double want, uint32_t kfloor) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int64_t parent = 0;
+  double above = 0.0, target = want;
+  int level = 0, sel = 0;
+  for (; level < kSelLevels; ++level) {
+    for (int i = tid; i < kWaves * kSelBuckets; i += kThreads) {
+      (&L.cnt[0][0])[i] = 0u;
+      (&L.mass[0][0])[i] = 0.0;
+    }
+    __syncthreads();
+    for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+      if (order_key(l) < kfloor) return;
+      const double D = (double)l * cd - (double)mref;
+      const int bk = sel_bucket(D, level, parent);
+      if (bk < 0) return;
+      atomicAdd(&L.cnt[wave][bk], 1u);
+      if (by_mass) atomicAdd(&L.mass[wave][bk], exp2_weight(D, L.tab));
+    });
+    __syncthreads();
+    unsigned n_t = 0;
+    double m_t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      n_t += L.cnt[w][tid];
+      m_t += L.mass[w][tid];
+    }
+    const double incl = block_scan(by_mass ? m_t : (double)n_t, L.scan);
+    if (level == 0 && by_mass) target = want * L.scan[kThreads - 1];
+    const double prev = tid ? L.scan[tid - 1] : 0.0;
+    if (tid == 0) L.sel = -1;
+    __syncthreads();
+    if (above + incl >= target && !(tid > 0 && above + prev >= target)) L.sel = tid;
+    __syncthreads();
+    sel = L.sel;
+    if (sel < 0 || (level == 0 && sel == kSelBuckets - 1)) return 0u;   // keep all
+    above += sel ? L.scan[sel - 1] : 0.0;
+    unsigned n_sel = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) n_sel += L.cnt[w][sel];
+    __syncthreads();
+    if (n_sel <= (unsigned)kSelCap) break;
+    if (level + 1 < kSelLevels) parent = (level == 0) ? sel : parent * kSelBuckets + sel;
+  }
+  if (level == kSelLevels) {
+    // more than kSelCap logits within 2^-18 / 4 of one log2 weight: keep
+    // that whole bucket (its smallest key)
+    if (tid == 0) L.kfloor = 0xFFFFFFFFu;
+    __syncthreads();
+    for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+      const uint32_t k = order_key(l);
+      if (k < kfloor) return;
+      const double D = (double)l * cd - (double)mref;
+      if (sel_bucket(D, kSelLevels - 1, parent) == sel) atomicMin(&L.kfloor, k);
+    });
+    __syncthreads();
+    const uint32_t k = L.kfloor;
+    __syncthreads();
+    return k;
+  }
+  // collect the bucket, sort it, scan it
+  if (tid == 0) L.n = 0;
+  __syncthreads();
+  for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+    const uint32_t k = order_key(l);
+    if (k < kfloor) return;
+    const double D = (double)l * cd - (double)mref;
+    if (sel_bucket(D, level, parent) != sel) return;
+    const int slot = atomicAdd(&L.n, 1);
+    if (slot < kSelCap) {
+      L.key[slot] = k;
+      L.w[slot] = by_mass ? exp2_weight(D, L.tab) : 1.0;
+    }
+  });
+  __syncthreads();
+  const int n = min(L.n, kSelCap);
+  sort_collected(L, n);
+  constexpr int kPer = kSelCap / kThreads;
+  double loc = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid * kPer + j;
+    loc += e < n ? L.w[e] : 0.0;
+  }
+  const double incl = block_scan(loc, L.scan);
+  if (tid == 0) L.sel = INT_MAX;
+  __syncthreads();
+  double run = above + incl - loc;
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid * kPer + j;
+    if (e >= n) break;
+    run += L.w[e];
+    if (run >= target) {
+      atomicMin(&L.sel, e);
+      break;
+    }
+  }
+  __syncthreads();
+  const int at = L.sel == INT_MAX ? n - 1 : L.sel;   // rounding short of the target: whole bucket
+  const uint32_t k = n > 0 ? L.key[at] : 0u;
+  __syncthreads();
+  return k;
+}
+
+// Per row: the cut (top-k, then top-p), and the fp32 chunk sums of the kept
+// weights 2^(l c - Mref) for the draw (without the draft token on one-hot
+// rows, as in the row pass), and their total.
+template <int MODE, int DT, bool kVec>
+__global__ __launch_bounds__(kThreads) void sv_select_kernel(Args A) {
+  __shared__ SelLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rowg = blockIdx.x;
+  const int b = rowg / A.rows, r = rowg % A.rows;
+  const Req rq = request(A, b);
+  const char* row = row_ptr(A, rq, r);
+  float* fp = A.fpart + (int64_t)rowg * A.n_chunk;
+  const float T = A.temperature[b];
+  // the row's largest scaled logit, from the row pass (which leaves a
+  // one-hot draft token out of its sums)
+  float m = kNegInf;
+  for (int w = tid; w < A.wpr; w += kThreads) m = fmaxf(m, A.wpart[(int64_t)rowg * A.wpr + w].x);
+  m = wave_max_all(m);
+  if (lane == 0) L.wsum[wave] = m;
+  if (tid < 64) L.tab[tid] = exp2((double)tid / 64.0);
+  __syncthreads();
+  float mref = fmaxf(fmaxf(L.wsum[0], L.wsum[1]), fmaxf(L.wsum[2], L.wsum[3]));
+  const float c = kLog2e / T;
+  int xe = -1;
+  if (MODE == kOneHot && r < A.K) {
+    xe = A.tokens[(int64_t)b * A.K + r];
+    if ((unsigned)xe < (unsigned)A.V) mref = fmaxf(mref, A.gath[rowg] * c);
+    else xe = -1;
+  }
+  __syncthreads();
+  if (!(T > 0.f && T < __builtin_inff()) || mref == kNegInf || mref != mref) {
+    for (int ch = tid; ch < A.n_chunk; ch += kThreads) fp[ch] = 0.f;
+    if (tid == 0) A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
+    return;
+  }
+  const double cd = 1.4426950408889634 / (double)T;
+  const int tk = A.top_k ? A.top_k[b] : 0;
+  const float tp = A.top_p ? A.top_p[b] : 1.f;
+  uint32_t cut = 0u;
+  if (tk > 0 && tk < A.V)
+    cut = select_cut<DT, kVec>(row, A.n_chunk, A.V, L, cd, mref, false, (double)tk, 0u);
+  if (tp < 1.f) {
+    const uint32_t cp = select_cut<DT, kVec>(row, A.n_chunk, A.V, L, cd, mref, true, (double)tp, cut);
+    if (cp) cut = cp;
+  }
+  const float thr = cut ? key_value(cut) : kNegInf;
+  // chunk sums of the kept weights, one wave per chunk, in the draw's layout
+  constexpr int E = Chunk<DT>::kElems / 64;
+  float tot = 0.f;
+  for (int ch = wave; ch < A.n_chunk; ch += kWaves) {
+    const int64_t c0 = (int64_t)ch * Chunk<DT>::kElems;
+    float x[E];
+    load_lane_run<DT, kVec, E>(row, c0, A.V, x);
+    const int64_t e0 = c0 + (int64_t)lane * E;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < E; ++k)
+      s += (x[k] >= thr && e0 + k != xe) ? fast_exp2(fmaf(x[k], c, -mref)) : 0.f;
+    s = wave_sum_all(s);
+    if (lane == 0) fp[ch] = s;
+    tot += s;
+  }
+  if (lane == 0) L.wsum[wave] = tot;
+  __syncthreads();
+  if (tid == 0)
+    A.rf[rowg] = RowFilter{mref, thr, (L.wsum[0] + L.wsum[1]) + (L.wsum[2] + L.wsum[3]), 0.f};
+}
+
+// The rule on filtered rows, one wave per request: p_i(x_i) = w(x_i) / S'_i
+// with the kept weights and sums of the select pass.
+template <int DT, bool kVec, int MODE>
+__device__ void filtered_tail(const Args& A, int b) {
+  const int lane = threadIdx.x & 63;
+  const Req rq = request(A, b);
+  const int K = A.K, V = A.V, R = A.R;
+  const int64_t rowg0 = (int64_t)b * A.rows;
+  int x = -1;
+  float lx = kNegInf, ld = kNegInf;
+  if (lane < K) {
+    x = A.tokens[(int64_t)b * K + lane];
+    lx = A.gath[rowg0 + lane];
+    if (MODE == kExplicit) ld = A.gath[rowg0 + R + lane];
+  }
+  RowFilter fpr = RowFilter{kNegInf, kNegInf, 0.f, 0.f}, fqr = fpr;
+  if (lane <= K) fpr = A.rf[rowg0 + lane];
+  if (MODE == kExplicit && lane < K) fqr = A.rf[rowg0 + R + lane];
+  const float T = A.temperature[b];
+  float2 un = make_float2(0.f, 0.f);
+  if (lane <= K) un = A.unif[(int64_t)b * R + lane];
+  int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
+  if (!(T > 0.f && T < __builtin_inff())) {        // refused request
+    if (lane <= K) otok[lane] = -1;
+    if (lane < K && A.out_p) A.out_p[(int64_t)b * K + lane] = 0.f;
+    if (lane < K && A.out_q) A.out_q[(int64_t)b * K + lane] = 0.f;
+    if (lane == 0) {
+      A.out_len[b] = 0;
+      if (MODE == kExplicit) A.rec[b].pending = 0;
+    }
+    return;
+  }
+  const float c = kLog2e / T;
+  float p = 0.f, q = 0.f, lp = kNegInf, lq = kNegInf;
+  if (lane < K) {
+    const bool valid = (unsigned)x < (unsigned)V;
+    const bool kept = valid && lx >= fpr.thr && fpr.mref != kNegInf;
+    if (MODE == kOneHot) {
+      const float e = kept ? fast_exp2(fmaf(lx, c, -fpr.mref)) : 0.f;
+      const float St = fpr.s + e;                 // the sums leave x out
+      p = St > 0.f ? e / St : 0.f;
+      q = valid ? 1.f : 0.f;
+    } else {
+      const bool keptq = valid && ld >= fqr.thr && fqr.mref != kNegInf;
+      const float dp = fmaf(lx, c, -fpr.mref), dq = fmaf(ld, c, -fqr.mref);
+      const bool okp = kept && fpr.s > 0.f, okq = keptq && fqr.s > 0.f;
+      p = okp ? fast_exp2(dp) / fpr.s : 0.f;
+      q = okq ? fast_exp2(dq) / fqr.s : 0.f;
+      lp = okp ? dp - __log2f(fpr.s) : kNegInf;
+      lq = okq ? dq - __log2f(fqr.s) : kNegInf;
+    }
+    if (A.out_p) A.out_p[(int64_t)b * K + lane] = p;
+    if (A.out_q) A.out_q[(int64_t)b * K + lane] = q;
+  }
+  const bool accept = MODE == kOneHot ? (un.x * q < p) : (__log2f(un.x) + lq < lp);
+  const int rej = first_lane(lane < K && !accept);
+  const int a = rej < 0 ? K : rej;
+  if (lane <= K && lane != a) otok[lane] = lane < a ? x : -1;
+  if (lane == 0) A.out_len[b] = a + 1;
+  const float ua = lane_f(un.y, a);
+  const float Ma = lane_f(fpr.mref, a), ta = lane_f(fpr.thr, a);
+  if (MODE == kExplicit) {
+    if (a < K) {
+      if (lane == 0) {
+        Record rc;
+        rc.a = a; rc.pending = 1; rc.c = c; rc.u = ua;
+        rc.Mp = Ma; rc.Sp = lane_f(fpr.s, a); rc.Mq = lane_f(fqr.mref, a); rc.Sq = lane_f(fqr.s, a);
+        rc.tp = ta; rc.tq = lane_f(fqr.thr, a);
+        A.rec[b] = rc;
+      }
+      return;
+    }
+    if (lane == 0) A.rec[b].pending = 0;
+  }
+  const int xe = (MODE == kOneHot && a < K) ? lane_i(x, a) : -1;
+  const float* fpa = A.fpart + (rowg0 + a) * A.n_chunk;
+  int y = draw_from_partials<DT, kVec, false, true>(A, b, rq, a, c, Ma, xe, ua, ta,
+                                                    [&](int s) { return make_float2(Ma, fpa[s]); });
+  if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
+  if (lane == 0) otok[a] = y;
+}
+
+template <int MODE, int DT, bool kVec>
+__global__ __launch_bounds__(64) void sv_ftail_kernel(Args A) {
+  filtered_tail<DT, kVec, MODE>(A, blockIdx.x);
+}
+
 // ------------------------------------------------------ residual pass ---
 // Explicit draft logits: for requests that stopped at a < K, chunk sums of
 // max(0, p_a - q_a); the last workgroup of the request draws the token.
-template <int DT, bool kVec, bool kMask>
+// kFilt: p_a and q_a are the top-k / top-p filtered rows (weights below a
+// row's cut count as zero).
+template <int DT, bool kVec, bool kMask, bool kFilt>
 __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   constexpr int kCE = Chunk<DT>::kElems;
   __shared__ TailLds S;
@@ -1110,9 +1526,15 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
 #pragma unroll
     for (int j = 0; j < kLoadsPerLane; ++j)
 #pragma unroll
-      for (int k = 0; k < kPer; ++k)
-        s += fmaxf(fast_exp2(fmaf(raw_elem<DT>(rp, j, k), c, -rc.Mp)) * ip -
-                   fast_exp2(fmaf(raw_elem<DT>(rq, j, k), c, -rc.Mq)) * iq, 0.f);
+      for (int k = 0; k < kPer; ++k) {
+        const float yp = raw_elem<DT>(rp, j, k), yq = raw_elem<DT>(rq, j, k);
+        float wp = fast_exp2(fmaf(yp, c, -rc.Mp)) * ip, wq = fast_exp2(fmaf(yq, c, -rc.Mq)) * iq;
+        if constexpr (kFilt) {
+          wp = yp >= rc.tp ? wp : 0.f;
+          wq = yq >= rc.tq ? wq : 0.f;
+        }
+        s += fmaxf(wp - wq, 0.f);
+      }
     s = wave_sum_all(s);
     if (lane == 0) publish(A.res_part + (int64_t)b * A.n_chunk + ch, s);
   }
@@ -1133,15 +1555,25 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
     load_lane_run<DT, kVec, E>(rowq, c0, A.V, xq);
     const uint32_t allow = kMask ? lane_mask_bits<E>(mrow, c0, A.mask_words) : ~0u;
 #pragma unroll
-    for (int k = 0; k < E; ++k)
-      w[k] = ((allow >> k) & 1u)
-                 ? fmaxf(fast_exp2(fmaf(xp[k], c, -rc.Mp)) * ip - fast_exp2(fmaf(xq[k], c, -rc.Mq)) * iq, 0.f)
-                 : 0.f;
+    for (int k = 0; k < E; ++k) {
+      float wp = fast_exp2(fmaf(xp[k], c, -rc.Mp)) * ip, wq = fast_exp2(fmaf(xq[k], c, -rc.Mq)) * iq;
+      if constexpr (kFilt) {
+        wp = xp[k] >= rc.tp ? wp : 0.f;
+        wq = xq[k] >= rc.tq ? wq : 0.f;
+      }
+      w[k] = ((allow >> k) & 1u) ? fmaxf(wp - wq, 0.f) : 0.f;
+    }
     y = wave_pick<E>(w, c0, t_in);
   }
   if (y < 0) {
     // p_a and q_a agree everywhere: draw from p_a with the row pass's partials
-    y = draw_softmax_row<DT, kVec, kMask>(A, b, req, a, c, rc.Mp, -1, rc.u, S, false);
+    if constexpr (kFilt) {
+      const float* fpa = A.fpart + ((int64_t)b * A.rows + a) * A.n_chunk;
+      y = draw_from_partials<DT, kVec, false, true>(A, b, req, a, c, rc.Mp, -1, rc.u, rc.tp,
+                                                    [&](int s) { return make_float2(rc.Mp, fpa[s]); });
+    } else {
+      y = draw_softmax_row<DT, kVec, kMask>(A, b, req, a, c, rc.Mp, -1, rc.u, S, false);
+    }
     if (y < 0) y = 0;
   }
   if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + a] = y;
@@ -1170,12 +1602,12 @@ using namespace sv;
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t part, wpart, gath, rec, res, unif, alive, total;
+  size_t part, wpart, gath, rec, res, unif, alive, rf, fpart, total;
 };
 
 // Workspace: [counters: 4 * SV_MAX_BATCH][chunk partials][workgroup
 //            partials][gathered logits][records][residual partials]
-//            [uniforms][alive flags]
+//            [uniforms][alive flags][row cuts][kept weight per chunk]
 Layout layout(int64_t B, int64_t rows, int64_t V) {
   const int64_t ce = Chunk<kF32>::kElems;          // the smaller chunk: a bound for both dtypes
   const int64_t nch = (V + ce - 1) / ce;
@@ -1187,7 +1619,9 @@ Layout layout(int64_t B, int64_t rows, int64_t V) {
   L.res = align_up(L.rec + (size_t)B * sizeof(Record), 256);
   L.unif = align_up(L.res + (size_t)(B * nch) * sizeof(float), 256);
   L.alive = align_up(L.unif + (size_t)(B * rows) * sizeof(float2), 256);   // R <= rows
-  L.total = align_up(L.alive + (size_t)B * sizeof(int), 256);
+  L.rf = align_up(L.alive + (size_t)B * sizeof(int), 256);
+  L.fpart = align_up(L.rf + (size_t)(B * rows) * sizeof(RowFilter), 256);
+  L.total = align_up(L.fpart + (size_t)(B * rows * nch) * sizeof(float), 256);
   return L;
 }
 
@@ -1249,6 +1683,11 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.res_part = reinterpret_cast<float*>(base + L.res);
   A.unif = reinterpret_cast<float2*>(base + L.unif);
   A.alive = reinterpret_cast<int*>(base + L.alive);
+  A.rf = reinterpret_cast<RowFilter*>(base + L.rf);
+  A.fpart = reinterpret_cast<float*>(base + L.fpart);
+  A.filtered = 0;
+  A.top_k = nullptr;
+  A.top_p = nullptr;
   A.out_p = nullptr; A.out_q = nullptr; A.out_aux = nullptr;
   A.temperature = nullptr; A.seeds = nullptr; A.offset = 0;
   A.n_nodes = 0;
@@ -1291,14 +1730,38 @@ void launch_rows(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t 
 
 template <int DT>
 void launch_residual_dt(const Args& A, bool vec, unsigned grid, hipStream_t st) {
-  const bool mask = A.mask != nullptr;
+  const bool mask = A.mask != nullptr, filt = A.filtered != 0;
   if (vec) {
-    if (mask) SV_LAUNCH((sv_residual_kernel<DT, true, true>), grid, st, A);
-    else      SV_LAUNCH((sv_residual_kernel<DT, true, false>), grid, st, A);
+    if (filt)      SV_LAUNCH((sv_residual_kernel<DT, true, false, true>), grid, st, A);
+    else if (mask) SV_LAUNCH((sv_residual_kernel<DT, true, true, false>), grid, st, A);
+    else           SV_LAUNCH((sv_residual_kernel<DT, true, false, false>), grid, st, A);
   } else {
-    if (mask) SV_LAUNCH((sv_residual_kernel<DT, false, true>), grid, st, A);
-    else      SV_LAUNCH((sv_residual_kernel<DT, false, false>), grid, st, A);
+    if (filt)      SV_LAUNCH((sv_residual_kernel<DT, false, false, true>), grid, st, A);
+    else if (mask) SV_LAUNCH((sv_residual_kernel<DT, false, true, false>), grid, st, A);
+    else           SV_LAUNCH((sv_residual_kernel<DT, false, false, false>), grid, st, A);
   }
+}
+
+// Filtered verification: the row pass, the select pass (one workgroup per
+// row), then the filtered rule (one wave per request).
+template <int MODE, int DT>
+void launch_filtered_dt(const Args& A, bool vec, unsigned grid, hipStream_t st) {
+  const dim3 rows((unsigned)((int64_t)A.B * A.rows)), reqs((unsigned)A.B), wave(64), wg(kThreads);
+  if (vec) {
+    SV_LAUNCH((sv_rows_kernel<MODE, DT, true, false, false>), grid, st, A);
+    hipLaunchKernelGGL((sv_select_kernel<MODE, DT, true>), rows, wg, 0, st, A);
+    hipLaunchKernelGGL((sv_ftail_kernel<MODE, DT, true>), reqs, wave, 0, st, A);
+  } else {
+    SV_LAUNCH((sv_rows_kernel<MODE, DT, false, false, false>), grid, st, A);
+    hipLaunchKernelGGL((sv_select_kernel<MODE, DT, false>), rows, wg, 0, st, A);
+    hipLaunchKernelGGL((sv_ftail_kernel<MODE, DT, false>), reqs, wave, 0, st, A);
+  }
+}
+
+template <int MODE>
+void launch_filtered(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
+  if (dtype == SV_DTYPE_BF16) launch_filtered_dt<MODE, kBF16>(A, vec, grid, st);
+  else                        launch_filtered_dt<MODE, kF32>(A, vec, grid, st);
 }
 
 void launch_residual(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
@@ -1329,7 +1792,8 @@ int hip_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; 
 // Sampling, dense (cu null: [B, K + 1] rows by the two strides) or ragged
 // (cu [B + 1] device prefix sums, packed rows by stride_k, stride_b unused).
 int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* cu, int32_t total_k,
-                const uint32_t* mask, bool lazy, const int32_t* draft_tokens, const float* temperature,
+                const uint32_t* mask, bool lazy, const int32_t* top_k, const float* top_p,
+                bool filtered, const int32_t* draft_tokens, const float* temperature,
                 const uint64_t* seeds, uint64_t offset,
                 int32_t B, int32_t K, int32_t V,
                 int32_t* out_tokens, int32_t* out_accept_len,
@@ -1371,6 +1835,23 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
   A.out_q = out_q_draft;
   const bool vec = aligned16(target) && (!explicit_q || aligned16(draft));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (filtered) {
+    A.filtered = 1;
+    A.top_k = top_k;
+    A.top_p = top_p;
+    const int64_t wgs = (int64_t)B * rows * A.wpr;
+    if ((st = check_grid(wgs))) return st;
+    if (explicit_q) launch_filtered<kExplicit>(A, target->dtype, vec, (unsigned)wgs, s);
+    else            launch_filtered<kOneHot>(A, target->dtype, vec, (unsigned)wgs, s);
+    if ((st = hip_status())) return st;
+    if (explicit_q) {
+      Args A2 = A;
+      A2.cpw = chunks_per_wg(B, A.n_chunk);
+      A2.wpr = (A.n_chunk + A2.cpw - 1) / A2.cpw;
+      launch_residual(A2, target->dtype, vec, (unsigned)((int64_t)B * A2.wpr), s);
+    }
+    return hip_status();
+  }
   if (lazy) {                                      // early-exit rounds, one position at a time
     for (int i = 0; i <= K; ++i) {
       Args Ai = A;
@@ -1481,9 +1962,9 @@ int spec_verify_sample(const sv_logits* target, const sv_logits* draft,
                        int32_t* out_tokens, int32_t* out_accept_len,
                        float* out_p_draft, float* out_q_draft,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return sample_impl(target, draft, nullptr, 0, nullptr, false, draft_tokens, temperature, seeds,
-                     offset, B, K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft,
-                     workspace, workspace_bytes, stream);
+  return sample_impl(target, draft, nullptr, 0, nullptr, false, nullptr, nullptr, false, draft_tokens,
+                     temperature, seeds, offset, B, K, V, out_tokens, out_accept_len, out_p_draft,
+                     out_q_draft, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_sample_lazy(const sv_logits* target, const sv_logits* draft,
@@ -1493,9 +1974,22 @@ int spec_verify_sample_lazy(const sv_logits* target, const sv_logits* draft,
                             int32_t* out_tokens, int32_t* out_accept_len,
                             float* out_p_draft, float* out_q_draft,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  return sample_impl(target, draft, nullptr, 0, nullptr, true, draft_tokens, temperature, seeds,
-                     offset, B, K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft,
-                     workspace, workspace_bytes, stream);
+  return sample_impl(target, draft, nullptr, 0, nullptr, true, nullptr, nullptr, false, draft_tokens,
+                     temperature, seeds, offset, B, K, V, out_tokens, out_accept_len, out_p_draft,
+                     out_q_draft, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_sample_filtered(const sv_logits* target, const sv_logits* draft,
+                                const int32_t* draft_tokens, const float* temperature,
+                                const int32_t* top_k, const float* top_p,
+                                const uint64_t* seeds, uint64_t offset,
+                                int32_t B, int32_t K, int32_t V,
+                                int32_t* out_tokens, int32_t* out_accept_len,
+                                float* out_p_draft, float* out_q_draft,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return sample_impl(target, draft, nullptr, 0, nullptr, false, top_k, top_p, true, draft_tokens,
+                     temperature, seeds, offset, B, K, V, out_tokens, out_accept_len, out_p_draft,
+                     out_q_draft, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_sample_masked(const sv_logits* target, const sv_logits* draft,
@@ -1506,9 +2000,9 @@ int spec_verify_sample_masked(const sv_logits* target, const sv_logits* draft,
                               float* out_p_draft, float* out_q_draft,
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (!bitmask) return SV_ERR_NULL;
-  return sample_impl(target, draft, nullptr, 0, bitmask, false, draft_tokens, temperature, seeds,
-                     offset, B, K, V, out_tokens, out_accept_len, out_p_draft, out_q_draft,
-                     workspace, workspace_bytes, stream);
+  return sample_impl(target, draft, nullptr, 0, bitmask, false, nullptr, nullptr, false, draft_tokens,
+                     temperature, seeds, offset, B, K, V, out_tokens, out_accept_len, out_p_draft,
+                     out_q_draft, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_sample_ragged(const sv_logits* target, const sv_logits* draft,
@@ -1524,9 +2018,9 @@ int spec_verify_sample_ragged(const sv_logits* target, const sv_logits* draft,
   sv_logits t = *target, d = draft ? *draft : sv_logits{};
   t.stride_b = 0;                                   // packed rows: stride_k only
   d.stride_b = 0;
-  return sample_impl(&t, draft ? &d : nullptr, cu_draft, total_k, nullptr, false, draft_tokens, temperature,
-                     seeds, offset, B, K_max, V, out_tokens, out_accept_len, out_p_draft,
-                     out_q_draft, workspace, workspace_bytes, stream);
+  return sample_impl(&t, draft ? &d : nullptr, cu_draft, total_k, nullptr, false, nullptr, nullptr,
+                     false, draft_tokens, temperature, seeds, offset, B, K_max, V, out_tokens,
+                     out_accept_len, out_p_draft, out_q_draft, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,

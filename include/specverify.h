@@ -152,6 +152,34 @@ int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Top-k / top-p filtered stochastic verification. The pages run speculative
+ * decoding with the sampler's parameters (temperature 0.8, top_p 0.95, in
+ * "Speculative Decoding Guide", vLLM-Ascend), so p and q are the filtered
+ * distributions the sampler draws from: for each target row and, with draft
+ * logits, each draft row, after the temperature:
+ *   top-k: keep the logits at least the k-th largest (ties at the cut kept);
+ *          top_k[b] <= 0 or >= V keeps all;
+ *   top-p: of those, keep the logits at least t, where t is the largest
+ *          logit value whose upper set {l >= t} holds at least top_p[b] of
+ *          their mass (ties kept); top_p[b] >= 1 (or NaN) keeps all;
+ * then renormalise, and run the rule of spec_verify_sample on the filtered
+ * rows. One-hot drafts stay one-hot. top_k and top_p are device arrays [B]
+ * (int32, fp32); either may be NULL (that filter off for every request).
+ * The cut is exact among logits whose weight is within 2^-64 of the row's
+ * largest; a cut below that keeps the whole row. out_p_draft / out_q_draft
+ * hold the filtered p_i(x_i) / q_i(x_i). Other arguments, limits and errors
+ * as spec_verify_sample; the workspace is sized as for it.
+ */
+int spec_verify_sample_filtered(const sv_logits* target, const sv_logits* draft,
+                                const int32_t* draft_tokens, const float* temperature,
+                                const int32_t* top_k, const float* top_p,
+                                const uint64_t* seeds, uint64_t offset,
+                                int32_t B, int32_t K, int32_t V,
+                                int32_t* out_tokens, int32_t* out_accept_len,
+                                float* out_p_draft, float* out_q_draft,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Early-exit ("lazy") stochastic verification. The rule stops at the first
  * rejection ("推测解码与 MTP" §2.1), so the rows after it are never needed:
  * this call reads position by position (round i reads target row i, and

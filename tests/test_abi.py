@@ -191,3 +191,22 @@ def test_lazy_argument_errors(lib):
     need = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, 2, 1, 5)
     assert call(wsb=need - 1) == sv.SV_ERR_WORKSPACE
     assert call(d=desc(dtype=1)) == sv.SV_ERR_DTYPE
+
+
+def test_filtered_argument_errors(lib):
+    s = lib.spec_verify_sample_filtered
+    t = desc()
+
+    def call(t=t, d=None, B=2, K=1, V=5, temp=FAKE, seeds=FAKE, ws=FAKE, wsb=BIG_WS, tk=FAKE, tp=FAKE):
+        return s(ctypes.byref(t) if t is not None else None, ctypes.byref(d) if d is not None else None,
+                 FAKE, temp, tk, tp, seeds, 0, B, K, V, FAKE, FAKE, None, None, ws, wsb, None)
+
+    assert call(t=None) == sv.SV_ERR_NULL
+    assert call(seeds=None) == sv.SV_ERR_NULL
+    assert call(B=0) == sv.SV_ERR_SHAPE
+    assert call(K=33) == sv.SV_ERR_SHAPE
+    assert call(ws=None) == sv.SV_ERR_WORKSPACE
+    need = sv.spec_verify_workspace_size(sv.SV_OP_SAMPLE, 2, 1, 5)
+    assert call(wsb=need - 1) == sv.SV_ERR_WORKSPACE
+    assert call(d=desc(dtype=1)) == sv.SV_ERR_DTYPE
+    assert call(tk=None, tp=None, t=desc(dtype=9)) == sv.SV_ERR_DTYPE   # both filters optional

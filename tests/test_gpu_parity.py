@@ -632,3 +632,115 @@ def test_lazy_agrees_with_dense_and_reuses_workspace():
     assert_report(rep, "lazy vs oracle")
     differ = int(np.sum(np.any(d1[0] != l1[0], axis=1)))
     assert differ <= rep["near_accept"][1e-5] + rep["near_select"][1e-5]
+
+
+# ----------------------------------------------------- top-k / top-p filters ---
+def run_filtered(wl, top_k, top_p, draft_bf16=False):
+    d = to_device(wl, DEV, draft_bf16=draft_bf16)
+    tk = None if top_k is None else torch.from_numpy(np.asarray(top_k, np.int32)).to(DEV)
+    tp = None if top_p is None else torch.from_numpy(np.asarray(top_p, np.float32)).to(DEV)
+    out = sv.spec_verify_sample_filtered(d["target"], d["draft"], d["tokens"], d["temperature"],
+                                         tk, tp, d["seeds"], wl["offset"])
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+def check_filtered(wl, name, top_k, top_p, near_frac=0.25):
+    print(f"[case] filtered {name} B={wl['B']} K={wl['K']} V={wl['V']} dtype={wl['dtype']}", flush=True)
+    g = run_filtered(wl, top_k, top_p)
+    rep = classify_sample(wl, *g, top_k=top_k, top_p=top_p)
+    assert_report(rep, f"filtered {name}")
+    assert rep["filter_near"] <= near_frac * rep["requests"] + 1, rep["filter_near"]
+    return rep
+
+
+def mixed_filters(B, V, seed):
+    rng = np.random.default_rng(seed)
+    top_k = rng.choice([0, 1, 5, 50, 1000, V], size=B).astype(np.int32)
+    top_p = rng.choice([1.0, 0.5, 0.8, 0.9, 0.95], size=B).astype(np.float32)
+    return top_k, top_p
+
+
+FILTER_REDUCED = [
+    ("c3-topp095", "c3_onehot", dict(B=32, V=2 * 8192 + 1232), "p"),
+    ("c3-topk50", "c3_onehot", dict(B=32, V=2 * 8192 + 1232), "k"),
+    ("c3-mixed", "c3_onehot", dict(B=48, V=2 * 8192 + 777), "mixed"),
+    ("c3-K0", "c3_onehot", dict(B=16, K=0, V=5000), "mixed"),
+    ("c2-topp095", "c2_stoch", dict(B=16, V=3 * 8192 + 1234), "p"),
+    ("c2-mixed-scalar-path", "c2_stoch", dict(B=24, V=20001), "mixed"),
+    ("c1", "c1_tiny", {}, "mixed"),
+]
+
+
+@pytest.mark.parametrize("name,cfg,kw,kind", FILTER_REDUCED, ids=[c[0] for c in FILTER_REDUCED])
+def test_filtered_sample(name, cfg, kw, kind):
+    for offset in range(2):
+        wl = make(cfg, data_seed=400 + offset, offset=offset, **kw)
+        B, V = wl["B"], wl["V"]
+        if kind == "p":
+            top_k, top_p = None, np.full(B, 0.95, np.float32)
+        elif kind == "k":
+            top_k, top_p = np.full(B, 50, np.int32), None
+        else:
+            top_k, top_p = mixed_filters(B, V, 410 + offset)
+        check_filtered(wl, f"{name}/off{offset}", top_k, top_p)
+
+
+def test_filtered_off_matches_oracle_unfiltered():
+    """No filter (None, or k = 0 and p = 1): the unfiltered rule."""
+    wl = make("c3_onehot", data_seed=420, B=32, V=9000)
+    for tk, tp in [(None, None), (np.zeros(32, np.int32), np.ones(32, np.float32))]:
+        g = run_filtered(wl, tk, tp)
+        assert_report(classify_sample(wl, *g), "filters off")
+
+
+def test_filtered_ties_and_flat_rows():
+    """All-equal rows (every cut keeps all: more equal logits than one sort holds), a row
+    with a tie at the top-k cut, and top-k = 1 (the largest value only)."""
+    wl = make("c2_stoch", data_seed=421, B=8, K=2, V=3 * 8192 + 5)
+    tgt = wl["target"].copy()
+    drf = wl["draft"].copy()
+    tgt[0] = 1.5
+    drf[0] = -0.25
+    tgt[1, :, :] = np.round(tgt[1], 0)               # few distinct values: wide ties
+    drf[1, :, :] = np.round(drf[1], 0)
+    wl = dict(wl, target=tgt, draft=drf)
+    top_k = np.array([10, 3000, 1, 1, 7, 0, 2, 24581], np.int32)
+    top_p = np.array([0.5, 0.9, 1.0, 0.3, 1.0, 0.95, 0.6, 0.99], np.float32)
+    check_filtered(wl, "ties", top_k, top_p, near_frac=0.5)
+
+
+def test_filtered_bf16_explicit_draft():
+    wl = make("c2_stoch", data_seed=422, B=12, V=8192 + 100)
+    wl = dict(wl, target=f32_to_bf16_bits(wl["target"]), dtype="bf16",
+              draft=f32_to_bf16_bits(wl["draft"]))
+    d = to_device(wl, DEV, draft_bf16=True)
+    top_k, top_p = mixed_filters(12, wl["V"], 423)
+    out = sv.spec_verify_sample_filtered(d["target"], d["draft"], d["tokens"], d["temperature"],
+                                         torch.from_numpy(top_k).to(DEV), torch.from_numpy(top_p).to(DEV),
+                                         d["seeds"], wl["offset"])
+    g = [t.cpu().numpy() for t in out]
+    rep = classify_sample(wl, *g, draft_dtype="bf16", top_k=top_k, top_p=top_p)
+    assert_report(rep, "filtered bf16 explicit")
+
+
+def test_filtered_deterministic():
+    wl = make("c3_onehot", data_seed=424, B=32, V=20000)
+    top_k, top_p = mixed_filters(32, 20000, 425)
+    a = run_filtered(wl, top_k, top_p)
+    b = run_filtered(wl, top_k, top_p)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_filtered_full_size_c3():
+    """C3 at its full size with top_p 0.95 (the pages' sampling setting), sampled requests."""
+    wl = make("c3_onehot", data_seed=1)
+    B = wl["B"]
+    top_p = np.full(B, 0.95, np.float32)
+    print("[case] filtered c3 full", flush=True)
+    g = run_filtered(wl, None, top_p)
+    reqs = list(range(0, B, 8))
+    rep = classify_sample(wl, *g, requests=reqs, top_p=top_p)
+    assert_report(rep, "filtered c3 full (sampled)")
+    assert rep["filter_near"] <= 0.25 * len(reqs) + 1
