@@ -1084,19 +1084,20 @@ __global__ __launch_bounds__(64) void sv_tail_kernel(Args A) {
 // remaining mass; ties at a cut are kept. One workgroup per row finds each
 // cut as a logit value by descent over histograms of the log2 weight
 //   D = l * log2(e) / T - Mref   (fp64; Mref = the row's largest l * log2(e) / T)
-// in 256 buckets of width 1/4 over [0, 64), refined 256-fold per level (at
-// most three levels) until the bucket holding the cut has at most kSelCap
-// logits. Those are sorted by value and scanned exactly. A cut more than
+// in 1024 buckets of width 1/16 over [0, 64), refined 256-fold per level
+// (at most three levels) until the bucket holding the cut has at most
+// kSelCap logits. Those are sorted by value and scanned exactly. A cut more than
 // 64 below the largest log2 weight keeps the whole row (the weights it
 // would drop are below 2^-64 of the largest).
 
-constexpr int kSelBuckets = 256;
+constexpr int kSelBuckets0 = 1024;                // first level: width 1/16 over [0, 64)
+constexpr int kSelBuckets = 256;                  // refinement levels
 constexpr int kSelCap = 2048;
 constexpr int kSelLevels = 3;
 
 struct SelLds {
-  unsigned cnt[kWaves][kSelBuckets];
-  double mass[kWaves][kSelBuckets];
+  unsigned cnt[kSelBuckets0];
+  double mass[kSelBuckets0];
   uint32_t key[kSelCap];
   double w[kSelCap];
   double scan[kThreads];
@@ -1136,20 +1137,22 @@ __device__ __forceinline__ double exp2_weight(double D, const double* tab) {
 // level - 1), or -1 outside it. Non-increasing in the logit.
 __device__ __forceinline__ int sel_bucket(double D, int level, int64_t parent) {
   if (level == 0) {
-    const double t = -4.0 * D;
-    if (!(t < 255.0)) return kSelBuckets - 1;      // also -inf logits and NaN
+    const double t = -16.0 * D;
+    if (!(t < (double)(kSelBuckets0 - 1))) return kSelBuckets0 - 1;   // also -inf and NaN
     return t > 0.0 ? (int)t : 0;
   }
-  const double scale = level == 1 ? 1024.0 : 262144.0;
+  const double scale = level == 1 ? 4096.0 : 1048576.0;
   const double lo = (double)parent * kSelBuckets;
   const double t = fmax(-D, 0.0) * scale;
   if (!(t >= lo && t < lo + kSelBuckets)) return -1;
   return (int)(t - lo);
 }
 
-// Inclusive scan of one value per thread; buf keeps the result.
+// Inclusive scan of one value per thread; buf keeps the result (the total
+// in its last entry) until the next call.
 __device__ double block_scan(double v, double* buf) {
   const int tid = threadIdx.x;
+  __syncthreads();                                 // earlier readers of buf are done
   buf[tid] = v;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {
@@ -1161,7 +1164,8 @@ __device__ double block_scan(double v, double* buf) {
   return buf[tid];
 }
 
-// Every logit of a row once (f(l, index)), four chunks in flight.
+// Every logit of a row once (f(l, index)), two chunks in flight; past the
+// row's end f sees -inf.
 template <int DT, bool kVec, class F>
 __device__ void for_each_logit(const char* row, int n_chunk, int V, F f) {
   constexpr int kCE = Chunk<DT>::kElems, kPT = Chunk<DT>::kPerThread, kU = 2;
@@ -1180,8 +1184,8 @@ __device__ void for_each_logit(const char* row, int n_chunk, int V, F f) {
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int k = 0; k < kPT; ++k) {
-        const int64_t e = (int64_t)(ch + u) * kCE + (int64_t)threadIdx.x * kPT + k;
-        if (ch + u < n_chunk && e < V) f(x[u][k], e);
+        // padding past the row reads as -inf: a weight of zero in the last bucket
+        f(x[u][k], (int64_t)(ch + u) * kCE + (int64_t)threadIdx.x * kPT + k);
       }
   }
 }
@@ -1214,88 +1218,13 @@ __device__ void sort_collected(SelLds& L, int n) {
     }
 }
 
-// The cut for one criterion among the logits with key >= kfloor: the
-// largest logit value t whose upper set holds at least `want` logits
-// (by_mass false) or `want` of their mass (by_mass true). Returns the key
-// of t, or 0 to keep them all.
-template <int DT, bool kVec>
-__device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, double cd, float mref,
-                               bool by_mass, double want, uint32_t kfloor) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  int64_t parent = 0;
-  double above = 0.0, target = want;
-  int level = 0, sel = 0;
-  for (; level < kSelLevels; ++level) {
-    for (int i = tid; i < kWaves * kSelBuckets; i += kThreads) {
-      (&L.cnt[0][0])[i] = 0u;
-      (&L.mass[0][0])[i] = 0.0;
-    }
-    __syncthreads();
-    for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
-      if (order_key(l) < kfloor) return;
-      const double D = (double)l * cd - (double)mref;
-      const int bk = sel_bucket(D, level, parent);
-      if (bk < 0) return;
-      atomicAdd(&L.cnt[wave][bk], 1u);
-      if (by_mass) atomicAdd(&L.mass[wave][bk], exp2_weight(D, L.tab));
-    });
-    __syncthreads();
-    unsigned n_t = 0;
-    double m_t = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      n_t += L.cnt[w][tid];
-      m_t += L.mass[w][tid];
-    }
-    const double incl = block_scan(by_mass ? m_t : (double)n_t, L.scan);
-    if (level == 0 && by_mass) target = want * L.scan[kThreads - 1];
-    const double prev = tid ? L.scan[tid - 1] : 0.0;
-    if (tid == 0) L.sel = -1;
-    __syncthreads();
-    if (above + incl >= target && !(tid > 0 && above + prev >= target)) L.sel = tid;
-    __syncthreads();
-    sel = L.sel;
-    if (sel < 0 || (level == 0 && sel == kSelBuckets - 1)) return 0u;   // keep all
-    above += sel ? L.scan[sel - 1] : 0.0;
-    unsigned n_sel = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) n_sel += L.cnt[w][sel];
-    __syncthreads();
-    if (n_sel <= (unsigned)kSelCap) break;
-    if (level + 1 < kSelLevels) parent = (level == 0) ? sel : parent * kSelBuckets + sel;
-  }
-  if (level == kSelLevels) {
-    // more than kSelCap logits within 2^-18 / 4 of one log2 weight: keep
-    // that whole bucket (its smallest key)
-    if (tid == 0) L.kfloor = 0xFFFFFFFFu;
-    __syncthreads();
-    for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
-      const uint32_t k = order_key(l);
-      if (k < kfloor) return;
-      const double D = (double)l * cd - (double)mref;
-      if (sel_bucket(D, kSelLevels - 1, parent) == sel) atomicMin(&L.kfloor, k);
-    });
-    __syncthreads();
-    const uint32_t k = L.kfloor;
-    __syncthreads();
-    return k;
-  }
-  // collect the bucket, sort it, scan it
-  if (tid == 0) L.n = 0;
-  __syncthreads();
-  for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
-    const uint32_t k = order_key(l);
-    if (k < kfloor) return;
-    const double D = (double)l * cd - (double)mref;
-    if (sel_bucket(D, level, parent) != sel) return;
-    const int slot = atomicAdd(&L.n, 1);
-    if (slot < kSelCap) {
-      L.key[slot] = k;
-      L.w[slot] = by_mass ? exp2_weight(D, L.tab) : 1.0;
-    }
-  });
-  __syncthreads();
-  const int n = min(L.n, kSelCap);
+// Sorts the n collected logits (key, weight) by value, largest first, and
+// returns the key at which above + their running sum first reaches target.
+// *where (optional): -1 when above alone reaches it (the cut lies above
+// these logits), +1 when even all of them fall short (below), else 0; with
+// where null, falling short keeps them all (rounding at the row's end).
+__device__ uint32_t scan_collected(SelLds& L, int n, double above, double target, int* where) {
+  const int tid = threadIdx.x;
   sort_collected(L, n);
   constexpr int kPer = kSelCap / kThreads;
   double loc = 0.0;
@@ -1305,6 +1234,7 @@ __device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, d
     loc += e < n ? L.w[e] : 0.0;
   }
   const double incl = block_scan(loc, L.scan);
+  const double all = L.scan[kThreads - 1];
   if (tid == 0) L.sel = INT_MAX;
   __syncthreads();
   double run = above + incl - loc;
@@ -1318,10 +1248,117 @@ __device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, d
     }
   }
   __syncthreads();
-  const int at = L.sel == INT_MAX ? n - 1 : L.sel;   // rounding short of the target: whole bucket
-  const uint32_t k = n > 0 ? L.key[at] : 0u;
+  const int sel = L.sel;
+  uint32_t k = 0u;
+  if (where) *where = above >= target ? -1 : (above + all < target ? 1 : 0);
+  if (sel != INT_MAX) k = L.key[sel];
+  else if (n > 0) k = L.key[n - 1];               // short of the target: the whole set
   __syncthreads();
   return k;
+}
+
+// The cut for one criterion among the logits with key >= kfloor: the
+// largest logit value t whose upper set holds at least `want` logits
+// (kMass false) or `want` of their mass (kMass true). Returns the key of t,
+// or 0 to keep them all. Logits below kfloor count as -inf.
+template <int DT, bool kVec, bool kMass>
+__device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, double cd, float mref,
+                               double want, uint32_t kfloor) {
+  const int tid = threadIdx.x;
+  int64_t parent = 0;
+  double above = 0.0, target = want;
+  int level = 0, sel = 0;
+  for (; level < kSelLevels; ++level) {
+    const int nb = level == 0 ? kSelBuckets0 : kSelBuckets;
+    for (int i = tid; i < nb; i += kThreads) {
+      L.cnt[i] = 0u;
+      L.mass[i] = 0.0;
+    }
+    __syncthreads();
+    if (level == 0) {                              // every logit lands in a bucket
+      for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+        const double D = order_key(l) >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
+        const int bk = sel_bucket(D, 0, 0);
+        atomicAdd(&L.cnt[bk], 1u);
+        if (kMass) atomicAdd(&L.mass[bk], exp2_weight(D, L.tab));
+      });
+    } else {                                       // only those of the parent bucket
+      for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+        const double D = order_key(l) >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
+        const int bk = sel_bucket(D, level, parent);
+        if (bk >= 0) {
+          atomicAdd(&L.cnt[bk], 1u);
+          if (kMass) atomicAdd(&L.mass[bk], exp2_weight(D, L.tab));
+        }
+      });
+    }
+    __syncthreads();
+    // inclusive scan over the buckets, nb / kThreads per thread
+    const int per = nb / kThreads;
+    double loc = 0.0;
+    for (int j = 0; j < per; ++j) {
+      const int e = tid * per + j;
+      loc += kMass ? L.mass[e] : (double)L.cnt[e];
+    }
+    const double incl = block_scan(loc, L.scan);
+    if (level == 0 && kMass) target = want * L.scan[kThreads - 1];
+    if (tid == 0) L.sel = INT_MAX;
+    __syncthreads();
+    double run = above + incl - loc;
+    for (int j = 0; j < per; ++j) {
+      const int e = tid * per + j;
+      run += kMass ? L.mass[e] : (double)L.cnt[e];
+      if (run >= target) {
+        atomicMin(&L.sel, e);
+        break;
+      }
+    }
+    __syncthreads();
+    sel = L.sel;
+    if (sel == INT_MAX || (level == 0 && sel == kSelBuckets0 - 1)) return 0u;   // keep all
+    // mass (or count) of the buckets before sel
+    double before = 0.0;
+    for (int j = 0; j < per; ++j) {
+      const int e = tid * per + j;
+      if (e < sel) before += kMass ? L.mass[e] : (double)L.cnt[e];
+    }
+    block_scan(before, L.scan);
+    above += L.scan[kThreads - 1];
+    const unsigned n_sel = L.cnt[sel];
+    __syncthreads();
+    if (n_sel <= (unsigned)kSelCap) break;
+    if (level + 1 < kSelLevels) parent = (level == 0) ? sel : parent * kSelBuckets + sel;
+  }
+  if (level == kSelLevels) {
+    // more than kSelCap logits within 2^-20 / 16 of one log2 weight: keep
+    // that whole bucket (its smallest key)
+    if (tid == 0) L.kfloor = 0xFFFFFFFFu;
+    __syncthreads();
+    for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+      const uint32_t k = order_key(l);
+      const double D = k >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
+      if (sel_bucket(D, kSelLevels - 1, parent) == sel) atomicMin(&L.kfloor, k);
+    });
+    __syncthreads();
+    const uint32_t k = L.kfloor;
+    __syncthreads();
+    return k;
+  }
+  // collect the bucket, sort it, scan it
+  if (tid == 0) L.n = 0;
+  __syncthreads();
+  for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+    const uint32_t k = order_key(l);
+    const double D = k >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
+    if (sel_bucket(D, level, parent) != sel) return;
+    const int slot = atomicAdd(&L.n, 1);
+    if (slot < kSelCap) {
+      L.key[slot] = k;
+      L.w[slot] = kMass ? exp2_weight(D, L.tab) : 1.0;
+    }
+  });
+  __syncthreads();
+  return scan_collected(L, min(L.n, kSelCap), above, target, nullptr);
 }
 
 // Per row: the cut (top-k, then top-p), and the fp32 chunk sums of the kept
@@ -1364,9 +1401,9 @@ __global__ __launch_bounds__(kThreads) void sv_select_kernel(Args A) {
   const float tp = A.top_p ? A.top_p[b] : 1.f;
   uint32_t cut = 0u;
   if (tk > 0 && tk < A.V)
-    cut = select_cut<DT, kVec>(row, A.n_chunk, A.V, L, cd, mref, false, (double)tk, 0u);
+    cut = select_cut<DT, kVec, false>(row, A.n_chunk, A.V, L, cd, mref, (double)tk, 0u);
   if (tp < 1.f) {
-    const uint32_t cp = select_cut<DT, kVec>(row, A.n_chunk, A.V, L, cd, mref, true, (double)tp, cut);
+    const uint32_t cp = select_cut<DT, kVec, true>(row, A.n_chunk, A.V, L, cd, mref, (double)tp, cut);
     if (cp) cut = cp;
   }
   const float thr = cut ? key_value(cut) : kNegInf;
