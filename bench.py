@@ -74,16 +74,22 @@ def algorithmic_bytes(wl, rejected=None) -> int:
 
 
 def lazy_bytes(wl, accept) -> int:
-    """Bytes early-exit verification must read: for a request that stopped at
-    position a (accept length a + 1), target rows 0..a and draft rows
-    0..min(a, K - 1), plus the draw's chunk, plus (explicit drafts) the stop
-    rows again for the residual when a < K."""
+    """Bytes early-exit verification reads: windows of positions [0], [1, 2],
+    [3, 6], ... are read in rounds, so a request that stopped at position a
+    (accept length a + 1) read target rows 0..e and draft rows 0..min(e, K - 1),
+    with e the end of a's window; plus the draw's chunk, plus (explicit
+    drafts) the stop rows again for the residual when a < K."""
     import numpy as np
     es = 2 if wl["dtype"] == "bf16" else 4
     K, V = wl["K"], wl["V"]
     explicit = wl.get("draft") is not None
     a = accept.astype(np.int64) - 1
-    rows = (a + 1) + (np.minimum(a + 1, K) if explicit else 0)
+    ends, lo, w = [], 0, 1
+    while lo <= K:
+        ends.append(min(lo + w - 1, K))
+        lo, w = lo + w, w * 2
+    e = np.array([next(x for x in ends if x >= ai) for ai in a], dtype=np.int64)
+    rows = (e + 1) + (np.minimum(e + 1, K) if explicit else 0)
     total = int(rows.sum()) * V * es + len(a) * min(CHUNK_BYTES, V * es)
     if explicit:
         total += int((a < K).sum()) * 2 * V * es
@@ -366,7 +372,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_record(wl["name"]),
-                     "kernel": (f"one verification call: {K + 1} rounds of row pass + decision"
+                     "kernel": ("one verification call: rounds of row pass + decision over "
+                                "position windows 1, 2, 4, ..."
                                 if lazy else "one verification call: row pass + select pass + tail"
                                 if filt else "one verification call: row pass + tail") +
                                (" + residual pass" if mode == "sample" and draft is not None else ""),

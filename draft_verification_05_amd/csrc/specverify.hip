@@ -26,6 +26,7 @@
 //              ticket) draws the token.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <cstdlib>
@@ -64,8 +65,9 @@ struct Args {
   int total_k;                             // ragged: number of packed drafts
   const uint32_t* mask;                    // grammar bitmask [B, K+1, mask_words] or null
   int mask_words;                          // ceil(V / 32)
-  int round;                               // early-exit rounds: position of this round, else -1
-  int round_rows;                          // rows per request in a round (1, or 2 with draft logits)
+  int round;                               // early-exit rounds: first position of this round, else -1
+  int round_hi;                            // last position of this round
+  int round_rows;                          // rows per request in a round (target + draft rows)
   int* alive;                              // [B]: request still open after the previous round
   const float* temperature;                // [B]
   const uint64_t* seeds;                   // [B]
@@ -642,11 +644,13 @@ __device__ void tree_tail(const Args& A, int b, TailLds& S) {
 
 // ------------------------------------------------- early-exit rounds ---
 // The rule stops at the first rejection ("推测解码与 MTP" §2.1), so rows
-// after it are never needed. Round i reads target row i (and draft row i)
-// of the requests still open; the last workgroup of a request to finish
-// its share then decides position i with one wave: accepted -> open for
-// round i + 1; rejected -> draw (or hand the residual to the residual
-// pass) and close; position K -> bonus draw. Everything the decision reads
+// after it are never needed. Rounds cover windows of positions 1, 2, 4, ...
+// wide ([0], [1, 2], [3, 6], ...): a round reads the window's target rows
+// (and draft rows) of the requests still open; the last workgroup of a
+// request to finish its share then decides the window's positions in order
+// with one wave: all accepted -> open for the next round; a rejection ->
+// draw (or hand the residual to the residual pass) and close; position K ->
+// bonus draw. Everything the decision reads
 // from other workgroups (partials, the gathered logits, the uniforms) is
 // published with agent-scope stores and fetched with agent-scope loads.
 
@@ -664,25 +668,12 @@ __device__ float2 merge_row(const Args& A, int b, int r) {
   return make_float2(M, s);
 }
 
+// Position i of request b: accept (true: go on), or stop there (draw, or
+// leave the residual to its pass) or, at i = K, draw the bonus token.
 template <int MODE, int DT, bool kVec>
-__device__ void round_decide(const Args& A, int b) {
+__device__ bool decide_position(const Args& A, int b, int i, float c, const Req& rq, int32_t* otok) {
   const int lane = threadIdx.x & 63;
-  const int i = A.round, K = A.K, R = A.R, V = A.V;
-  const Req rq = request(A, b);
-  int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
-  const float T = A.temperature[b];
-  if (!(T > 0.f && T < __builtin_inff())) {        // refused request (round 0 only)
-    if (lane <= K) otok[lane] = -1;
-    if (lane < K && A.out_p) A.out_p[(int64_t)b * K + lane] = 0.f;
-    if (lane < K && A.out_q) A.out_q[(int64_t)b * K + lane] = 0.f;
-    if (lane == 0) {
-      A.out_len[b] = 0;
-      A.alive[b] = 0;
-      if (MODE == kExplicit) A.rec[b].pending = 0;
-    }
-    return;
-  }
-  const float c = kLog2e / T;
+  const int K = A.K, R = A.R, V = A.V;
   const float2 un = fetch(A.unif + (int64_t)b * R + i);
   const float2 mp = merge_row(A, b, i);
   const int64_t rowg0 = (int64_t)b * A.rows;
@@ -723,13 +714,10 @@ __device__ void round_decide(const Args& A, int b) {
       if (A.out_q) A.out_q[(int64_t)b * K + i] = q;
     }
     if (accept) {
-      if (lane == 0) {
-        otok[i] = x;
-        A.alive[b] = 1;
-      }
-      return;
+      if (lane == 0) otok[i] = x;
+      return true;
     }
-    // stop at a = i: positions after it are padding, their p and q unread
+    // stop at a = i: positions after it are padding, their p and q not reported
     if (lane > i && lane <= K) otok[lane] = -1;
     if (lane > i && lane < K) {
       if (A.out_p) A.out_p[(int64_t)b * K + lane] = 0.f;
@@ -739,7 +727,7 @@ __device__ void round_decide(const Args& A, int b) {
       A.out_len[b] = i + 1;
       A.alive[b] = 0;
     }
-    if (MODE == kExplicit) return;
+    if (MODE == kExplicit) return false;
     y = draw_from_partials<DT, kVec, false, false>(A, b, rq, i, c, Mx, x, un.y, kNegInf, [&](int s) {
       return fetch(A.part + (rowg0 + i) * A.n_chunk + s);
     });
@@ -756,6 +744,32 @@ __device__ void round_decide(const Args& A, int b) {
     }
   }
   if (lane == 0) otok[i] = y;
+  return false;
+}
+
+// The positions round..round_hi of request b, in order, until one stops it.
+template <int MODE, int DT, bool kVec>
+__device__ void round_decide(const Args& A, int b) {
+  const int lane = threadIdx.x & 63;
+  const int K = A.K;
+  const Req rq = request(A, b);
+  int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
+  const float T = A.temperature[b];
+  if (!(T > 0.f && T < __builtin_inff())) {        // refused request (round 0 only)
+    if (lane <= K) otok[lane] = -1;
+    if (lane < K && A.out_p) A.out_p[(int64_t)b * K + lane] = 0.f;
+    if (lane < K && A.out_q) A.out_q[(int64_t)b * K + lane] = 0.f;
+    if (lane == 0) {
+      A.out_len[b] = 0;
+      A.alive[b] = 0;
+      if (MODE == kExplicit) A.rec[b].pending = 0;
+    }
+    return;
+  }
+  const float c = kLog2e / T;
+  for (int i = A.round; i <= A.round_hi; ++i)
+    if (!decide_position<MODE, DT, kVec>(A, b, i, c, rq, otok)) return;
+  if (lane == 0) A.alive[b] = 1;                   // every position of the window accepted
 }
 
 // ------------------------------------------------------------ row pass ---
@@ -922,8 +936,8 @@ __device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, const MaskRaw& mk, 
 // streams chunks c_lo + v, c_lo + v + 4, ... Full chunks go through a
 // two-deep pipeline of raw 16-byte loads; a row's last, partial chunk and
 // rows that are not 16-byte aligned take the checked element path.
-// kRound: one early-exit round (rows `round` of the open requests), the
-// decision taken at the end by the request's last workgroup.
+// kRound: one early-exit round (rows round..round_hi of the open requests),
+// the decision taken at the end by the request's last workgroup.
 template <int MODE, int DT, bool kVec, bool kMask, bool kRound>
 __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   constexpr int kCE = Chunk<DT>::kElems;
@@ -935,9 +949,10 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   if constexpr (!kRound) {                        // every row of every request
     b = slot / A.rows;
     r = slot % A.rows;
-  } else {                                        // target (and draft) row `round`
+  } else {                                        // target (and draft) rows round..round_hi
     b = slot / A.round_rows;
-    r = (slot % A.round_rows == 0) ? A.round : A.R + A.round;
+    const int j = slot % A.round_rows, w = A.round_hi - A.round + 1;
+    r = j < w ? A.round + j : A.R + A.round + (j - w);
     if (A.round > 0 && !A.alive[b]) return;       // the request stopped in an earlier round
   }
   const int rowg = b * A.rows + r;
@@ -1695,6 +1710,19 @@ int chunks_per_wg(int64_t rows_total, int n_chunk) {
   return (int)((n_chunk + wpr - 1) / wpr);
 }
 
+// Early-exit rounds on long rows (at least 48 chunks): at least three
+// chunks per wave, so each workgroup's loads stay pipelined (a round has
+// few rows, and one-chunk runs left C3's round 0 at about half the
+// streaming rate); still at least four workgroups per row. Shorter rows
+// keep the plain run length (measured slower otherwise). Runs balanced as
+// above.
+int round_chunks_per_wg(int64_t rows_total, int n_chunk) {
+  const int floor_len = n_chunk >= 12 * kWaves ? 3 * kWaves : 0;
+  const int target = std::max(chunks_per_wg(rows_total, n_chunk), floor_len);
+  const int wpr = (n_chunk + target - 1) / target;
+  return (n_chunk + wpr - 1) / wpr;
+}
+
 void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int rows, void* ws) {
   const int64_t es = elem_bytes(t->dtype);
   A.tgt = static_cast<const char*>(t->data);
@@ -1703,7 +1731,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.drf = nullptr; A.d_sb = 0; A.d_sk = 0;
   A.cu = nullptr; A.total_k = 0;
   A.mask = nullptr; A.mask_words = (V + 31) / 32;
-  A.round = -1; A.round_rows = 0;
+  A.round = -1; A.round_hi = -1; A.round_rows = 0;
   A.B = B; A.K = K; A.V = V; A.R = R; A.rows = rows;
   const int ce = t->dtype == SV_DTYPE_BF16 ? Chunk<kBF16>::kElems : Chunk<kF32>::kElems;
   A.n_chunk = (V + ce - 1) / ce;
@@ -1890,11 +1918,14 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
     return hip_status();
   }
   if (lazy) {                                      // early-exit rounds, one position at a time
-    for (int i = 0; i <= K; ++i) {
+    // windows of positions 1, 2, 4, ... wide: [0], [1, 2], [3, 6], ...
+    for (int lo = 0, w = 1; lo <= K; lo += w, w *= 2) {
+      const int hi = std::min(lo + w - 1, (int)K);
       Args Ai = A;
-      Ai.round = i;
-      Ai.round_rows = (explicit_q && i < K) ? 2 : 1;
-      Ai.cpw = chunks_per_wg((int64_t)B * Ai.round_rows, A.n_chunk);
+      Ai.round = lo;
+      Ai.round_hi = hi;
+      Ai.round_rows = (hi - lo + 1) + (explicit_q ? std::max(0, std::min(hi, K - 1) - lo + 1) : 0);
+      Ai.cpw = round_chunks_per_wg((int64_t)B * Ai.round_rows, A.n_chunk);
       Ai.wpr = (A.n_chunk + Ai.cpw - 1) / Ai.cpw;
       const int64_t g = (int64_t)B * Ai.round_rows * Ai.wpr;
       if ((st = check_grid(g))) return st;

@@ -181,15 +181,18 @@ int spec_verify_sample_filtered(const sv_logits* target, const sv_logits* draft,
 
 /*
  * Early-exit ("lazy") stochastic verification. The rule stops at the first
- * rejection ("推测解码与 MTP" §2.1), so the rows after it are never needed:
- * this call reads position by position (round i reads target row i, and
- * draft row i, only of the requests still open after round i - 1) instead
- * of every row at once. It costs K + 1 dependent rounds and pays off when
- * drafts are rejected early. Tokens, accept lengths and the uniforms used
- * are those of spec_verify_sample; out_p_draft / out_q_draft hold p_i(x_i) /
- * q_i(x_i) up to the stop position and 0 after it (those rows are not
- * read). Arguments, limits and errors as spec_verify_sample; the workspace
- * is sized as for it.
+ * rejection ("推测解码与 MTP" §2.1), so the rows after it are not needed.
+ * This call reads position-major rounds over windows of positions 1, 2, 4,
+ * ... wide ([0], [1, 2], [3, 6], ...). A round reads the window's target
+ * rows (and draft rows) only of the requests still open after the previous
+ * round, and decides its positions in order. A request that stops at
+ * position a has read the rows up to the end of a's window: at most that
+ * window's width minus one past a. It costs about log2(K + 2) dependent
+ * rounds and pays off when drafts are rejected early. Tokens, accept
+ * lengths and the uniforms used are those of spec_verify_sample;
+ * out_p_draft / out_q_draft hold p_i(x_i) / q_i(x_i) up to the stop
+ * position and 0 after it. Arguments, limits and errors as
+ * spec_verify_sample; the workspace is sized as for it.
  */
 int spec_verify_sample_lazy(const sv_logits* target, const sv_logits* draft,
                             const int32_t* draft_tokens, const float* temperature,
