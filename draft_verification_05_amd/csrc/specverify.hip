@@ -654,18 +654,25 @@ __device__ void tree_tail(const Args& A, int b, TailLds& S) {
 // from other workgroups (partials, the gathered logits, the uniforms) is
 // published with agent-scope stores and fetched with agent-scope loads.
 
-// (M, S) of one row from its row-pass workgroup partials.
-__device__ float2 merge_row(const Args& A, int b, int r) {
+// (M, S) of rows r1 and (when r2 >= 0) r2 from their row-pass workgroup
+// partials; the loads of both rows are issued before either merge.
+__device__ void merge_rows(const Args& A, int b, int r1, int r2, float2* out1, float2* out2) {
   const int lane = threadIdx.x & 63;
-  const float2* wp = A.wpart + ((int64_t)b * A.rows + r) * A.wpr;
-  float m = kNegInf, s = 0.f;
+  const float2* wp1 = A.wpart + ((int64_t)b * A.rows + r1) * A.wpr;
+  const float2* wp2 = A.wpart + ((int64_t)b * A.rows + (r2 < 0 ? r1 : r2)) * A.wpr;
+  float m1 = kNegInf, s1 = 0.f, m2 = kNegInf, s2 = 0.f;
   for (int w = lane; w < A.wpr; w += 64) {
-    const float2 v = fetch(wp + w);
-    ms_merge(m, s, v.x, v.y);
+    const float2 v1 = fetch(wp1 + w);
+    const float2 v2 = r2 >= 0 ? fetch(wp2 + w) : make_float2(kNegInf, 0.f);
+    ms_merge(m1, s1, v1.x, v1.y);
+    ms_merge(m2, s2, v2.x, v2.y);
   }
-  const float M = wave_max_all(m);
-  s = wave_sum_all((m == kNegInf) ? 0.f : s * fast_exp2(m - M));
-  return make_float2(M, s);
+  const float M1 = wave_max_all(m1);
+  *out1 = make_float2(M1, wave_sum_all((m1 == kNegInf) ? 0.f : s1 * fast_exp2(m1 - M1)));
+  if (r2 >= 0) {
+    const float M2 = wave_max_all(m2);
+    *out2 = make_float2(M2, wave_sum_all((m2 == kNegInf) ? 0.f : s2 * fast_exp2(m2 - M2)));
+  }
 }
 
 // Position i of request b: accept (true: go on), or stop there (draw, or
@@ -674,14 +681,25 @@ template <int MODE, int DT, bool kVec>
 __device__ bool decide_position(const Args& A, int b, int i, float c, const Req& rq, int32_t* otok) {
   const int lane = threadIdx.x & 63;
   const int K = A.K, R = A.R, V = A.V;
-  const float2 un = fetch(A.unif + (int64_t)b * R + i);
-  const float2 mp = merge_row(A, b, i);
   const int64_t rowg0 = (int64_t)b * A.rows;
+  // every load the position needs, issued together: the draft token, the
+  // gathered logits, the uniforms, the row's chunk partials for a draw (one
+  // per lane when they fit) and the workgroup partials
+  const int xt = i < K ? A.tokens[(int64_t)b * K + i] : -1;
+  const float gx = i < K ? fetch(A.gath + rowg0 + i) : kNegInf;
+  const float gd = (MODE == kExplicit && i < K) ? fetch(A.gath + rowg0 + R + i) : kNegInf;
+  const float2 un = fetch(A.unif + (int64_t)b * R + i);
+  const float2* part_i = A.part + (rowg0 + i) * A.n_chunk;
+  const bool pre_on = A.n_chunk <= 64 && (MODE == kOneHot || i == K);
+  const float2 pre = (pre_on && lane < A.n_chunk) ? fetch(part_i + lane) : make_float2(kNegInf, 0.f);
+  auto part_of = [&](int s) { return pre_on ? pre : fetch(part_i + s); };   // s == lane when pre_on
+  float2 mp, mq = make_float2(kNegInf, 0.f);
+  merge_rows(A, b, i, (MODE == kExplicit && i < K) ? R + i : -1, &mp, &mq);
   int y;
   if (i < K) {
-    const int x = A.tokens[(int64_t)b * K + i];
+    const int x = xt;
     const bool valid = (unsigned)x < (unsigned)V;
-    const float lx = valid ? fetch(A.gath + rowg0 + i) : kNegInf;
+    const float lx = valid ? gx : kNegInf;
     float p, q, Mx = mp.x;
     bool accept;
     if (MODE == kOneHot) {
@@ -694,8 +712,7 @@ __device__ bool decide_position(const Args& A, int b, int i, float c, const Req&
       q = valid ? 1.f : 0.f;
       accept = un.x * q < p;
     } else {
-      const float2 mq = merge_row(A, b, R + i);
-      const float ld = valid ? fetch(A.gath + rowg0 + R + i) : kNegInf;
+      const float ld = valid ? gd : kNegInf;
       const float dp = fmaf(lx, c, -mp.x), dq = fmaf(ld, c, -mq.x);
       p = (valid && mp.y > 0.f) ? fast_exp2(dp) / mp.y : 0.f;
       q = (valid && mq.y > 0.f) ? fast_exp2(dq) / mq.y : 0.f;
@@ -728,14 +745,10 @@ __device__ bool decide_position(const Args& A, int b, int i, float c, const Req&
       A.alive[b] = 0;
     }
     if (MODE == kExplicit) return false;
-    y = draw_from_partials<DT, kVec, false, false>(A, b, rq, i, c, Mx, x, un.y, kNegInf, [&](int s) {
-      return fetch(A.part + (rowg0 + i) * A.n_chunk + s);
-    });
+    y = draw_from_partials<DT, kVec, false, false>(A, b, rq, i, c, Mx, x, un.y, kNegInf, part_of);
     if (y < 0) y = valid ? x : 0;                  // residual without mass: p's mode
   } else {                                         // all K accepted: the bonus token from p_K
-    y = draw_from_partials<DT, kVec, false, false>(A, b, rq, K, c, mp.x, -1, un.y, kNegInf, [&](int s) {
-      return fetch(A.part + (rowg0 + K) * A.n_chunk + s);
-    });
+    y = draw_from_partials<DT, kVec, false, false>(A, b, rq, K, c, mp.x, -1, un.y, kNegInf, part_of);
     if (y < 0) y = 0;
     if (lane == 0) {
       A.out_len[b] = K + 1;
