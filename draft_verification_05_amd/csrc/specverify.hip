@@ -1192,29 +1192,30 @@ __device__ double block_scan(double v, double* buf) {
   return buf[tid];
 }
 
-// Every logit of a row once (f(l, index)), two chunks in flight; past the
-// row's end f sees -inf.
+// Every logit of a row once (f(l, index)), chunk by chunk, the next chunk's
+// load in flight during the current chunk's math; past the row's end f
+// sees -inf.
 template <int DT, bool kVec, class F>
 __device__ void for_each_logit(const char* row, int n_chunk, int V, F f) {
-  constexpr int kCE = Chunk<DT>::kElems, kPT = Chunk<DT>::kPerThread, kU = 2;
-  for (int ch = 0; ch < n_chunk; ch += kU) {
-    float x[kU][kPT];
+  constexpr int kCE = Chunk<DT>::kElems, kPT = Chunk<DT>::kPerThread;
+  float nx[kPT];
+  auto load = [&](int ch) {
+    if (ch < n_chunk) {
+      load_chunk_wg<DT, kVec>(row, (int64_t)ch * kCE, V, nx);
+    } else {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (ch + u < n_chunk) {
-        load_chunk_wg<DT, kVec>(row, (int64_t)(ch + u) * kCE, V, x[u]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < kPT; ++k) x[u][k] = kNegInf;
-      }
+      for (int k = 0; k < kPT; ++k) nx[k] = kNegInf;
     }
+  };
+  load(0);
+  for (int ch = 0; ch < n_chunk; ++ch) {
+    float x[kPT];
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+    for (int k = 0; k < kPT; ++k) x[k] = nx[k];
+    if (ch + 1 < n_chunk) load(ch + 1);
+    // padding past the row reads as -inf: a weight of zero in the last bucket
 #pragma unroll
-      for (int k = 0; k < kPT; ++k) {
-        // padding past the row reads as -inf: a weight of zero in the last bucket
-        f(x[u][k], (int64_t)(ch + u) * kCE + (int64_t)threadIdx.x * kPT + k);
-      }
+    for (int k = 0; k < kPT; ++k) f(x[k], (int64_t)ch * kCE + (int64_t)threadIdx.x * kPT + k);
   }
 }
 
@@ -1392,8 +1393,10 @@ __device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, d
 // Per row: the cut (top-k, then top-p), and the fp32 chunk sums of the kept
 // weights 2^(l c - Mref) for the draw (without the draft token on one-hot
 // rows, as in the row pass), and their total.
+// Four workgroups per CU: the passes are latency-bound, and the occupancy
+// this buys outweighs the few registers it spills.
 template <int MODE, int DT, bool kVec>
-__global__ __launch_bounds__(kThreads) void sv_select_kernel(Args A) {
+__global__ __launch_bounds__(kThreads, 4) void sv_select_kernel(Args A) {
   __shared__ SelLds L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rowg = blockIdx.x;
