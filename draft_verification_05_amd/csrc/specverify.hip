@@ -10,10 +10,14 @@
 //              with y = logit * log2(e) / T for sampling, or (max, argmax)
 //              for greedy/tree. It also keeps the logit of each row's draft
 //              token.
-//   tail       one workgroup per request merges that request's partials
-//              and runs the rule: Philox uniforms, the acceptance scan and
-//              the draw. The launch boundary is the only synchronisation
-//              between the two.
+//   tail       one wave per request merges that request's partials and
+//              runs the rule: the acceptance scan and the draw (the row
+//              pass draws the Philox uniforms). Greedy, tree and one-hot
+//              calls (and small calls with draft logits) run it in the same
+//              launch: one tail workgroup per request after the row pass's
+//              workgroups in the grid, fed through tagged slots (see the
+//              one-launch hand-off below). Otherwise it is a second launch,
+//              and the launch boundary is the only synchronisation.
 //   draw       the chunk sums locate the chunk that holds u * Z, and one
 //              workgroup scan over that single re-read chunk finds the
 //              token. With one-hot drafts the row pass already leaves the
@@ -27,6 +31,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <climits>
 #include <cstdint>
 #include <cstdlib>
@@ -93,6 +99,13 @@ struct Args {
   const float* top_p;   // [B] or null (no top-p)
   RowFilter* rf;        // [B * rows]
   float* fpart;         // [B * rows * n_chunk]: kept weight per chunk
+  // one-launch calls: the row pass hands its results to tail workgroups of
+  // the same grid through tagged slots (value bits, call tag), see put_tag
+  uint64_t* tz_part;    // sampling [B * rows * n_chunk][2]: chunk (M, S); argmax [B * rows * wpr][2]
+  uint64_t* tz_gath;    // [B * rows]: logit of the row's draft token
+  uint64_t* tz_unif;    // [B * R][2]: (u_accept, u_sample) of each position
+  uint32_t tag;         // this call's tag
+  int n_rowwg;          // row-pass workgroups; the B tail workgroups follow them in the grid
   int n_nodes;
   int8_t parent[SV_MAX_TREE_NODES];
   int8_t depth[SV_MAX_TREE_NODES];   // depth of each node (root 0)
@@ -205,6 +218,47 @@ __device__ inline bool last_of_request(unsigned* counter, unsigned n, int* s_las
   }
   __syncthreads();
   return *s_last != 0;
+}
+
+// ------------------------------------------------- one-launch hand-off ---
+// Dense calls run the row pass and the per-request rule in one launch: the
+// grid holds every row-pass workgroup first and then one tail workgroup per
+// request. A row-pass workgroup stores its results as 64-bit words (value
+// bits, tag) with device-coherent stores and ends without waiting for them;
+// a tail workgroup loads the words its request needs with device-coherent
+// loads until every one carries this call's tag. A 64-bit access is single-
+// copy atomic, so a word with the right tag holds the right value, and a word
+// left by an earlier call carries that call's tag: nothing is cleared between
+// calls and no workgroup waits for its stores. Tags are negative-NaN bit
+// patterns, which no other use of the workspace stores.
+__device__ inline void put_tag(uint64_t* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t get_tag(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline bool has_tag(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+__device__ inline float tag_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// A tail workgroup gives up after this many polls (far beyond any row pass:
+// every poll is at least one trip to memory) and refuses its request, so
+// every wave of the launch ends whatever the workspace holds.
+constexpr int kSpinLimit = 1 << 20;
+// Tagged words per lane a one-launch tail loads (per kind of value).
+constexpr int kFusedQ = 8;
+
+// Waits (all lanes loading one broadcast word) until the slot at p carries
+// the tag: a tail first waits this way on its request's last row-pass
+// workgroup, which is dispatched last and usually finishes last, and only
+// then loads all its slots, so requests still streaming cost one word per
+// poll instead of every slot. Returns false when the wait gave up.
+__device__ inline bool wait_tag(const uint64_t* p, uint32_t tag) {
+  for (int spin = 0; spin < kSpinLimit; ++spin) {
+    if (has_tag(get_tag(p), tag)) return true;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  return false;
 }
 
 // ------------------------------------------------------------ drawing ---
@@ -422,6 +476,49 @@ __device__ inline void wstage_issue(const Args& A, int b, int n_rows, float2 ide
   }
 }
 
+// wstage_issue's layout from tagged workgroup partials (one-launch calls):
+// polls until the partials of every live row carry this call's tag. Returns
+// false when the wait gave up. The host admits a one-launch call only when
+// the layout fits (1 <= passes <= 8).
+__device__ inline bool wstage_tagged(const Args& A, int b, int n_live, float2 identity, WStaged& t) {
+  const int lane = threadIdx.x & 63;
+  int G = 1;
+  while (G < A.wpr) G <<= 1;
+  t.G = G;
+  t.per = 64 / G;
+  t.passes = (A.rows + t.per - 1) / t.per;
+  const uint64_t* wp = A.tz_part + 2 * (int64_t)b * A.rows * A.wpr;
+  const int w = lane & (G - 1), rsub = lane / G;
+  uint64_t hv[8], hi[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) { hv[q] = 0ull; hi[q] = 0ull; }
+  // the last live row's last workgroup first (see wait_tag)
+  if (n_live > 0 && !wait_tag(wp + 2 * ((n_live - 1) * A.wpr + A.wpr - 1) + 1, A.tag)) return false;
+  for (int spin = 0;; ++spin) {
+    bool miss = false;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int rr = q * t.per + rsub;
+      if (q < t.passes && rr < n_live && w < A.wpr) {
+        const uint64_t* slot = wp + 2 * (rr * A.wpr + w);
+        if (!has_tag(hv[q], A.tag)) hv[q] = get_tag(slot);
+        if (!has_tag(hi[q], A.tag)) hi[q] = get_tag(slot + 1);
+        miss |= !(has_tag(hv[q], A.tag) && has_tag(hi[q], A.tag));
+      }
+    }
+    if (__ballot(miss) == 0ull) break;
+    if (spin >= kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int rr = q * t.per + rsub;
+    t.v[q] = (q < t.passes && rr < n_live && w < A.wpr) ? make_float2(tag_val(hv[q]), tag_val(hi[q]))
+                                                        : identity;
+  }
+  return true;
+}
+
 // Per-row (max, sum) into S.rowM / S.rowS.
 __device__ void merge_softmax_rows(const Args& A, int b, TailLds& S, const WStaged& t) {
   const int lane = threadIdx.x & 63;
@@ -454,8 +551,8 @@ __device__ void merge_softmax_rows(const Args& A, int b, TailLds& S, const WStag
   __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
 }
 
-// Per-row argmax into S.g.
-__device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, const WStaged& t) {
+// Per-row argmax into sg.
+__device__ void merge_argmax_rows(const Args& A, int b, int n_rows, int* sg, const WStaged& t) {
   const int lane = threadIdx.x & 63;
   if (t.passes > 0) {
     const int rsub = lane / t.G;
@@ -466,7 +563,7 @@ __device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, 
         int idx = __float_as_int(t.v[q].y);
         seg_reduce_am(t.G, v, idx);
         const int rr = q * t.per + rsub;
-        if ((lane & (t.G - 1)) == 0 && rr < n_rows) S.g[rr] = idx;
+        if ((lane & (t.G - 1)) == 0 && rr < n_rows) sg[rr] = idx;
       }
     }
   } else {
@@ -478,7 +575,7 @@ __device__ void merge_argmax_rows(const Args& A, int b, int n_rows, TailLds& S, 
         const float2 p = wp[rr * A.wpr + w];
         am_step(v, idx, p.x, __float_as_int(p.y));
       }
-      S.g[rr] = idx;
+      sg[rr] = idx;
     }
   }
   __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
@@ -579,20 +676,184 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   if (lane == 0) otok[a] = y;
 }
 
-__device__ void greedy_tail(const Args& A, int b, TailLds& S) {
+// sample_tail in a one-launch call: the request's chunk partials (row rr,
+// chunk s in lane s % 64, load rr * npl + s / 64), gathered logits and
+// uniforms come from tagged slots, loaded together and polled until all
+// carry this call's tag; rows merge from the chunk partials, and the draw
+// locates its chunk among the partials already in registers. The host
+// admits a call only when rows * npl <= kFusedQ.
+template <int DT, bool kVec, int MODE, bool kMask>
+__device__ void fused_sample_tail(const Args& A, int b) {
+  __shared__ float s_rowM[kFusedQ], s_rowS[kFusedQ];
+  const int lane = threadIdx.x & 63;
+  const Req rq = request(A, b);
+  const int K = rq.k, V = A.V, R = A.R, nch = A.n_chunk;
+  const int npl = (nch + 63) >> 6;
+  const int nq = A.rows * npl;
+  const int64_t rowg0 = (int64_t)b * A.rows;
+  const uint32_t tag = A.tag;
+  const int x = lane < K ? A.tokens[rq.x0 + lane] : -1;
+  const bool valid = lane < K && (unsigned)x < (unsigned)V;
+  const float T = A.temperature[b];
+  const bool refused = !rq.ok || !(T > 0.f && T < __builtin_inff());
+  // what this request needs from the row pass (nothing when refused)
+  bool need[kFusedQ];
+#pragma unroll
+  for (int q = 0; q < kFusedQ; ++q) {
+    const int rr = q < nq ? q / npl : 0, s = (q < nq ? q % npl : 0) * 64 + lane;
+    need[q] = !refused && q < nq && (rr < R ? rr <= K : rr - R < K) && s < nch;
+  }
+  const bool need_u = !refused && lane <= K;
+  const bool need_g = !refused && valid;
+  const bool need_d = MODE == kExplicit && need_g;
+  uint64_t pm[kFusedQ], ps[kFusedQ], hx = 0ull, hd = 0ull, hu0 = 0ull, hu1 = 0ull;
+#pragma unroll
+  for (int q = 0; q < kFusedQ; ++q) { pm[q] = 0ull; ps[q] = 0ull; }
+  // the last chunk of the last live row belongs to the request's last workgroup
+  const int r_last = (MODE == kExplicit && K > 0) ? R + K - 1 : K;
+  bool got = refused || wait_tag(A.tz_part + 2 * ((rowg0 + r_last) * nch + nch - 1) + 1, tag);
+  for (int spin = 0; got; ++spin) {
+    bool miss = false;
+#pragma unroll
+    for (int q = 0; q < kFusedQ; ++q) {
+      if (need[q]) {
+        const uint64_t* slot = A.tz_part + 2 * ((rowg0 + q / npl) * nch + (q % npl) * 64 + lane);
+        if (!has_tag(pm[q], tag)) pm[q] = get_tag(slot);
+        if (!has_tag(ps[q], tag)) ps[q] = get_tag(slot + 1);
+      }
+    }
+    if (need_g && !has_tag(hx, tag)) hx = get_tag(A.tz_gath + rowg0 + lane);
+    if (need_d && !has_tag(hd, tag)) hd = get_tag(A.tz_gath + rowg0 + R + lane);
+    if (need_u) {
+      const uint64_t* us = A.tz_unif + 2 * ((int64_t)b * R + lane);
+      if (!has_tag(hu0, tag)) hu0 = get_tag(us);
+      if (!has_tag(hu1, tag)) hu1 = get_tag(us + 1);
+    }
+#pragma unroll
+    for (int q = 0; q < kFusedQ; ++q) miss |= need[q] && !(has_tag(pm[q], tag) && has_tag(ps[q], tag));
+    miss |= need_g && !has_tag(hx, tag);
+    miss |= need_d && !has_tag(hd, tag);
+    miss |= need_u && !(has_tag(hu0, tag) && has_tag(hu1, tag));
+    if (__ballot(miss) == 0ull) break;
+    if (spin >= kSpinLimit) { got = false; break; }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  float cm[kFusedQ], cs[kFusedQ];                  // chunk partials (identity where not needed)
+#pragma unroll
+  for (int q = 0; q < kFusedQ; ++q) {
+    cm[q] = need[q] ? tag_val(pm[q]) : kNegInf;
+    cs[q] = need[q] ? tag_val(ps[q]) : 0.f;
+  }
+  int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
+  for (int j = K + 1 + lane; j < A.out_cols; j += 64) otok[j] = -1;   // columns past this request's drafts
+  if (refused || !got) {
+    if (lane <= K) otok[lane] = -1;
+    if (lane < K && A.out_p) A.out_p[rq.x0 + lane] = 0.f;
+    if (lane < K && A.out_q) A.out_q[rq.x0 + lane] = 0.f;
+    if (lane == 0) {
+      A.out_len[b] = 0;
+      if (MODE == kExplicit) A.rec[b].pending = 0;
+    }
+    return;
+  }
+  // per-row (max, sum): a lane's npl partials of the row, then the wave
+  {
+    float m = kNegInf, sacc = 0.f;
+#pragma unroll
+    for (int q = 0; q < kFusedQ; ++q) {
+      if (q < nq) {                                // uniform
+        ms_merge(m, sacc, cm[q], cs[q]);
+        if ((q + 1) % npl == 0) {                  // the row's last load: uniform
+          float mr = m, sr = sacc;
+          seg_reduce_ms(64, mr, sr);
+          if (lane == 0) { s_rowM[q / npl] = mr; s_rowS[q / npl] = sr; }
+          m = kNegInf;
+          sacc = 0.f;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
+  }
+  const float uacc = tag_val(hu0), usmp = tag_val(hu1);
+  float lx = need_g ? tag_val(hx) : kNegInf, ld = need_d ? tag_val(hd) : kNegInf;
+  const float c = kLog2e / T;
+  float p = 0.f, q = 0.f, Mx = kNegInf, lp = kNegInf, lq = kNegInf;
+  if (lane < K) {
+    if (MODE == kOneHot) {
+      // row `lane`'s sums leave x out: add its own term back for p(x)
+      const float Mi = s_rowM[lane], Si = s_rowS[lane];
+      Mx = fmaxf(Mi, lx * c);
+      const float Sx = (Mi == kNegInf) ? 0.f : Si * fast_exp2(Mi - Mx);
+      const float e = (valid && Mx != kNegInf) ? fast_exp2(fmaf(lx, c, -Mx)) : 0.f;
+      const float St = Sx + e;
+      p = St > 0.f ? e / St : 0.f;
+      q = valid ? 1.f : 0.f;
+    } else {
+      const float Mp = s_rowM[lane], Sp = s_rowS[lane];
+      const float Mq = s_rowM[R + lane], Sq = s_rowS[R + lane];
+      const float dp = fmaf(lx, c, -Mp), dq = fmaf(ld, c, -Mq);
+      p = (valid && Sp > 0.f) ? fast_exp2(dp) / Sp : 0.f;
+      q = (valid && Sq > 0.f) ? fast_exp2(dq) / Sq : 0.f;
+      lp = (valid && Sp > 0.f) ? dp - __log2f(Sp) : kNegInf;
+      lq = (valid && Sq > 0.f) ? dq - __log2f(Sq) : kNegInf;
+    }
+    if (A.out_p) A.out_p[rq.x0 + lane] = p;
+    if (A.out_q) A.out_q[rq.x0 + lane] = q;
+  }
+  const bool accept = MODE == kOneHot ? (uacc * q < p) : (__log2f(uacc) + lq < lp);
+  const int rej = first_lane(lane < K && !accept);
+  const int a = rej < 0 ? K : rej;
+  if (lane <= K && lane != a) otok[lane] = lane < a ? x : -1;
+  if (lane == 0) A.out_len[b] = a + 1;
+  const float ua = lane_f(usmp, a);
+  if (MODE == kExplicit) {
+    if (a < K) {
+      if (lane == 0) {
+        Record rc;
+        rc.a = a; rc.pending = 1; rc.c = c; rc.u = ua;
+        rc.Mp = s_rowM[a]; rc.Sp = s_rowS[a]; rc.Mq = s_rowM[R + a]; rc.Sq = s_rowS[R + a];
+        A.rec[b] = rc;
+      }
+      return;
+    }
+    if (lane == 0) A.rec[b].pending = 0;
+  }
+  const bool resid = (MODE == kOneHot && a < K);
+  const float M = resid ? lane_f(Mx, a) : s_rowM[a];
+  const int xe = resid ? lane_i(x, a) : -1;
+  // chunk s of row a sits in this lane's load a * npl + s / 64 (s = lane mod 64)
+  auto part_of = [&](int s) {
+    const int qa = a * npl + (s >> 6);             // uniform
+    float2 v = make_float2(kNegInf, 0.f);
+#pragma unroll
+    for (int qq = 0; qq < kFusedQ; ++qq)
+      if (qq == qa) v = make_float2(cm[qq], cs[qq]);
+    return v;
+  };
+  int y = draw_from_partials<DT, kVec, kMask, false>(A, b, rq, a, c, M, xe, ua, kNegInf, part_of);
+  if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
+  if (lane == 0) otok[a] = y;
+}
+
+// kTagged: the partials come from the same launch's row pass (tagged slots).
+template <bool kTagged>
+__device__ void greedy_tail(const Args& A, int b, int* sg) {
   const int lane = threadIdx.x & 63;
   const Req rq = request(A, b);
   const int K = rq.k;
   const int x = lane < K ? A.tokens[rq.x0 + lane] : -1;
   WStaged ws;
-  wstage_issue(A, b, A.rows, make_float2(kNegInf, __int_as_float(INT_MAX)), ws);
-  merge_argmax_rows(A, b, A.rows, S, ws);
-  const int g = lane <= K ? S.g[lane] : -1;
+  const float2 identity = make_float2(kNegInf, __int_as_float(INT_MAX));
+  bool got = true;
+  if constexpr (kTagged) got = wstage_tagged(A, b, rq.ok ? K + 1 : 0, identity, ws);
+  else wstage_issue(A, b, A.rows, identity, ws);
+  merge_argmax_rows(A, b, A.rows, sg, ws);
+  const int g = lane <= K ? sg[lane] : -1;
   const int mis = first_lane(lane < K && x != g);
   const int a = mis < 0 ? K : mis;
   int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
   for (int j = K + 1 + lane; j < A.out_cols; j += 64) otok[j] = -1;   // columns past this request's drafts
-  if (!rq.ok) {                                    // refused (ragged offsets)
+  if (!rq.ok || !got) {                            // refused (ragged offsets; a wait that gave up)
     if (lane <= K) otok[lane] = -1;
     if (lane == 0) A.out_len[b] = 0;
     return;
@@ -608,15 +869,28 @@ __device__ void greedy_tail(const Args& A, int b, TailLds& S) {
 // when its token is its parent's argmax and its parent is accepted, settled
 // one depth level at a time; the answer is the deepest accepted node (the
 // lowest index among equals), and its root path is read off the parents.
-__device__ void tree_tail(const Args& A, int b, TailLds& S) {
+template <bool kTagged>
+__device__ void tree_tail(const Args& A, int b, int* sg) {
   const int lane = threadIdx.x & 63, N = A.n_nodes;
   const int xn = lane < N ? A.tokens[(int64_t)b * N + lane] : -1;
   WStaged ws;
-  wstage_issue(A, b, N, make_float2(kNegInf, __int_as_float(INT_MAX)), ws);
+  const float2 identity = make_float2(kNegInf, __int_as_float(INT_MAX));
+  if constexpr (kTagged) {
+    if (!wstage_tagged(A, b, N, identity, ws)) {   // the wait gave up: refuse the request
+      if (lane < N) A.out_tokens[(int64_t)b * A.out_cols + lane] = -1;
+      if (lane == 0) {
+        A.out_len[b] = 0;
+        if (A.out_aux) A.out_aux[b] = -1;
+      }
+      return;
+    }
+  } else {
+    wstage_issue(A, b, N, identity, ws);
+  }
   const int par = lane < N ? A.parent[lane] : -1;
   const int dep = lane < N ? A.depth[lane] : 0;
-  merge_argmax_rows(A, b, N, S, ws);
-  const int g_par = S.g[par < 0 ? 0 : par];
+  merge_argmax_rows(A, b, N, sg, ws);
+  const int g_par = sg[par < 0 ? 0 : par];
   const bool ok = lane == 0 || (lane < N && xn == g_par);
   const int max_depth = (int)wave_max_all((float)dep);
   int acc = lane == 0 ? 1 : 0;
@@ -634,7 +908,7 @@ __device__ void tree_tail(const Args& A, int b, TailLds& S) {
   // the argmax at the deepest node, then -1
   int32_t* out = A.out_tokens + (int64_t)b * A.out_cols;
   if (lane > 0 && lane < N && ((on_path >> lane) & 1ull)) out[dep - 1] = xn;
-  if (lane == len) out[len] = S.g[best];
+  if (lane == len) out[len] = sg[best];
   if (lane > len && lane < N) out[lane] = -1;
   if (lane == 0) {
     A.out_len[b] = len + 1;
@@ -951,11 +1225,28 @@ __device__ __forceinline__ float2 chunk_partial(ChunkRaw& r, const MaskRaw& mk, 
 // rows that are not 16-byte aligned take the checked element path.
 // kRound: one early-exit round (rows round..round_hi of the open requests),
 // the decision taken at the end by the request's last workgroup.
-template <int MODE, int DT, bool kVec, bool kMask, bool kRound>
+// kFused: a one-launch call; the B workgroups after the row pass's run the
+// rule, one request each, on the row pass's tagged results.
+template <int MODE, int DT, bool kVec, bool kMask, bool kRound, bool kFused>
 __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   constexpr int kCE = Chunk<DT>::kElems;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
+  if constexpr (kFused) {
+    if (blockIdx.x >= (unsigned)A.n_rowwg) {      // a tail workgroup: one wave does the work
+      if (wave == 0) {
+        const int bt = (int)(blockIdx.x - (unsigned)A.n_rowwg);
+        if constexpr (MODE == kOneHot || MODE == kExplicit) {
+          fused_sample_tail<DT, kVec, MODE, kMask>(A, bt);
+        } else {
+          __shared__ int s_g[SV_MAX_TREE_NODES];
+          if constexpr (MODE == kGreedy) greedy_tail<true>(A, bt, s_g);
+          else tree_tail<true>(A, bt, s_g);
+        }
+      }
+      return;
+    }
+  }
   const int wi = (int)(blockIdx.x % (unsigned)A.wpr);
   const int slot = (int)(blockIdx.x / (unsigned)A.wpr);
   int b, r;
@@ -979,7 +1270,8 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   // store sits between the chunk loads.
   __shared__ float2 s_part[kMaxChunksPerWg];
   __shared__ float2 s_unif[SV_MAX_DRAFT + 1];
-  float* gath = A.gath + rowg;
+  __shared__ float s_gx;                          // one-launch calls: the draft token's logit
+  float* gath = kFused ? &s_gx : A.gath + rowg;
 
   int ch = c_lo + wave;
   const int ch_end = kVec ? min(c_hi, A.n_full) : c_lo;
@@ -1049,6 +1341,38 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
     if (lane == 0) s_part[ch - c_lo] = res;
   }
   __syncthreads();
+  if constexpr (kFused) {
+    // one-launch call: tagged stores for the tail workgroups, then done
+    // (nothing waits for them). Sampling: every chunk partial, the draft
+    // token's logit (by the workgroup whose run holds it) and the uniforms;
+    // greedy / tree: the workgroup's argmax.
+    const uint32_t tag = A.tag;
+    if constexpr (MODE == kOneHot || MODE == kExplicit) {
+      uint64_t* tp = A.tz_part + 2 * ((int64_t)rowg * A.n_chunk + c_lo);
+      for (int i = tid; i < c_hi - c_lo; i += kThreads) {
+        put_tag(tp + 2 * i, s_part[i].x, tag);
+        put_tag(tp + 2 * i + 1, s_part[i].y, tag);
+      }
+      if (tid == 0 && (unsigned)xe < (unsigned)A.V && xe / kCE >= c_lo && xe / kCE < c_hi)
+        put_tag(A.tz_gath + rowg, s_gx, tag);
+      if (r == 0 && wi == A.wpr - 1 && tid < A.R) {
+        uint64_t* tu = A.tz_unif + 2 * ((int64_t)b * A.R + tid);
+        put_tag(tu, s_unif[tid].x, tag);
+        put_tag(tu + 1, s_unif[tid].y, tag);
+      }
+    } else if (wave == 0) {
+      float v = kNegInf;
+      int idx = INT_MAX;
+      for (int i = lane; i < c_hi - c_lo; i += 64) am_step(v, idx, s_part[i].x, __float_as_int(s_part[i].y));
+      wave_argmax_all(v, idx);
+      if (lane == 0) {
+        uint64_t* tw = A.tz_part + 2 * ((int64_t)rowg * A.wpr + wi);
+        put_tag(tw, v, tag);
+        put_tag(tw + 1, __int_as_float(idx), tag);
+      }
+    }
+    return;
+  }
   float2* part = A.part + (int64_t)rowg * A.n_chunk;
   for (int i = tid; i < c_hi - c_lo; i += kThreads) {
     if constexpr (kRound) publish(part + c_lo + i, s_part[i]);
@@ -1098,9 +1422,9 @@ __global__ __launch_bounds__(64) void sv_tail_kernel(Args A) {
   if constexpr (MODE == kOneHot || MODE == kExplicit) {
     sample_tail<DT, kVec, MODE, kMask>(A, b, S);
   } else if constexpr (MODE == kGreedy) {
-    greedy_tail(A, b, S);
+    greedy_tail<false>(A, b, S.g);
   } else {
-    tree_tail(A, b, S);
+    tree_tail<false>(A, b, S.g);
   }
 }
 
@@ -1670,12 +1994,13 @@ using namespace sv;
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t part, wpart, gath, rec, res, unif, alive, rf, fpart, total;
+  size_t part, wpart, gath, rec, res, unif, alive, rf, fpart, tz, total;
 };
 
 // Workspace: [counters: 4 * SV_MAX_BATCH][chunk partials][workgroup
 //            partials][gathered logits][records][residual partials]
 //            [uniforms][alive flags][row cuts][kept weight per chunk]
+//            [tagged slots of one-launch calls]
 Layout layout(int64_t B, int64_t rows, int64_t V) {
   const int64_t ce = Chunk<kF32>::kElems;          // the smaller chunk: a bound for both dtypes
   const int64_t nch = (V + ce - 1) / ce;
@@ -1689,7 +2014,10 @@ Layout layout(int64_t B, int64_t rows, int64_t V) {
   L.alive = align_up(L.unif + (size_t)(B * rows) * sizeof(float2), 256);   // R <= rows
   L.rf = align_up(L.alive + (size_t)B * sizeof(int), 256);
   L.fpart = align_up(L.rf + (size_t)(B * rows) * sizeof(RowFilter), 256);
-  L.total = align_up(L.fpart + (size_t)(B * rows * nch) * sizeof(float), 256);
+  L.tz = align_up(L.fpart + (size_t)(B * rows * nch) * sizeof(float), 256);
+  // tagged slots of one-launch calls: partials [2 words each], gathered
+  // logits, uniforms [2 words each] (R <= rows, wpr <= nch)
+  L.total = align_up(L.tz + (size_t)(B * rows * (2 * nch + 1 + 2)) * sizeof(uint64_t), 256);
   return L;
 }
 
@@ -1766,6 +2094,11 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.alive = reinterpret_cast<int*>(base + L.alive);
   A.rf = reinterpret_cast<RowFilter*>(base + L.rf);
   A.fpart = reinterpret_cast<float*>(base + L.fpart);
+  A.tz_part = reinterpret_cast<uint64_t*>(base + L.tz);
+  A.tz_gath = A.tz_part + 2 * (size_t)(B * rows * A.n_chunk);
+  A.tz_unif = A.tz_gath + (size_t)(B * rows);
+  A.tag = 0;
+  A.n_rowwg = 0;
   A.filtered = 0;
   A.top_k = nullptr;
   A.top_p = nullptr;
@@ -1780,9 +2113,15 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
 
 // Row pass over every (request, row, chunk run), then one tail wave per
 // request, back to back on the caller's stream.
+// A one-launch call (A.n_rowwg > 0): the row pass's workgroups and then one
+// tail workgroup per request, in one grid.
 template <int MODE, int DT, bool kVec, bool kMask>
 void launch_pair(const Args& A, unsigned grid, hipStream_t st) {
-  SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask, false>), grid, st, A);
+  if (A.n_rowwg > 0) {
+    SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask, false, true>), grid + (unsigned)A.B, st, A);
+    return;
+  }
+  SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask, false, false>), grid, st, A);
   hipLaunchKernelGGL((sv_tail_kernel<MODE, DT, kVec, kMask>), dim3((unsigned)A.B), dim3(64), 0, st, A);
 }
 
@@ -1829,11 +2168,11 @@ template <int MODE, int DT>
 void launch_filtered_dt(const Args& A, bool vec, unsigned grid, hipStream_t st) {
   const dim3 rows((unsigned)((int64_t)A.B * A.rows)), reqs((unsigned)A.B), wave(64), wg(kThreads);
   if (vec) {
-    SV_LAUNCH((sv_rows_kernel<MODE, DT, true, false, false>), grid, st, A);
+    SV_LAUNCH((sv_rows_kernel<MODE, DT, true, false, false, false>), grid, st, A);
     hipLaunchKernelGGL((sv_select_kernel<MODE, DT, true>), rows, wg, 0, st, A);
     hipLaunchKernelGGL((sv_ftail_kernel<MODE, DT, true>), reqs, wave, 0, st, A);
   } else {
-    SV_LAUNCH((sv_rows_kernel<MODE, DT, false, false, false>), grid, st, A);
+    SV_LAUNCH((sv_rows_kernel<MODE, DT, false, false, false, false>), grid, st, A);
     hipLaunchKernelGGL((sv_select_kernel<MODE, DT, false>), rows, wg, 0, st, A);
     hipLaunchKernelGGL((sv_ftail_kernel<MODE, DT, false>), reqs, wave, 0, st, A);
   }
@@ -1855,12 +2194,61 @@ void launch_residual(const Args& A, int dtype, bool vec, unsigned grid, hipStrea
 template <int MODE>
 void launch_round(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
   if (dtype == SV_DTYPE_BF16) {
-    if (vec) SV_LAUNCH((sv_rows_kernel<MODE, kBF16, true, false, true>), grid, st, A);
-    else     SV_LAUNCH((sv_rows_kernel<MODE, kBF16, false, false, true>), grid, st, A);
+    if (vec) SV_LAUNCH((sv_rows_kernel<MODE, kBF16, true, false, true, false>), grid, st, A);
+    else     SV_LAUNCH((sv_rows_kernel<MODE, kBF16, false, false, true, false>), grid, st, A);
   } else {
-    if (vec) SV_LAUNCH((sv_rows_kernel<MODE, kF32, true, false, true>), grid, st, A);
-    else     SV_LAUNCH((sv_rows_kernel<MODE, kF32, false, false, true>), grid, st, A);
+    if (vec) SV_LAUNCH((sv_rows_kernel<MODE, kF32, true, false, true, false>), grid, st, A);
+    else     SV_LAUNCH((sv_rows_kernel<MODE, kF32, false, false, true, false>), grid, st, A);
   }
+}
+
+// One-launch calls. Every call takes a fresh tag: a negative-NaN pattern
+// (0xFF800001 ... 0xFFFFFFFF) from a per-process counter that starts at a
+// clock-derived value, so a library loaded again does not repeat the tags
+// still in a workspace. Tail workgroups may be resident before the last
+// row-pass workgroups, so the batch is capped (1024 tail workgroups leave
+// most of every CU to the row pass). SPECVERIFY_ONE_LAUNCH=0 in the
+// environment at the time of a call selects the two-launch path (the same
+// results up to fp32 rounding order; timing comparisons and tests).
+constexpr int kFusedMaxBatch = 1024;
+
+uint32_t next_tag() {
+  static std::atomic<uint32_t> counter{
+      (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count()};
+  return 0xFF800000u | (1u + counter.fetch_add(1u, std::memory_order_relaxed) % 0x7FFFFFu);
+}
+
+bool one_launch_enabled() {
+  const char* e = getenv("SPECVERIFY_ONE_LAUNCH");
+  return !(e && e[0] == '0');
+}
+
+// Whether the tail's loads fit: sampling, every chunk partial of the
+// request in kFusedQ loads per lane; argmax, the workgroup partials in
+// wstage_issue's grouped layout.
+bool one_launch_fits(const Args& A, int mode) {
+  if (!one_launch_enabled() || A.B > kFusedMaxBatch) return false;
+  if (mode == kOneHot || mode == kExplicit) return A.rows * ((A.n_chunk + 63) / 64) <= kFusedQ;
+  int G = 1;
+  while (G < A.wpr) G <<= 1;
+  if (G > 64) return false;
+  return (A.rows + 64 / G - 1) / (64 / G) <= 8;
+}
+
+// Marks A as a one-launch call when it fits. With draft logits the tail's
+// registers lower the row pass's occupancy (74 VGPRs, six waves per SIMD
+// instead of seven) and a residual pass follows anyway: measured slower
+// once the row pass fills the chip (B=64, K=3, V=32000: 26.9 us against
+// 23.2 us), faster when it is a handful of workgroups (B=1, K=1, V=1000:
+// 9.8 against 10.9 us), so explicit drafts take one launch only up to
+// kFusedExplicitWgs row-pass workgroups.
+constexpr int64_t kFusedExplicitWgs = 1024;
+
+void plan_one_launch(Args& A, int mode, int64_t row_wgs) {
+  if (!one_launch_fits(A, mode) || row_wgs + A.B > (int64_t)(UINT32_MAX / kThreads)) return;
+  if (mode == kExplicit && row_wgs > kFusedExplicitWgs) return;
+  A.n_rowwg = (int)row_wgs;
+  A.tag = next_tag();
 }
 
 // A dispatch counts work-items in 32 bits per dimension.
@@ -1959,11 +2347,13 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
   }
   const int64_t wgs = (int64_t)B * rows * A.wpr;
   if ((st = check_grid(wgs))) return st;
+  plan_one_launch(A, explicit_q ? kExplicit : kOneHot, wgs);
   if (explicit_q) {
     launch_rows<kExplicit>(A, target->dtype, vec, (unsigned)wgs, s);
     if ((st = hip_status())) return st;
     // the residual pass streams one stop row pair per request
     Args A2 = A;
+    A2.n_rowwg = 0;
     A2.cpw = chunks_per_wg(B, A.n_chunk);
     A2.wpr = (A.n_chunk + A2.cpw - 1) / A2.cpw;
     launch_residual(A2, target->dtype, vec, (unsigned)((int64_t)B * A2.wpr), s);
@@ -1999,6 +2389,7 @@ int greedy_impl(const sv_logits* target, const int32_t* cu, int32_t total_k, con
   A.out_aux = out_argmax;
   const int64_t wgs = (int64_t)B * R * A.wpr;
   if ((st = check_grid(wgs))) return st;
+  plan_one_launch(A, kGreedy, wgs);
   launch_rows<kGreedy>(A, target->dtype, aligned16(target), (unsigned)wgs,
                        static_cast<hipStream_t>(stream));
   return hip_status();
@@ -2164,6 +2555,7 @@ int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
   }
   const int64_t wgs = (int64_t)B * N * A.wpr;
   if ((st = check_grid(wgs))) return st;
+  plan_one_launch(A, kTree, wgs);
   launch_rows<kTree>(A, target->dtype, aligned16(target), (unsigned)wgs,
                      static_cast<hipStream_t>(stream));
   return hip_status();

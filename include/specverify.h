@@ -16,9 +16,9 @@
  *    (broadcast). Rows whose address and strides are 16-byte aligned take
  *    the 128-bit load path, others a scalar path with identical results.
  *  - The caller owns every buffer. The library allocates nothing, keeps no
- *    state between calls, never synchronises and launches only on `stream`
- *    (a hipStream_t; NULL = the default stream). Results are ready when the
- *    stream reaches them.
+ *    state between calls beyond a per-process call counter (below), never
+ *    synchronises and launches only on `stream` (a hipStream_t; NULL = the
+ *    default stream). Results are ready when the stream reaches them.
  *  - Argument errors are detected on the host before anything is launched
  *    and returned as a negative status; nothing is written then.
  *    Device-resident values are not checked on the host; their handling is
@@ -27,7 +27,13 @@
  *    spec_verify_workspace_init() (or any zero fill) before its first use.
  *    Every call leaves the workspace's counter words zero again, so it can
  *    be reused by any later call that fits; it must not be shared by calls
- *    that may run concurrently (different streams).
+ *    that may run concurrently (different streams). Calls that run the
+ *    row pass and the per-request rule in one launch hand results over
+ *    through workspace words tagged with a value unique to the call (a
+ *    per-process counter), so a later call never mistakes an earlier
+ *    call's words for its own and nothing needs clearing between calls.
+ *    Setting SPECVERIFY_ONE_LAUNCH=0 in the environment makes every call
+ *    use two launches (the same results up to fp32 summation order).
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
