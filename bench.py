@@ -43,7 +43,11 @@ RAGGED_BASE = {"c3_ragged": "c3_onehot"}   # ragged workloads: base workload cut
 MASKED_BASE = {"c3_masked": "c3_onehot"}   # grammar-masked workloads: base workload + a bitmask
 LAZY_BASE = {"c3_lazy": "c3_onehot", "c2_lazy": "c2_stoch"}   # early-exit verification of a workload
 # top-k / top-p filtered verification: base workload, top_k, top_p (the pages' top_p 0.95)
-FILTER_BASE = {"c3_topp": ("c3_onehot", 0, 0.95), "c2_topp": ("c2_stoch", 0, 0.95)}
+FILTER_BASE = {"c3_topp": ("c3_onehot", 0, 0.95), "c2_topp": ("c2_stoch", 0, 0.95),
+               "c3_topp_tok": ("c3_onehot", 0, 0.95)}
+# calls that ask for tokens and accept lengths only (no p / q outputs), as a
+# serving engine would
+TOKENS_ONLY = {"c3_topp_tok"}
 
 
 def algorithmic_bytes(wl, rejected=None) -> int:
@@ -162,7 +166,8 @@ def main():
                          "(C3 with per-request draft counts K_b ~ uniform{0..5}) or c3_masked "
                          "(C3 with a grammar bitmask allowing each token w.p. 1/2); c3_lazy / c2_lazy "
                          "run C3 / C2 through early-exit verification; c3_topp / c2_topp "
-                         "add a top_p 0.95 filter")
+                         "add a top_p 0.95 filter; c3_topp_tok is c3_topp returning tokens "
+                         "and accept lengths only")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -188,6 +193,7 @@ def main():
     masked = args.workload in MASKED_BASE
     lazy = args.workload in LAZY_BASE
     filt = args.workload in FILTER_BASE
+    tok_only = args.workload in TOKENS_ONLY
     if filt:
         base, f_k, f_p = FILTER_BASE[args.workload]
         wl = dict(make(base, data_seed=0), name=args.workload)
@@ -264,8 +270,9 @@ def main():
                                                  tokens.data_ptr(), temp.data_ptr(), top_k.data_ptr(),
                                                  top_p.data_ptr(), seeds.data_ptr(), i, B, K, V,
                                                  out_tok.data_ptr(), out_len.data_ptr(),
-                                                 out_p.data_ptr(), out_q.data_ptr(), ws.data_ptr(),
-                                                 ws_bytes, stream)
+                                                 None if tok_only else out_p.data_ptr(),
+                                                 None if tok_only else out_q.data_ptr(),
+                                                 ws.data_ptr(), ws_bytes, stream)
         elif lazy:
             rc = lib.spec_verify_sample_lazy(ctypes.byref(descs[c]),
                                              ctypes.byref(ddescs[c]) if ddescs else None,
@@ -367,6 +374,7 @@ def main():
                                                                / (ms_per_step * 1e-3) / 1e9, 1)}}
                       if lazy else {}),
                    **({"filter": {"top_k": f_k, "top_p": f_p}} if filt else {}),
+                   **({"outputs": "tokens and accept lengths (no p / q)"} if tok_only else {}),
                    **({"bitmask": {"allowed_fraction": round(float(wl["mask_allowed"]), 4),
                                    "bytes": int(wl["bitmask"].nbytes)}} if masked else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,

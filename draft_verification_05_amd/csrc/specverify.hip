@@ -1726,6 +1726,52 @@ __global__ __launch_bounds__(kThreads, 4) void sv_select_kernel(Args A) {
   const int rowg = blockIdx.x;
   const int b = rowg / A.rows, r = rowg % A.rows;
   const Req rq = request(A, b);
+  if constexpr (MODE == kOneHot) {
+    // Rows past a certain rejection are not cut when the caller takes only
+    // tokens (no p / q outputs) and top-k is off: the kept mass of a top-p
+    // cut is at least top_p, so the filtered p'(x) <= p(x) / top_p, and
+    // u * top_p >= p(x) (with a margin for fp32 rounding) rejects position j
+    // whatever the cut; the rule stops at or before it and never reads the
+    // cuts of later rows. p(x) is the unfiltered probability from the row
+    // pass. A draft token outside [0, V) is always rejected.
+    if (!A.out_p && !A.out_q && r > 0 && r <= A.K) {
+      __shared__ int s_skip;
+      if (wave == 0) {
+        const int tk0 = A.top_k ? A.top_k[b] : 0;
+        const float tp0 = A.top_p ? A.top_p[b] : 1.f;
+        const float tpe = (tp0 >= 1.f || tp0 != tp0) ? 1.f : tp0;   // filter off: p' = p
+        const float T0 = A.temperature[b];
+        const bool can = (tk0 <= 0 || tk0 >= A.V) && tpe > 0.f && T0 > 0.f && T0 < __builtin_inff();
+        bool certain = false;
+        if (can && lane < r) {
+          const int j = lane;
+          const int xj = A.tokens[(int64_t)b * A.K + j];
+          if ((unsigned)xj >= (unsigned)A.V) {
+            certain = true;
+          } else {
+            const int64_t rj = (int64_t)b * A.rows + j;
+            float M = kNegInf, S = 0.f;
+            for (int w = 0; w < A.wpr; ++w) {
+              const float2 v = A.wpart[rj * A.wpr + w];
+              ms_merge(M, S, v.x, v.y);
+            }
+            const float cj = kLog2e / T0, lx = A.gath[rj];
+            const float Mx = fmaxf(M, lx * cj);
+            const float Sx = (M == kNegInf) ? 0.f : S * fast_exp2(M - Mx);
+            const float e = (Mx != kNegInf) ? fast_exp2(fmaf(lx, cj, -Mx)) : 0.f;
+            const float St = Sx + e;
+            const float pj = St > 0.f ? e / St : 0.f;
+            const float u = A.unif[(int64_t)b * A.R + j].x;
+            certain = u * tpe >= pj * 1.0001f + 1e-30f;
+          }
+        }
+        const bool skip = __ballot(certain) != 0ull;
+        if (lane == 0) s_skip = skip ? 1 : 0;
+      }
+      __syncthreads();
+      if (s_skip) return;
+    }
+  }
   const char* row = row_ptr(A, rq, r);
   float* fp = A.fpart + (int64_t)rowg * A.n_chunk;
   const float T = A.temperature[b];

@@ -173,8 +173,12 @@ int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
  * (int32, fp32); either may be NULL (that filter off for every request).
  * The cut is exact among logits whose weight is within 2^-64 of the row's
  * largest; a cut below that keeps the whole row. out_p_draft / out_q_draft
- * hold the filtered p_i(x_i) / q_i(x_i). Other arguments, limits and errors
- * as spec_verify_sample; the workspace is sized as for it.
+ * hold the filtered p_i(x_i) / q_i(x_i). When both are NULL, drafts are
+ * one-hot and top-k is off for a request, rows past its first certain
+ * rejection (u * top_p >= p_j(x_j), which rejects whatever the cut) are not
+ * cut: the tokens and accept lengths are the same, the call is faster.
+ * Other arguments, limits and errors as spec_verify_sample; the workspace
+ * is sized as for it.
  */
 int spec_verify_sample_filtered(const sv_logits* target, const sv_logits* draft,
                                 const int32_t* draft_tokens, const float* temperature,

@@ -744,3 +744,38 @@ def test_filtered_full_size_c3():
     rep = classify_sample(wl, *g, requests=reqs, top_p=top_p)
     assert_report(rep, "filtered c3 full (sampled)")
     assert rep["filter_near"] <= 0.25 * len(reqs) + 1
+
+
+def test_filtered_tokens_only_equals_full_outputs():
+    """Without p / q outputs the select pass skips the rows past a request's first
+    certain rejection (one-hot drafts, top-k off). Tokens and accept lengths must
+    equal those of the call with p / q outputs bitwise, including requests whose
+    drafts are accepted often (peaked rows, argmax drafts) and requests whose
+    filters forbid skipping (top-k on, top_p off or NaN)."""
+    full = make("c3_onehot", data_seed=1)
+    peaked = make("c3_onehot", data_seed=427, B=40, V=2 * 8192 + 777)
+    vals = oracle.logits_f64(peaked["target"].reshape(-1), "bf16").reshape(peaked["target"].shape)
+    am = vals.argmax(-1).astype(np.int32)
+    rng = np.random.default_rng(428)
+    tok = np.where(rng.random((40, peaked["K"])) < 0.9, am[:, :peaked["K"]], 7).astype(np.int32)
+    peaked = dict(peaked, draft_tokens=tok, temperature=np.full(40, 0.15, np.float32))
+    mixed = make("c3_onehot", data_seed=429, B=48, V=20000)
+    mk, mp = mixed_filters(48, 20000, 430)
+    mp[::7] = np.nan
+    cases = [("c3 full top_p 0.95", full, None, np.full(full["B"], 0.95, np.float32)),
+             ("peaked, argmax drafts", peaked, None, rng.choice([0.5, 0.9, 0.99, 1.0], 40).astype(np.float32)),
+             ("mixed filters", mixed, mk, mp)]
+    for name, wl, top_k, top_p in cases:
+        print(f"[case] filtered tokens-only {name} B={wl['B']} V={wl['V']}", flush=True)
+        d = to_device(wl, DEV)
+        tk = None if top_k is None else torch.from_numpy(top_k).to(DEV)
+        tp = torch.from_numpy(top_p).to(DEV)
+        args = (d["target"], d["draft"], d["tokens"], d["temperature"], tk, tp, d["seeds"], wl["offset"])
+        t1, l1, _, _ = sv.spec_verify_sample_filtered(*args)
+        t2, l2, p2, q2 = sv.spec_verify_sample_filtered(*args, want_probs=False)
+        torch.cuda.synchronize()
+        assert p2 is None and q2 is None
+        np.testing.assert_array_equal(l1.cpu().numpy(), l2.cpu().numpy())
+        np.testing.assert_array_equal(t1.cpu().numpy(), t2.cpu().numpy())
+        hist = np.bincount(l2.cpu().numpy(), minlength=wl["K"] + 2).tolist()
+        print(f"[parity] tokens-only {name}: identical, accept_len histogram {hist}", flush=True)
