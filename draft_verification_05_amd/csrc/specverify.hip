@@ -712,7 +712,7 @@ __device__ void fused_sample_tail(const Args& A, int b) {
   // the last chunk of the last live row belongs to the request's last workgroup
   const int r_last = (MODE == kExplicit && K > 0) ? R + K - 1 : K;
   bool got = refused || wait_tag(A.tz_part + 2 * ((rowg0 + r_last) * nch + nch - 1) + 1, tag);
-  for (int spin = 0; got; ++spin) {
+  for (int spin = 0; got && !refused; ++spin) {
     bool miss = false;
 #pragma unroll
     for (int q = 0; q < kFusedQ; ++q) {
@@ -720,6 +720,7 @@ __device__ void fused_sample_tail(const Args& A, int b) {
         const uint64_t* slot = A.tz_part + 2 * ((rowg0 + q / npl) * nch + (q % npl) * 64 + lane);
         if (!has_tag(pm[q], tag)) pm[q] = get_tag(slot);
         if (!has_tag(ps[q], tag)) ps[q] = get_tag(slot + 1);
+        miss |= !(has_tag(pm[q], tag) && has_tag(ps[q], tag));
       }
     }
     if (need_g && !has_tag(hx, tag)) hx = get_tag(A.tz_gath + rowg0 + lane);
@@ -729,20 +730,12 @@ __device__ void fused_sample_tail(const Args& A, int b) {
       if (!has_tag(hu0, tag)) hu0 = get_tag(us);
       if (!has_tag(hu1, tag)) hu1 = get_tag(us + 1);
     }
-#pragma unroll
-    for (int q = 0; q < kFusedQ; ++q) miss |= need[q] && !(has_tag(pm[q], tag) && has_tag(ps[q], tag));
     miss |= need_g && !has_tag(hx, tag);
     miss |= need_d && !has_tag(hd, tag);
     miss |= need_u && !(has_tag(hu0, tag) && has_tag(hu1, tag));
     if (__ballot(miss) == 0ull) break;
-    if (spin >= kSpinLimit) { got = false; break; }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  float cm[kFusedQ], cs[kFusedQ];                  // chunk partials (identity where not needed)
-#pragma unroll
-  for (int q = 0; q < kFusedQ; ++q) {
-    cm[q] = need[q] ? tag_val(pm[q]) : kNegInf;
-    cs[q] = need[q] ? tag_val(ps[q]) : 0.f;
+    if (spin >= kSpinLimit) got = false;
+    else __builtin_amdgcn_s_sleep(2);
   }
   int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
   for (int j = K + 1 + lane; j < A.out_cols; j += 64) otok[j] = -1;   // columns past this request's drafts
@@ -757,26 +750,19 @@ __device__ void fused_sample_tail(const Args& A, int b) {
     return;
   }
   // per-row (max, sum): a lane's npl partials of the row, then the wave
-  {
-    float m = kNegInf, sacc = 0.f;
+  for (int rr = 0; rr < A.rows; ++rr) {            // uniform
+    float m = kNegInf, sr = 0.f;
 #pragma unroll
-    for (int q = 0; q < kFusedQ; ++q) {
-      if (q < nq) {                                // uniform
-        ms_merge(m, sacc, cm[q], cs[q]);
-        if ((q + 1) % npl == 0) {                  // the row's last load: uniform
-          float mr = m, sr = sacc;
-          seg_reduce_ms(64, mr, sr);
-          if (lane == 0) { s_rowM[q / npl] = mr; s_rowS[q / npl] = sr; }
-          m = kNegInf;
-          sacc = 0.f;
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
+    for (int q = 0; q < kFusedQ; ++q)
+      if (q >= rr * npl && q < (rr + 1) * npl)     // uniform
+        ms_merge(m, sr, need[q] ? tag_val(pm[q]) : kNegInf, need[q] ? tag_val(ps[q]) : 0.f);
+    seg_reduce_ms(64, m, sr);
+    if (lane == 0) { s_rowM[rr] = m; s_rowS[rr] = sr; }
   }
-  const float uacc = tag_val(hu0), usmp = tag_val(hu1);
-  float lx = need_g ? tag_val(hx) : kNegInf, ld = need_d ? tag_val(hd) : kNegInf;
+  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
   const float c = kLog2e / T;
+  const float uacc = tag_val(hu0), usmp = tag_val(hu1);
+  const float lx = need_g ? tag_val(hx) : kNegInf, ld = need_d ? tag_val(hd) : kNegInf;
   float p = 0.f, q = 0.f, Mx = kNegInf, lp = kNegInf, lq = kNegInf;
   if (lane < K) {
     if (MODE == kOneHot) {
@@ -827,7 +813,7 @@ __device__ void fused_sample_tail(const Args& A, int b) {
     float2 v = make_float2(kNegInf, 0.f);
 #pragma unroll
     for (int qq = 0; qq < kFusedQ; ++qq)
-      if (qq == qa) v = make_float2(cm[qq], cs[qq]);
+      if (qq == qa && need[qq]) v = make_float2(tag_val(pm[qq]), tag_val(ps[qq]));
     return v;
   };
   int y = draw_from_partials<DT, kVec, kMask, false>(A, b, rq, a, c, M, xe, ua, kNegInf, part_of);
@@ -2281,13 +2267,12 @@ bool one_launch_fits(const Args& A, int mode) {
   return (A.rows + 64 / G - 1) / (64 / G) <= 8;
 }
 
-// Marks A as a one-launch call when it fits. With draft logits the tail's
-// registers lower the row pass's occupancy (74 VGPRs, six waves per SIMD
-// instead of seven) and a residual pass follows anyway: measured slower
-// once the row pass fills the chip (B=64, K=3, V=32000: 26.9 us against
-// 23.2 us), faster when it is a handful of workgroups (B=1, K=1, V=1000:
-// 9.8 against 10.9 us), so explicit drafts take one launch only up to
-// kFusedExplicitWgs row-pass workgroups.
+// Marks A as a one-launch call when it fits. With draft logits a residual
+// pass follows anyway, and one launch measured slower once the row pass
+// fills the chip (B=64, K=3, V=32000: 28.5 us against 23.4 us) but faster
+// when it is a handful of workgroups (B=1, K=1, V=1000: 9.8 against
+// 10.9 us), so explicit drafts take one launch only up to kFusedExplicitWgs
+// row-pass workgroups.
 constexpr int64_t kFusedExplicitWgs = 1024;
 
 void plan_one_launch(Args& A, int mode, int64_t row_wgs) {
