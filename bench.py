@@ -78,8 +78,8 @@ def algorithmic_bytes(wl, rejected=None) -> int:
 
 
 def lazy_bytes(wl, accept) -> int:
-    """Bytes early-exit verification reads: windows of positions [0], [1, 2],
-    [3, 6], ... are read in rounds, so a request that stopped at position a
+    """Bytes early-exit verification reads: windows of positions [0], then
+    [1, K], are read in rounds, so a request that stopped at position a
     (accept length a + 1) read target rows 0..e and draft rows 0..min(e, K - 1),
     with e the end of a's window; plus the draw's chunk, plus (explicit
     drafts) the stop rows again for the residual when a < K."""
@@ -91,7 +91,7 @@ def lazy_bytes(wl, accept) -> int:
     ends, lo, w = [], 0, 1
     while lo <= K:
         ends.append(min(lo + w - 1, K))
-        lo, w = lo + w, w * 2
+        lo, w = lo + w, K
     e = np.array([next(x for x in ends if x >= ai) for ai in a], dtype=np.int64)
     rows = (e + 1) + (np.minimum(e + 1, K) if explicit else 0)
     total = int(rows.sum()) * V * es + len(a) * min(CHUNK_BYTES, V * es)
@@ -381,7 +381,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_record(wl["name"]),
                      "kernel": ("one verification call: rounds of row pass + decision over "
-                                "position windows 1, 2, 4, ..."
+                                "position windows [0], [1, K]"
                                 if lazy else "one verification call: row pass + select pass + tail"
                                 if filt else "one verification call: row pass + tail") +
                                (" + residual pass" if mode == "sample" and draft is not None else ""),

@@ -904,9 +904,11 @@ __device__ void tree_tail(const Args& A, int b, int* sg) {
 
 // ------------------------------------------------- early-exit rounds ---
 // The rule stops at the first rejection ("推测解码与 MTP" §2.1), so rows
-// after it are never needed. Rounds cover windows of positions 1, 2, 4, ...
-// wide ([0], [1, 2], [3, 6], ...): a round reads the window's target rows
-// (and draft rows) of the requests still open; the last workgroup of a
+// after it are never needed. Two rounds: position 0 alone, then positions
+// 1..K together (each extra round costs a launch, a ticket and a chain of
+// dependent loads, which measured more than the rows a finer split saves).
+// A round reads the window's target rows (and draft rows) of the requests
+// still open; the last workgroup of a
 // request to finish its share then decides the window's positions in order
 // with one wave: all accepted -> open for the next round; a rejection ->
 // draw (or hand the residual to the residual pass) and close; position K ->
@@ -2352,9 +2354,9 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
     }
     return hip_status();
   }
-  if (lazy) {                                      // early-exit rounds, one position at a time
-    // windows of positions 1, 2, 4, ... wide: [0], [1, 2], [3, 6], ...
-    for (int lo = 0, w = 1; lo <= K; lo += w, w *= 2) {
+  if (lazy) {                                      // early-exit rounds
+    // windows of positions [0], then [1, K]
+    for (int lo = 0, w = 1; lo <= K; lo += w, w = K) {
       const int hi = std::min(lo + w - 1, (int)K);
       Args Ai = A;
       Ai.round = lo;

@@ -192,13 +192,12 @@ int spec_verify_sample_filtered(const sv_logits* target, const sv_logits* draft,
 /*
  * Early-exit ("lazy") stochastic verification. The rule stops at the first
  * rejection ("推测解码与 MTP" §2.1), so the rows after it are not needed.
- * This call reads position-major rounds over windows of positions 1, 2, 4,
- * ... wide ([0], [1, 2], [3, 6], ...). A round reads the window's target
- * rows (and draft rows) only of the requests still open after the previous
- * round, and decides its positions in order. A request that stops at
- * position a has read the rows up to the end of a's window: at most that
- * window's width minus one past a. It costs about log2(K + 2) dependent
- * rounds and pays off when drafts are rejected early. Tokens, accept
+ * This call reads two position-major rounds: position 0, then positions
+ * 1..K. A round reads the window's target rows (and draft rows) only of the
+ * requests still open after the previous round, and decides its positions
+ * in order. A request that stops at position 0 has read only its row 0
+ * (and draft row 0); one that goes on reads all its rows. It pays off when
+ * most drafts are rejected at the first position. Tokens, accept
  * lengths and the uniforms used are those of spec_verify_sample;
  * out_p_draft / out_q_draft hold p_i(x_i) / q_i(x_i) up to the stop
  * position and 0 after it. Arguments, limits and errors as
