@@ -106,6 +106,7 @@ struct Args {
   uint64_t* tz_unif;    // [B * R][2]: (u_accept, u_sample) of each position
   uint32_t tag;         // this call's tag
   int n_rowwg;          // row-pass workgroups; the B tail workgroups follow them in the grid
+  int no_tail;          // two-launch explicit calls: the residual pass runs the rule
   int n_nodes;
   int8_t parent[SV_MAX_TREE_NODES];
   int8_t depth[SV_MAX_TREE_NODES];   // depth of each node (root 0)
@@ -584,7 +585,13 @@ __device__ void merge_argmax_rows(const Args& A, int b, int n_rows, int* sg, con
 // ---------------------------------------------------------- row tails ---
 // One wave per request.
 template <int DT, bool kVec, int MODE, bool kMask>
-__device__ void sample_tail(const Args& A, int b, TailLds& S) {
+// write_out: write the outputs and the residual record (false: only return
+// the decision, for the residual pass's other workgroups). Returns the
+// record of a request whose residual draw is still to be done (pending 1),
+// else pending 0.
+__device__ Record sample_tail(const Args& A, int b, TailLds& S, bool write_out = true) {
+  Record rc;
+  rc.pending = 0;
   const int lane = threadIdx.x & 63;
   const Req rq = request(A, b);
   const int K = rq.k, V = A.V, R = A.R;
@@ -608,8 +615,10 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   merge_softmax_rows(A, b, S, ws);
   const bool cached = stage_commit(A, b, S, st);
   int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
-  for (int j = K + 1 + lane; j < A.out_cols; j += 64) otok[j] = -1;   // columns past this request's drafts
+  if (write_out)
+    for (int j = K + 1 + lane; j < A.out_cols; j += 64) otok[j] = -1;   // columns past this request's drafts
   if (!rq.ok || !(T > 0.f && T < __builtin_inff())) {      // refused request
+    if (!write_out) return rc;
     if (lane <= K) otok[lane] = -1;
     if (lane < K && A.out_p) A.out_p[rq.x0 + lane] = 0.f;
     if (lane < K && A.out_q) A.out_q[rq.x0 + lane] = 0.f;
@@ -617,7 +626,7 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
       A.out_len[b] = 0;
       if (MODE == kExplicit) A.rec[b].pending = 0;
     }
-    return;
+    return rc;
   }
   const float c = kLog2e / T;
   float p = 0.f, q = 0.f, Mx = kNegInf, lp = kNegInf, lq = kNegInf;
@@ -644,8 +653,8 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
       lp = (valid && Sp > 0.f) ? dp - __log2f(Sp) : kNegInf;
       lq = (valid && Sq > 0.f) ? dq - __log2f(Sq) : kNegInf;
     }
-    if (A.out_p) A.out_p[rq.x0 + lane] = p;
-    if (A.out_q) A.out_q[rq.x0 + lane] = q;
+    if (write_out && A.out_p) A.out_p[rq.x0 + lane] = p;
+    if (write_out && A.out_q) A.out_q[rq.x0 + lane] = q;
   }
   // the first position whose draft is rejected (u q >= p), K if none; with
   // draft logits the test is log2 u + log2 q < log2 p (log2 0 = -inf)
@@ -653,20 +662,21 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
                                       : (__log2f(uacc) + lq < lp);
   const int rej = first_lane(lane < K && !accept);
   const int a = rej < 0 ? K : rej;
-  if (lane <= K && lane != a) otok[lane] = lane < a ? x : -1;
-  if (lane == 0) A.out_len[b] = a + 1;
+  if (write_out) {
+    if (lane <= K && lane != a) otok[lane] = lane < a ? x : -1;
+    if (lane == 0) A.out_len[b] = a + 1;
+  }
   const float ua = lane_f(usmp, a);
   if (MODE == kExplicit) {
     if (a < K) {
-      if (lane == 0) {
-        Record rc;
-        rc.a = a; rc.pending = 1; rc.c = c; rc.u = ua;
-        rc.Mp = S.rowM[a]; rc.Sp = S.rowS[a]; rc.Mq = S.rowM[R + a]; rc.Sq = S.rowS[R + a];
-        A.rec[b] = rc;
-      }
-      return;
+      rc.a = a; rc.pending = 1; rc.c = c; rc.u = ua;
+      rc.Mp = S.rowM[a]; rc.Sp = S.rowS[a]; rc.Mq = S.rowM[R + a]; rc.Sq = S.rowS[R + a];
+      rc.tp = kNegInf; rc.tq = kNegInf;
+      if (write_out && lane == 0) A.rec[b] = rc;
+      return rc;
     }
-    if (lane == 0) A.rec[b].pending = 0;
+    if (write_out && lane == 0) A.rec[b].pending = 0;
+    if (!write_out) return rc;                     // the bonus draw is the writer's
   }
   const bool resid = (MODE == kOneHot && a < K);
   const float M = resid ? lane_f(Mx, a) : S.rowM[a];
@@ -674,6 +684,7 @@ __device__ void sample_tail(const Args& A, int b, TailLds& S) {
   int y = draw_softmax_row<DT, kVec, kMask>(A, b, rq, a, c, M, xe, ua, S, cached);
   if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
   if (lane == 0) otok[a] = y;
+  return rc;
 }
 
 // sample_tail in a one-launch call: the request's chunk partials (row rr,
@@ -1910,7 +1921,11 @@ __global__ __launch_bounds__(64) void sv_ftail_kernel(Args A) {
 // max(0, p_a - q_a); the last workgroup of the request draws the token.
 // kFilt: p_a and q_a are the top-k / top-p filtered rows (weights below a
 // row's cut count as zero).
-template <int DT, bool kVec, bool kMask, bool kFilt>
+// kDecide: no tail launch came before; every workgroup of a request runs
+// the rule itself (one wave, sample_tail on the row pass's results: the
+// same decision in each), workgroup 0 writes the outputs or draws the bonus
+// token, and the pass goes on for requests that rejected.
+template <int DT, bool kVec, bool kMask, bool kFilt, bool kDecide>
 __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   constexpr int kCE = Chunk<DT>::kElems;
   __shared__ TailLds S;
@@ -1919,7 +1934,18 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   const int wi = (int)(blockIdx.x % (unsigned)A.wpr);
   const int b = (int)(blockIdx.x / (unsigned)A.wpr);
-  const Record rc = A.rec[b];
+  Record rc;
+  if constexpr (kDecide) {
+    __shared__ Record s_rc;
+    if (wave == 0) {
+      const Record r0 = sample_tail<DT, kVec, kExplicit, kMask>(A, b, S, wi == 0);
+      if (lane == 0) s_rc = r0;
+    }
+    __syncthreads();
+    rc = s_rc;
+  } else {
+    rc = A.rec[b];
+  }
   if (!rc.pending) return;
   const int a = rc.a;
   const float c = rc.c;
@@ -2133,6 +2159,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.tz_unif = A.tz_gath + (size_t)(B * rows);
   A.tag = 0;
   A.n_rowwg = 0;
+  A.no_tail = 0;
   A.filtered = 0;
   A.top_k = nullptr;
   A.top_p = nullptr;
@@ -2156,6 +2183,7 @@ void launch_pair(const Args& A, unsigned grid, hipStream_t st) {
     return;
   }
   SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask, false, false>), grid, st, A);
+  if (A.no_tail) return;                           // the residual pass runs the rule
   hipLaunchKernelGGL((sv_tail_kernel<MODE, DT, kVec, kMask>), dim3((unsigned)A.B), dim3(64), 0, st, A);
 }
 
@@ -2182,18 +2210,25 @@ void launch_rows(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t 
   else                        launch_rows_dt<MODE, kF32>(A, vec, mask, grid, st);
 }
 
-template <int DT>
-void launch_residual_dt(const Args& A, bool vec, unsigned grid, hipStream_t st) {
+// decide: the residual pass runs the rule itself (no tail launch before it).
+template <int DT, bool kDecide>
+void launch_residual_dd(const Args& A, bool vec, unsigned grid, hipStream_t st) {
   const bool mask = A.mask != nullptr, filt = A.filtered != 0;
   if (vec) {
-    if (filt)      SV_LAUNCH((sv_residual_kernel<DT, true, false, true>), grid, st, A);
-    else if (mask) SV_LAUNCH((sv_residual_kernel<DT, true, true, false>), grid, st, A);
-    else           SV_LAUNCH((sv_residual_kernel<DT, true, false, false>), grid, st, A);
+    if (filt)      SV_LAUNCH((sv_residual_kernel<DT, true, false, true, false>), grid, st, A);
+    else if (mask) SV_LAUNCH((sv_residual_kernel<DT, true, true, false, kDecide>), grid, st, A);
+    else           SV_LAUNCH((sv_residual_kernel<DT, true, false, false, kDecide>), grid, st, A);
   } else {
-    if (filt)      SV_LAUNCH((sv_residual_kernel<DT, false, false, true>), grid, st, A);
-    else if (mask) SV_LAUNCH((sv_residual_kernel<DT, false, true, false>), grid, st, A);
-    else           SV_LAUNCH((sv_residual_kernel<DT, false, false, false>), grid, st, A);
+    if (filt)      SV_LAUNCH((sv_residual_kernel<DT, false, false, true, false>), grid, st, A);
+    else if (mask) SV_LAUNCH((sv_residual_kernel<DT, false, true, false, kDecide>), grid, st, A);
+    else           SV_LAUNCH((sv_residual_kernel<DT, false, false, false, kDecide>), grid, st, A);
   }
+}
+
+template <int DT>
+void launch_residual_dt(const Args& A, bool vec, unsigned grid, hipStream_t st, bool decide) {
+  if (decide && A.filtered == 0) launch_residual_dd<DT, true>(A, vec, grid, st);
+  else                           launch_residual_dd<DT, false>(A, vec, grid, st);
 }
 
 // Filtered verification: the row pass, the select pass (one workgroup per
@@ -2218,9 +2253,10 @@ void launch_filtered(const Args& A, int dtype, bool vec, unsigned grid, hipStrea
   else                        launch_filtered_dt<MODE, kF32>(A, vec, grid, st);
 }
 
-void launch_residual(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st) {
-  if (dtype == SV_DTYPE_BF16) launch_residual_dt<kBF16>(A, vec, grid, st);
-  else                        launch_residual_dt<kF32>(A, vec, grid, st);
+void launch_residual(const Args& A, int dtype, bool vec, unsigned grid, hipStream_t st,
+                     bool decide = false) {
+  if (dtype == SV_DTYPE_BF16) launch_residual_dt<kBF16>(A, vec, grid, st, decide);
+  else                        launch_residual_dt<kF32>(A, vec, grid, st, decide);
 }
 
 // One early-exit round: the row pass over this round's rows, which ends in
@@ -2382,6 +2418,11 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
   if ((st = check_grid(wgs))) return st;
   plan_one_launch(A, explicit_q ? kExplicit : kOneHot, wgs);
   if (explicit_q) {
+    // two launches: the row pass, then the residual pass, whose workgroups
+    // run the rule themselves (no tail launch between); one launch: the row
+    // pass with its tail workgroups, then the residual pass
+    const bool decide = A.n_rowwg == 0;
+    A.no_tail = decide ? 1 : 0;
     launch_rows<kExplicit>(A, target->dtype, vec, (unsigned)wgs, s);
     if ((st = hip_status())) return st;
     // the residual pass streams one stop row pair per request
@@ -2389,7 +2430,7 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
     A2.n_rowwg = 0;
     A2.cpw = chunks_per_wg(B, A.n_chunk);
     A2.wpr = (A.n_chunk + A2.cpw - 1) / A2.cpw;
-    launch_residual(A2, target->dtype, vec, (unsigned)((int64_t)B * A2.wpr), s);
+    launch_residual(A2, target->dtype, vec, (unsigned)((int64_t)B * A2.wpr), s, decide);
   } else {
     launch_rows<kOneHot>(A, target->dtype, vec, (unsigned)wgs, s);
   }
