@@ -106,28 +106,33 @@ __device__ __forceinline__ void issue_chunk(const char* row, int64_t c0, ChunkRa
 // (c0 + (j * 64 + lane) * kPer) / 32 (a chunk starts on a word, a vector
 // never straddles one). Word indices past the row's last word are clamped
 // (those logits read as -inf anyway).
-struct MaskRaw { uint32_t w[kLoadsPerLane]; };
+struct MaskRaw { uint32_t w; };
 
+// One coalesced load of a chunk's bitmask: lane l holds word l of it (a
+// chunk starts on a word: 64 words for bf16, 32 for fp32, where lanes
+// 32..63 repeat lanes 0..31). Word indices past the row's last word are
+// clamped (those logits read as -inf anyway).
 template <int DT>
 __device__ __forceinline__ void issue_mask(const uint32_t* mrow, int64_t c0, int n_words, MaskRaw& m) {
-  constexpr int kPer = Elem<DT>::kPerVec;
-#pragma unroll
-  for (int j = 0; j < kLoadsPerLane; ++j) {
-    const int64_t wi = (c0 + (int64_t)(j * 64 + (threadIdx.x & 63)) * kPer) >> 5;
-    m.w[j] = mrow[wi < n_words ? wi : n_words - 1];
-  }
+  constexpr int kWords = Chunk<DT>::kElems / 32;
+  const int64_t wi = (c0 >> 5) + ((threadIdx.x & 63) % kWords);
+  m.w = mrow[wi < n_words ? wi : n_words - 1];
 }
 
-// Disallowed logits of a chunk become -inf in the packed words: bit k of
-// the lane's vector j (after the shift below) allows logit k of it. Per
-// 32-bit word one bitfield insert against the -inf pattern.
+// Disallowed logits of a chunk become -inf in the packed words. The kPer
+// bits of the lane's vector j sit in word (j * 64 + lane) * kPer / 32 of the
+// chunk's mask, fetched from the lane that loaded it; after the shift bit k
+// allows logit k of the vector. Per 32-bit word one bitfield insert against
+// the -inf pattern. Every lane of the wave must be active.
 template <int DT>
 __device__ __forceinline__ void apply_mask(ChunkRaw& r, const MaskRaw& m) {
   constexpr int kPer = Elem<DT>::kPerVec;
-  const uint32_t shift = ((threadIdx.x & 63) * kPer) & 31;
+  const int lane = threadIdx.x & 63;
+  const uint32_t shift = (lane * kPer) & 31;
 #pragma unroll
   for (int j = 0; j < kLoadsPerLane; ++j) {
-    const uint32_t bits = m.w[j] >> shift;
+    const int src = ((j * 64 + lane) * kPer) >> 5;   // < 64: a chunk's mask has at most 64 words
+    const uint32_t bits = (uint32_t)__shfl((int)m.w, src) >> shift;
     auto blend = [bits](uint32_t& w, int q) {
       uint32_t keep;
       if constexpr (DT == kF32) {
