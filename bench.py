@@ -113,6 +113,41 @@ def traffic_record(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def read_ceiling(copies, torch, steps: int) -> dict:
+    """Times the read-only probe (draft_verification_05_amd/probe) over the
+    logits copies: GB/s of one full read of the same bytes (rounded down to
+    whole 4 KiB chunks)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "draft_verification_05_amd", "libsvprobe.so"))
+    lib.sv_probe_read.restype = ctypes.c_int
+    lib.sv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sv_probe_workgroups.restype = ctypes.c_int
+    lib.sv_probe_workgroups.argtypes = [ctypes.c_size_t]
+    nbytes = copies[0].numel() * copies[0].element_size() // 4096 * 4096
+    if nbytes == 0:
+        return {"kernel": "read-only probe", "bytes": 0, "us": None, "gbps": None}
+    dev = copies[0].device
+    out = torch.empty(lib.sv_probe_workgroups(nbytes), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    iters = max(10, min(steps, 100))
+
+    def run(i):
+        rc = lib.sv_probe_read(copies[i % len(copies)].data_ptr(), nbytes, out.data_ptr(), stream)
+        if rc:
+            raise RuntimeError(f"sv_probe_read failed ({rc})")
+    for i in range(len(copies)):
+        run(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(iters):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    return {"kernel": "read-only probe over the same logits bytes (4 KiB runs, 16-byte loads)",
+            "bytes": nbytes, "us": round(ms * 1e3, 2), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(wl, seconds: float):
     import numpy as np
     import oracle
@@ -121,7 +156,12 @@ def cpu_baseline(wl, seconds: float):
     t0 = time.perf_counter()
     n = 0
     while n < B and (time.perf_counter() - t0) < seconds:
-        if rg is None:
+        if wl["mode"] == "greedy":
+            oracle.spec_verify_greedy(wl["target"][n:n + 1], wl["draft_tokens"][n:n + 1], wl["dtype"])
+        elif wl["mode"] == "tree":
+            oracle.spec_verify_tree(wl["target"][n:n + 1], wl["draft_tokens"][n:n + 1], wl["parents"],
+                                    wl["dtype"])
+        elif rg is None:
             oracle.spec_verify_sample(wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"],
                                       wl["seeds"], wl["offset"], target_dtype=wl["dtype"], requests=[n],
                                       bitmask=wl.get("bitmask"), top_k=wl.get("top_k"),
@@ -138,7 +178,7 @@ def cpu_baseline(wl, seconds: float):
     sample_bytes = algorithmic_bytes(wl) * n / B
     return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} of {B} requests of {wl['name']} "
-                      f"({int(rg['ks'][:n].sum()) + n if rg is not None else n * (wl['K'] + 1)} logits rows), "
+                      f"({int(rg['ks'][:n].sum()) + n if rg is not None else n * len(wl['parents']) if wl['mode'] == 'tree' else n * (wl['K'] + 1)} logits rows), "
                       f"{dt:.1f} s, single thread",
             "us_per_step_equiv": round(dt / n * B * 1e6, 1)}
 
@@ -333,6 +373,11 @@ def main():
         ends[i].record()
     torch.cuda.synchronize()
 
+    # Read-stream ceiling: a read-only probe kernel (4 KiB runs, 16-byte
+    # loads, nothing else) over the same logits bytes, rotating over the same
+    # copies, timed the same way.
+    stream = read_ceiling(copies, torch, args.steps)
+
     per_launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     mean_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
     ms_per_step = region_ms / args.steps
@@ -388,6 +433,12 @@ def main():
                      "launch_us_mean": round(mean_launch_ms * 1e3, 2),
                      "launch_us_p10": round(per_launch_ms[len(per_launch_ms) // 10] * 1e3, 2),
                      "launch_us_p90": round(per_launch_ms[(9 * len(per_launch_ms)) // 10] * 1e3, 2)},
+        # the probe reads the target logits; with draft logits the call reads
+        # more than that, so no ratio is given
+        "stream_ceiling": dict(stream, call_logical_gbps=round(
+            copies[0].numel() * copies[0].element_size() / (ms_per_step * 1e-3) / 1e9, 1),
+            call_frac=round(copies[0].numel() * copies[0].element_size() / (ms_per_step * 1e-3) / 1e9
+                            / stream["gbps"], 4) if stream["gbps"] and draft is None else None),
         "accept_len_hist": np.bincount(accept, minlength=(K + 2) if mode != "tree" else 5).tolist(),
         "source_digest": source_digest(),
     }
