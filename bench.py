@@ -48,6 +48,9 @@ FILTER_BASE = {"c3_topp": ("c3_onehot", 0, 0.95), "c2_topp": ("c2_stoch", 0, 0.9
 # calls that ask for tokens and accept lengths only (no p / q outputs), as a
 # serving engine would
 TOKENS_ONLY = {"c3_topp_tok"}
+# one GPU's share of a workload whose requests are split over several GPUs
+# (requests are independent: each GPU verifies B / G of them, no exchange)
+SHARD_BASE = {"c3_shard8": ("c3_onehot", 8)}
 
 
 def algorithmic_bytes(wl, rejected=None) -> int:
@@ -207,7 +210,8 @@ def main():
                          "(C3 with a grammar bitmask allowing each token w.p. 1/2); c3_lazy / c2_lazy "
                          "run C3 / C2 through early-exit verification; c3_topp / c2_topp "
                          "add a top_p 0.95 filter; c3_topp_tok is c3_topp returning tokens "
-                         "and accept lengths only")
+                         "and accept lengths only; c3_shard8 is one GPU's share of C3 split "
+                         "over 8 GPUs (B=32)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -247,6 +251,10 @@ def main():
     elif masked:
         from workloads import make_masked
         wl = make_masked(MASKED_BASE[args.workload], data_seed=0)
+    elif args.workload in SHARD_BASE:
+        base, g = SHARD_BASE[args.workload]
+        full = make(base, data_seed=0)
+        wl = dict(make(base, data_seed=0, B=full["B"] // g), name=args.workload)
     else:
         wl = make(args.workload, data_seed=0)
     lib = sv.load_library()

@@ -779,3 +779,10 @@ def test_filtered_tokens_only_equals_full_outputs():
         np.testing.assert_array_equal(t1.cpu().numpy(), t2.cpu().numpy())
         hist = np.bincount(l2.cpu().numpy(), minlength=wl["K"] + 2).tolist()
         print(f"[parity] tokens-only {name}: identical, accept_len histogram {hist}", flush=True)
+
+
+def test_small_batch_long_rows():
+    """Small launches of long rows take four-chunk runs per wave: one GPU's
+    share of C3 split over 8 GPUs (B=32), and greedy rows of 127 chunks at B=16."""
+    check_sample(make("c3_onehot", data_seed=2, B=32), "c3 B=32 (8-way shard)")
+    check_greedy(make("c4_greedy", data_seed=3, B=16), "c4 B=16")
