@@ -33,7 +33,11 @@
  *    per-process counter), so a later call never mistakes an earlier
  *    call's words for its own and nothing needs clearing between calls.
  *    Setting SPECVERIFY_ONE_LAUNCH=0 in the environment makes every call
- *    use two launches (the same results up to fp32 summation order).
+ *    use two launches (the same results up to fp32 summation order). The
+ *    wait for those words is bounded (2^20 polls, each at least one trip to
+ *    memory); a request whose words never arrive, which a working device
+ *    does not produce, is refused (accept length 0, tokens -1) rather than
+ *    left hanging.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
