@@ -442,11 +442,12 @@ def main():
                      "launch_us_p10": round(per_launch_ms[len(per_launch_ms) // 10] * 1e3, 2),
                      "launch_us_p90": round(per_launch_ms[(9 * len(per_launch_ms)) // 10] * 1e3, 2)},
         # the probe reads the target logits; with draft logits the call reads
-        # more than that, so no ratio is given
+        # more than that, and early exit reads less, so no ratio is given
         "stream_ceiling": dict(stream, call_logical_gbps=round(
             copies[0].numel() * copies[0].element_size() / (ms_per_step * 1e-3) / 1e9, 1),
             call_frac=round(copies[0].numel() * copies[0].element_size() / (ms_per_step * 1e-3) / 1e9
-                            / stream["gbps"], 4) if stream["gbps"] and draft is None else None),
+                            / stream["gbps"], 4) if stream["gbps"] and draft is None and not lazy
+            else None),
         "accept_len_hist": np.bincount(accept, minlength=(K + 2) if mode != "tree" else 5).tolist(),
         "source_digest": source_digest(),
     }
