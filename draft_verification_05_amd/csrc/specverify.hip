@@ -13,11 +13,13 @@
 //   tail       one wave per request merges that request's partials and
 //              runs the rule: the acceptance scan and the draw (the row
 //              pass draws the Philox uniforms). Greedy, tree and one-hot
-//              calls (and small calls with draft logits) run it in the same
-//              launch: one tail workgroup per request after the row pass's
-//              workgroups in the grid, fed through tagged slots (see the
-//              one-launch hand-off below). Otherwise it is a second launch,
-//              and the launch boundary is the only synchronisation.
+//              calls run it in the same launch: one tail workgroup per
+//              request after the row pass's workgroups in the grid, fed
+//              through tagged slots (see the one-launch hand-off below).
+//              With draft logits the residual pass's workgroups run it.
+//              Otherwise (shapes the one-launch tail cannot hold) it is a
+//              second launch, and the launch boundary is the only
+//              synchronisation.
 //   draw       the chunk sums locate the chunk that holds u * Z, and one
 //              workgroup scan over that single re-read chunk finds the
 //              token. With one-hot drafts the row pass already leaves the
@@ -2191,9 +2193,11 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
 // tail workgroup per request, in one grid.
 template <int MODE, int DT, bool kVec, bool kMask>
 void launch_pair(const Args& A, unsigned grid, hipStream_t st) {
-  if (A.n_rowwg > 0) {
-    SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask, false, true>), grid + (unsigned)A.B, st, A);
-    return;
+  if constexpr (MODE != kExplicit) {              // draft logits: never one launch
+    if (A.n_rowwg > 0) {
+      SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask, false, true>), grid + (unsigned)A.B, st, A);
+      return;
+    }
   }
   SV_LAUNCH((sv_rows_kernel<MODE, DT, kVec, kMask, false, false>), grid, st, A);
   if (A.no_tail) return;                           // the residual pass runs the rule
@@ -2319,17 +2323,13 @@ bool one_launch_fits(const Args& A, int mode) {
   return (A.rows + 64 / G - 1) / (64 / G) <= 8;
 }
 
-// Marks A as a one-launch call when it fits. With draft logits a residual
-// pass follows anyway, and one launch measured slower once the row pass
-// fills the chip (B=64, K=3, V=32000: 28.5 us against 23.4 us) but faster
-// when it is a handful of workgroups (B=1, K=1, V=1000: 9.8 against
-// 10.9 us), so explicit drafts take one launch only up to kFusedExplicitWgs
-// row-pass workgroups.
-constexpr int64_t kFusedExplicitWgs = 1024;
-
+// Marks A as a one-launch call when it fits. Calls with draft logits keep
+// two launches: a residual pass follows anyway and runs the rule itself,
+// which measured faster at every size (B=64, K=3, V=32000: 19.8 against
+// 28.5 us in one launch; B=1, K=1, V=1000: 8.9 against 10.4 us).
 void plan_one_launch(Args& A, int mode, int64_t row_wgs) {
+  if (mode == kExplicit) return;
   if (!one_launch_fits(A, mode) || row_wgs + A.B > (int64_t)(UINT32_MAX / kThreads)) return;
-  if (mode == kExplicit && row_wgs > kFusedExplicitWgs) return;
   A.n_rowwg = (int)row_wgs;
   A.tag = next_tag();
 }
@@ -2444,9 +2444,8 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
   if ((st = check_grid(wgs))) return st;
   plan_one_launch(A, explicit_q ? kExplicit : kOneHot, wgs);
   if (explicit_q) {
-    // two launches: the row pass, then the residual pass, whose workgroups
-    // run the rule themselves (no tail launch between); one launch: the row
-    // pass with its tail workgroups, then the residual pass
+    // the row pass, then the residual pass, whose workgroups run the rule
+    // themselves (no tail launch between)
     const bool decide = A.n_rowwg == 0;
     A.no_tail = decide ? 1 : 0;
     launch_rows<kExplicit>(A, target->dtype, vec, (unsigned)wgs, s);

@@ -56,6 +56,8 @@ def check_both_paths(wl, name):
           flush=True)
 
 
+# Calls with draft logits (c2, c1) take the row pass and a residual pass that
+# runs the rule on either setting; they stay here as parity cases for that path.
 ONE_LAUNCH_SAMPLE = [
     ("c3-onehot-bf16", "c3_onehot", dict(B=48, V=3 * 8192 + 1232)),
     ("c3-onehot-scalar-path", "c3_onehot", dict(B=24, V=2 * 8192 + 777)),
