@@ -689,13 +689,14 @@ __device__ Record sample_tail(const Args& A, int b, TailLds& S, bool write_out =
   return rc;
 }
 
-// sample_tail in a one-launch call: the request's chunk partials (row rr,
+// sample_tail in a one-launch call (one-hot drafts; calls with draft logits
+// decide in the residual pass): the request's chunk partials (row rr,
 // chunk s in lane s % 64, load rr * npl + s / 64), gathered logits and
 // uniforms come from tagged slots, loaded together and polled until all
 // carry this call's tag; rows merge from the chunk partials, and the draw
 // locates its chunk among the partials already in registers. The host
 // admits a call only when rows * npl <= kFusedQ.
-template <int DT, bool kVec, int MODE, bool kMask>
+template <int DT, bool kVec, bool kMask>
 __device__ void fused_sample_tail(const Args& A, int b) {
   __shared__ float s_rowM[kFusedQ], s_rowS[kFusedQ];
   const int lane = threadIdx.x & 63;
@@ -718,13 +719,11 @@ __device__ void fused_sample_tail(const Args& A, int b) {
   }
   const bool need_u = !refused && lane <= K;
   const bool need_g = !refused && valid;
-  const bool need_d = MODE == kExplicit && need_g;
-  uint64_t pm[kFusedQ], ps[kFusedQ], hx = 0ull, hd = 0ull, hu0 = 0ull, hu1 = 0ull;
+  uint64_t pm[kFusedQ], ps[kFusedQ], hx = 0ull, hu0 = 0ull, hu1 = 0ull;
 #pragma unroll
   for (int q = 0; q < kFusedQ; ++q) { pm[q] = 0ull; ps[q] = 0ull; }
-  // the last chunk of the last live row belongs to the request's last workgroup
-  const int r_last = (MODE == kExplicit && K > 0) ? R + K - 1 : K;
-  bool got = refused || wait_tag(A.tz_part + 2 * ((rowg0 + r_last) * nch + nch - 1) + 1, tag);
+  // the last chunk of the last live row (row K) belongs to the request's last workgroup
+  bool got = refused || wait_tag(A.tz_part + 2 * ((rowg0 + K) * nch + nch - 1) + 1, tag);
   for (int spin = 0; got && !refused; ++spin) {
     bool miss = false;
 #pragma unroll
@@ -737,14 +736,12 @@ __device__ void fused_sample_tail(const Args& A, int b) {
       }
     }
     if (need_g && !has_tag(hx, tag)) hx = get_tag(A.tz_gath + rowg0 + lane);
-    if (need_d && !has_tag(hd, tag)) hd = get_tag(A.tz_gath + rowg0 + R + lane);
     if (need_u) {
       const uint64_t* us = A.tz_unif + 2 * ((int64_t)b * R + lane);
       if (!has_tag(hu0, tag)) hu0 = get_tag(us);
       if (!has_tag(hu1, tag)) hu1 = get_tag(us + 1);
     }
     miss |= need_g && !has_tag(hx, tag);
-    miss |= need_d && !has_tag(hd, tag);
     miss |= need_u && !(has_tag(hu0, tag) && has_tag(hu1, tag));
     if (__ballot(miss) == 0ull) break;
     if (spin >= kSpinLimit) got = false;
@@ -756,10 +753,7 @@ __device__ void fused_sample_tail(const Args& A, int b) {
     if (lane <= K) otok[lane] = -1;
     if (lane < K && A.out_p) A.out_p[rq.x0 + lane] = 0.f;
     if (lane < K && A.out_q) A.out_q[rq.x0 + lane] = 0.f;
-    if (lane == 0) {
-      A.out_len[b] = 0;
-      if (MODE == kExplicit) A.rec[b].pending = 0;
-    }
+    if (lane == 0) A.out_len[b] = 0;
     return;
   }
   // per-row (max, sum): a lane's npl partials of the row, then the wave
@@ -775,49 +769,27 @@ __device__ void fused_sample_tail(const Args& A, int b) {
   __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
   const float c = kLog2e / T;
   const float uacc = tag_val(hu0), usmp = tag_val(hu1);
-  const float lx = need_g ? tag_val(hx) : kNegInf, ld = need_d ? tag_val(hd) : kNegInf;
-  float p = 0.f, q = 0.f, Mx = kNegInf, lp = kNegInf, lq = kNegInf;
+  const float lx = need_g ? tag_val(hx) : kNegInf;
+  float p = 0.f, q = 0.f, Mx = kNegInf;
   if (lane < K) {
-    if (MODE == kOneHot) {
-      // row `lane`'s sums leave x out: add its own term back for p(x)
-      const float Mi = s_rowM[lane], Si = s_rowS[lane];
-      Mx = fmaxf(Mi, lx * c);
-      const float Sx = (Mi == kNegInf) ? 0.f : Si * fast_exp2(Mi - Mx);
-      const float e = (valid && Mx != kNegInf) ? fast_exp2(fmaf(lx, c, -Mx)) : 0.f;
-      const float St = Sx + e;
-      p = St > 0.f ? e / St : 0.f;
-      q = valid ? 1.f : 0.f;
-    } else {
-      const float Mp = s_rowM[lane], Sp = s_rowS[lane];
-      const float Mq = s_rowM[R + lane], Sq = s_rowS[R + lane];
-      const float dp = fmaf(lx, c, -Mp), dq = fmaf(ld, c, -Mq);
-      p = (valid && Sp > 0.f) ? fast_exp2(dp) / Sp : 0.f;
-      q = (valid && Sq > 0.f) ? fast_exp2(dq) / Sq : 0.f;
-      lp = (valid && Sp > 0.f) ? dp - __log2f(Sp) : kNegInf;
-      lq = (valid && Sq > 0.f) ? dq - __log2f(Sq) : kNegInf;
-    }
+    // row `lane`'s sums leave x out: add its own term back for p(x)
+    const float Mi = s_rowM[lane], Si = s_rowS[lane];
+    Mx = fmaxf(Mi, lx * c);
+    const float Sx = (Mi == kNegInf) ? 0.f : Si * fast_exp2(Mi - Mx);
+    const float e = (valid && Mx != kNegInf) ? fast_exp2(fmaf(lx, c, -Mx)) : 0.f;
+    const float St = Sx + e;
+    p = St > 0.f ? e / St : 0.f;
+    q = valid ? 1.f : 0.f;
     if (A.out_p) A.out_p[rq.x0 + lane] = p;
     if (A.out_q) A.out_q[rq.x0 + lane] = q;
   }
-  const bool accept = MODE == kOneHot ? (uacc * q < p) : (__log2f(uacc) + lq < lp);
+  const bool accept = uacc * q < p;
   const int rej = first_lane(lane < K && !accept);
   const int a = rej < 0 ? K : rej;
   if (lane <= K && lane != a) otok[lane] = lane < a ? x : -1;
   if (lane == 0) A.out_len[b] = a + 1;
   const float ua = lane_f(usmp, a);
-  if (MODE == kExplicit) {
-    if (a < K) {
-      if (lane == 0) {
-        Record rc;
-        rc.a = a; rc.pending = 1; rc.c = c; rc.u = ua;
-        rc.Mp = s_rowM[a]; rc.Sp = s_rowS[a]; rc.Mq = s_rowM[R + a]; rc.Sq = s_rowS[R + a];
-        A.rec[b] = rc;
-      }
-      return;
-    }
-    if (lane == 0) A.rec[b].pending = 0;
-  }
-  const bool resid = (MODE == kOneHot && a < K);
+  const bool resid = a < K;
   const float M = resid ? lane_f(Mx, a) : s_rowM[a];
   const int xe = resid ? lane_i(x, a) : -1;
   // chunk s of row a sits in this lane's load a * npl + s / 64 (s = lane mod 64)
@@ -1237,8 +1209,10 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
     if (blockIdx.x >= (unsigned)A.n_rowwg) {      // a tail workgroup: one wave does the work
       if (wave == 0) {
         const int bt = (int)(blockIdx.x - (unsigned)A.n_rowwg);
-        if constexpr (MODE == kOneHot || MODE == kExplicit) {
-          fused_sample_tail<DT, kVec, MODE, kMask>(A, bt);
+        if constexpr (MODE == kOneHot) {
+          fused_sample_tail<DT, kVec, kMask>(A, bt);
+        } else if constexpr (MODE == kExplicit) {
+          static_assert(MODE != kExplicit, "calls with draft logits never take one launch");
         } else {
           __shared__ int s_g[SV_MAX_TREE_NODES];
           if constexpr (MODE == kGreedy) greedy_tail<true>(A, bt, s_g);
