@@ -12,6 +12,9 @@ how many draws were that close to a boundary at all.
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -52,6 +55,36 @@ def new_report():
                 max_p_err=0.0, max_q_err=0.0)
 
 
+def near_cut_invalid(wl, b, tok, n, top_k, top_p, draft_dtype):
+    """Checks a request whose top-p cut lies within FILTER_TOL of a cumulative
+    mass, where the library may keep one value more or fewer than the oracle:
+    the accepted prefix must be the drafts, the rest -1, and the drawn token
+    must lie in the larger of the two candidate kept sets of the row it was
+    drawn from (the set kept at top_p + FILTER_TOL), and differ from a
+    rejected one-hot draft. Returns what is wrong, or "" when valid."""
+    K, V = wl["K"], wl["V"]
+    if not 1 <= n <= K + 1:
+        return f"accept_len {n}"
+    a = n - 1
+    if not np.array_equal(tok[:a], wl["draft_tokens"][b, :a]):
+        return "accepted prefix differs from the drafts"
+    if np.any(tok[a + 1:] != -1):
+        return "padding"
+    y = int(tok[a])
+    if not 0 <= y < V:
+        return f"token {y} out of range"
+    T = float(wl["temperature"][b])
+    tk = 0 if top_k is None else int(top_k[b])
+    tp = 1.0 if top_p is None else float(top_p[b])
+    row = oracle.logits_f64(wl["target"][b, a], wl["dtype"])
+    keep_large, _ = oracle.filter_keep(row, T, tk, min(tp + FILTER_TOL, 1.0))
+    if not keep_large[y]:
+        return f"token {y} outside both candidate kept sets"
+    if wl.get("draft") is None and a < K and y == int(wl["draft_tokens"][b, a]):
+        return "the rejected one-hot draft was drawn again"
+    return ""
+
+
 def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32", report=None,
                     bitmask=None, lazy=False, top_k=None, top_p=None):
     """Run the oracle on `requests` and fold the comparison into a report dict.
@@ -76,8 +109,9 @@ def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32"
         tr = traces[b]
         if tr.get("filter_margin", np.inf) < FILTER_TOL:
             rep["filter_near"] += 1
-            if not (1 <= g_len[b] <= K + 1 and np.all((g_tok[b, :g_len[b]] >= 0) & (g_tok[b, :g_len[b]] < V))):
-                rep["mismatches"].append((b, "invalid output near a top-p cut", g_tok[b].tolist()))
+            bad = near_cut_invalid(wl, b, g_tok[b], int(g_len[b]), top_k, top_p, draft_dtype)
+            if bad:
+                rep["mismatches"].append((b, "invalid output near a top-p cut: " + bad, g_tok[b].tolist()))
             continue
         n = min(max(int(g_len[b]), 0), K) if lazy else K
         if n:
@@ -135,7 +169,23 @@ def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32"
     return rep
 
 
+def record_report(rep, name):
+    """Appends the report (counts only) as one JSON line to the file named by
+    SV_PARITY_LOG, when that variable is set."""
+    path = os.environ.get("SV_PARITY_LOG")
+    if not path:
+        return
+    row = dict(name=name, **{k: rep[k] for k in ("requests", "exact", "refused", "accept_div", "select_div",
+                                                  "filter_near")},
+               near_accept={str(t): int(v) for t, v in rep["near_accept"].items()},
+               near_select={str(t): int(v) for t, v in rep["near_select"].items()},
+               max_p_err=rep["max_p_err"], max_q_err=rep["max_q_err"], mismatches=len(rep["mismatches"]))
+    with open(path, "a") as f:
+        f.write(json.dumps(row) + "\n")
+
+
 def assert_report(rep, name):
+    record_report(rep, name)
     print(f"[parity] {name}: requests={rep['requests']} exact={rep['exact']} refused={rep['refused']} "
           f"accept_div={rep['accept_div']} select_div={rep['select_div']} "
           f"filter_near={rep['filter_near']} "

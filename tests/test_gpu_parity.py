@@ -1,8 +1,10 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
 
-Reduced sizes span several 8192-logit segments plus a ragged tail, in both
-the 128-bit and the scalar (misaligned) load paths; the five named workloads
-run at their full sizes in the launch configuration the benchmark times.
+Reduced sizes span several 4 KiB chunks (2048 bf16 or 1024 fp32 logits) plus
+a ragged tail, in both the 128-bit and the scalar (misaligned) load paths;
+the five named workloads run at their full sizes in the launch configuration
+the benchmark times. With SV_PARITY_LOG set, every report's counts are
+appended to that file as JSON lines.
 """
 import numpy as np
 import pytest
