@@ -18,9 +18,15 @@ import ctypes
 import glob
 import hashlib
 import json
+import multiprocessing
 import os
 import sys
 import time
+
+# The CPU baseline's worker processes each run one thread of numpy (BLAS
+# threads = 1); set before numpy is imported anywhere in this process.
+for _v in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = "1"
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -151,39 +157,185 @@ def read_ceiling(copies, torch, steps: int) -> dict:
             "bytes": nbytes, "us": round(ms * 1e3, 2), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(wl, seconds: float):
+# The workload the CPU-baseline workers see: set before the pool forks them,
+# so each inherits it without a copy through a pipe.
+_CPU_WL = None
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers() -> int:
+    """Worker processes for the CPU baseline: every core the process may use,
+    at most 16 (a GPU machine's share of its host for one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, os.cpu_count() or n, 16))
+
+
+def oracle_request(wl, n, offset):
+    """The oracle on request n alone at `offset` (what one CPU unit of work is).
+    Returns the oracle's full output tuple (only row n filled)."""
     import numpy as np
     import oracle
-    B = wl["B"]
+    if wl["mode"] == "greedy":
+        return oracle.spec_verify_greedy(wl["target"][n:n + 1], wl["draft_tokens"][n:n + 1], wl["dtype"])
+    if wl["mode"] == "tree":
+        return oracle.spec_verify_tree(wl["target"][n:n + 1], wl["draft_tokens"][n:n + 1], wl["parents"],
+                                       wl["dtype"])
     rg = wl.get("ragged")
+    if rg is None:
+        return oracle.spec_verify_sample(wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"],
+                                         wl["seeds"], offset, target_dtype=wl["dtype"], requests=[n],
+                                         keep_trace=True, bitmask=wl.get("bitmask"),
+                                         top_k=wl.get("top_k"), top_p=wl.get("top_p"))
+    c0, c1 = int(rg["cu"][n]), int(rg["cu"][n + 1])       # request n as a one-request ragged batch
+    return oracle.spec_verify_sample_ragged(
+        rg["target_rows"][c0 + n: c1 + n + 1], None, np.array([0, c1 - c0], np.int32),
+        rg["draft_tokens"][c0:c1], wl["temperature"][n:n + 1], wl["seeds"][n:n + 1], offset,
+        k_max=wl["K"], target_dtype=wl["dtype"])
+
+
+def request_rows(wl, n) -> int:
+    """Logits rows request n consults (the unit the sample is stated in)."""
+    if wl["mode"] == "tree":
+        return len(wl["parents"])
+    rg = wl.get("ragged")
+    k = int(rg["ks"][n]) if rg is not None else wl["K"]
+    return k + 1 + (k if wl.get("draft") is not None else 0)
+
+
+def _cpu_shard(args):
+    """One worker: requests lo, lo + 1, ... < hi, round and round, until
+    `seconds` have passed. Returns the requests done and the time taken."""
+    lo, hi, seconds, offset = args
     t0 = time.perf_counter()
-    n = 0
-    while n < B and (time.perf_counter() - t0) < seconds:
-        if wl["mode"] == "greedy":
-            oracle.spec_verify_greedy(wl["target"][n:n + 1], wl["draft_tokens"][n:n + 1], wl["dtype"])
-        elif wl["mode"] == "tree":
-            oracle.spec_verify_tree(wl["target"][n:n + 1], wl["draft_tokens"][n:n + 1], wl["parents"],
-                                    wl["dtype"])
-        elif rg is None:
-            oracle.spec_verify_sample(wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"],
-                                      wl["seeds"], wl["offset"], target_dtype=wl["dtype"], requests=[n],
-                                      bitmask=wl.get("bitmask"), top_k=wl.get("top_k"),
-                                      top_p=wl.get("top_p"))
-        else:                                       # request n alone, as a one-request ragged batch
-            c0, c1 = int(rg["cu"][n]), int(rg["cu"][n + 1])
-            oracle.spec_verify_sample_ragged(
-                rg["target_rows"][c0 + n: c1 + n + 1], None,
-                np.array([0, c1 - c0], np.int32), rg["draft_tokens"][c0:c1],
-                wl["temperature"][n:n + 1], wl["seeds"][n:n + 1], wl["offset"], k_max=wl["K"],
-                target_dtype=wl["dtype"])
-        n += 1
-    dt = time.perf_counter() - t0
-    sample_bytes = algorithmic_bytes(wl) * n / B
-    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} of {B} requests of {wl['name']} "
-                      f"({int(rg['ks'][:n].sum()) + n if rg is not None else n * len(wl['parents']) if wl['mode'] == 'tree' else n * (wl['K'] + 1)} logits rows), "
-                      f"{dt:.1f} s, single thread",
-            "us_per_step_equiv": round(dt / n * B * 1e6, 1)}
+    done = 0
+    while time.perf_counter() - t0 < seconds:
+        oracle_request(_CPU_WL, lo + done % (hi - lo), offset)
+        done += 1
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(wl, seconds: float, pool, offset: int, gpu_out):
+    """The fp64 oracle (untuned) on the host cores, on a bounded sample of the
+    same workload: (i) one thread in this process, whose requests are also
+    compared with the GPU's outputs of the last call at the same offset;
+    (ii) `pool`'s worker processes, requests sharded between them. Each leg
+    runs about `seconds`; throughput is the bytes of the requests done
+    (the step's algorithmic bytes pro rata) over the leg's wall time."""
+    import numpy as np
+    B = wl["B"]
+    per_req = algorithmic_bytes(wl) / B
+    # (i) one thread: requests 0, 1, ... (round and round when the batch is
+    # quick), the first pass kept for the parity counts
+    outs = []
+    n1 = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        o = oracle_request(wl, n1 % B, offset)
+        if n1 < B:
+            outs.append(o)
+        n1 += 1
+    dt1 = time.perf_counter() - t0
+    rows1 = sum(request_rows(wl, n % B) for n in range(n1))
+    single = {"value": round(per_req * n1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+              "sample": f"{n1} requests in order from request 0 of {B} ({rows1} logits rows), "
+                        f"{dt1:.1f} s",
+              "us_per_step_equiv": round(dt1 / n1 * B * 1e6, 1)}
+    # (ii) worker processes, a contiguous shard of requests each
+    workers = pool._processes
+    shard = (B + workers - 1) // workers
+    jobs = [(w * shard, min(B, (w + 1) * shard), seconds, offset) for w in range(workers) if w * shard < B]
+    t0 = time.perf_counter()
+    res = pool.map(_cpu_shard, jobs)
+    dtn = time.perf_counter() - t0
+    done = sum(r[0] for r in res)
+    rowsn = sum(request_rows(wl, j[0] + k % (j[1] - j[0])) for j, r in zip(jobs, res) for k in range(r[0]))
+    multi = {"value": round(per_req * done / dtn / 1e9, 4), "unit": "GB/s", "cores": len(jobs),
+             "kind": "oracle", "cpu_model": cpu_model(), "host_cores": os.cpu_count(),
+             "sample": f"{done} requests of the {B} of {wl['name']} ({rowsn} logits rows), sharded "
+                       f"over {len(jobs)} worker processes (one numpy thread each), {dtn:.1f} s wall",
+             "us_per_step_equiv": round(dtn / max(done, 1) * B * 1e6, 1),
+             "single_thread": single}
+    multi["parity"] = parity_of_sample(wl, outs, offset, gpu_out)
+    return multi
+
+
+def parity_of_sample(wl, outs, offset, gpu_out):
+    """The GPU's last call against the oracle on the single-thread leg's
+    requests: the sound parity counts for sampling (tests/parity.py: exact,
+    divergences only at draws within 1e-5 of a threshold, band counts at
+    1e-5 / 1e-6 / 1e-7, mismatches), exact-match counts for greedy and tree."""
+    import numpy as np
+    n = len(outs)
+    g_tok, g_len = gpu_out["tokens"], gpu_out["accept_len"]
+    if wl["mode"] in ("greedy", "tree"):
+        same = sum(int(np.array_equal(o[0][0], g_tok[i]) and o[1][0] == g_len[i]) for i, o in enumerate(outs))
+        return {"requests": n, "exact": same, "mismatches": n - same, "offset": offset}
+    if wl.get("ragged") is not None:
+        same = 0
+        for i, o in enumerate(outs):
+            k = int(wl["ragged"]["ks"][i])
+            same += int(o[1][0] == g_len[i] and np.array_equal(o[0][0][:k + 1], g_tok[i][:k + 1]))
+        return {"requests": n, "identical": same, "offset": offset,
+                "note": "ragged: requests identical to the oracle (no near-threshold classification)"}
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import classify_sample
+    B, K = wl["B"], wl["K"]
+    o_tok = np.full((B, K + 1), -1, np.int32)
+    o_len = np.zeros(B, np.int32)
+    o_p = np.zeros((B, K))
+    o_q = np.zeros((B, K))
+    traces = {}
+    for i, o in enumerate(outs):
+        o_tok[i], o_len[i], o_p[i], o_q[i] = o[0][i], o[1][i], o[2][i], o[3][i]
+        traces.update(o[4])
+    rep = classify_sample(dict(wl, offset=offset), g_tok, g_len, gpu_out.get("p"), gpu_out.get("q"),
+                          requests=range(n), bitmask=wl.get("bitmask"), lazy=gpu_out.get("lazy", False),
+                          top_k=wl.get("top_k"), top_p=wl.get("top_p"),
+                          oracle_out=(o_tok, o_len, o_p, o_q, traces))
+    return {"requests": rep["requests"], "exact": rep["exact"], "refused": rep["refused"],
+            "accept_div": rep["accept_div"], "select_div": rep["select_div"],
+            "filter_near": rep["filter_near"],
+            "near_accept": {str(t): int(v) for t, v in rep["near_accept"].items()},
+            "near_select": {str(t): int(v) for t, v in rep["near_select"].items()},
+            "max_abs_dp": rep["max_p_err"], "max_abs_dq": rep["max_q_err"],
+            "mismatches": len(rep["mismatches"]), "offset": offset}
+
+
+def launches_per_call(wl, workload, lazy, filt, explicit) -> int:
+    """Kernel launches one call makes (the library's launch plan for these
+    shapes: one-launch calls for one-hot, greedy and tree batches up to 1024
+    requests whose rule fits in registers; draft logits add a residual pass;
+    early exit takes two rounds; filters add the select pass and a tail)."""
+    if lazy:
+        return 2 + (1 if explicit else 0)
+    if filt:
+        return 3
+    if wl["mode"] == "sample" and explicit:
+        return 2
+    return 1 if wl["B"] <= 1024 else 2
+
+
+def roofline_kernel(wl, lazy, filt, explicit, n) -> str:
+    if n == 1:
+        return ("sv_rows_kernel, one launch per call (row pass + per-request rule); "
+                "algorithmic bytes of the call / its kernel time")
+    what = ("early-exit rounds over position windows [0], [1, K]" if lazy else
+            "row pass + select pass + rule" if filt else "row pass + rule")
+    return (f"whole call, {n} launches ({what}{' + residual pass' if explicit else ''}); "
+            "algorithmic bytes / call time")
 
 
 def run_copy(args):
@@ -213,6 +365,8 @@ def main():
                          "and accept lengths only; c3_shard8 is one GPU's share of C3 split "
                          "over 8 GPUs (B=32)")
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="untimed steps for at least this long before the warmup steps (GPU clocks)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["verify", "copy"], default="verify")
@@ -224,15 +378,12 @@ def main():
         sys.exit(2)
 
     import numpy as np
-    import torch
 
     if args.mode == "copy":
         return run_copy(args)
 
-    import draft_verification_05_amd as sv
     from workloads import make
 
-    dev = torch.device("cuda:0")
     ragged = args.workload in RAGGED_BASE
     masked = args.workload in MASKED_BASE
     lazy = args.workload in LAZY_BASE
@@ -257,6 +408,18 @@ def main():
         wl = dict(make(base, data_seed=0, B=full["B"] // g), name=args.workload)
     else:
         wl = make(args.workload, data_seed=0)
+    # The CPU baseline's worker processes are forked now, before this process
+    # makes its first GPU call; they inherit the workload.
+    pool = None
+    if not args.no_cpu_baseline:
+        global _CPU_WL
+        _CPU_WL = wl
+        pool = multiprocessing.get_context("fork").Pool(cpu_workers())
+
+    import torch
+    import draft_verification_05_amd as sv
+
+    dev = torch.device("cuda:0")
     lib = sv.load_library()
     B, K, V = wl["B"], wl["K"], wl["V"]
     mode = wl["mode"]
@@ -353,6 +516,18 @@ def main():
         if rc:
             raise sv.SpecVerifyError(rc, "bench step")
 
+    # Clock settle: the GPU leaves its idle clocks only after some ms of
+    # sustained load (a first round of 200 calls measured ~5% slower than
+    # the next), so steps run untimed for at least `settle_s` before the W
+    # warmup steps; their offsets are distinct from every timed step's.
+    settle_calls = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(50):
+            step(10_000_000 + settle_calls)
+            settle_calls += 1
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -389,13 +564,22 @@ def main():
     per_launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     mean_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
     ms_per_step = region_ms / args.steps
+    last_offset = args.warmup + 2 * args.steps - 1       # the offset of the last call made
+    gpu_out = {"tokens": out_tok.cpu().numpy(), "accept_len": out_len.cpu().numpy(), "lazy": lazy}
+    if mode == "sample" and not ragged and not tok_only:
+        gpu_out["p"] = out_p.cpu().numpy().reshape(B, K)
+        gpu_out["q"] = out_q.cpu().numpy().reshape(B, K)
     accept = out_len.cpu().numpy()
     rejected = int((accept < K + 1).sum()) if mode == "sample" else None
     # the last step's accept lengths stand for every step's (the offset changes
     # the uniforms, not the drafts' odds)
     nbytes = lazy_bytes(wl, accept) if lazy else algorithmic_bytes(wl, rejected)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
+    # The dominant kernel: a one-launch call is one kernel per step, so its
+    # average duration is the timed region over the steps (events on the
+    # launch stream); calls of several launches are priced as a whole.
+    n_launches = launches_per_call(wl, args.workload, lazy, filt, draft is not None)
+    achieved = nbytes / (ms_per_step * 1e-3) / 1e9
 
     line = {
         "metric": METRIC,
@@ -406,6 +590,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"calls": settle_calls, "s": round(settle_s, 3)},
         "ms_per_step": round(ms_per_step, 5),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True,
@@ -433,14 +618,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_record(wl["name"]),
-                     "kernel": ("one verification call: rounds of row pass + decision over "
-                                "position windows [0], [1, K]"
-                                if lazy else "one verification call: row pass + select pass + tail"
-                                if filt else "one verification call: row pass + tail") +
-                               (" + residual pass" if mode == "sample" and draft is not None else ""),
-                     "launch_us_mean": round(mean_launch_ms * 1e3, 2),
-                     "launch_us_p10": round(per_launch_ms[len(per_launch_ms) // 10] * 1e3, 2),
-                     "launch_us_p90": round(per_launch_ms[(9 * len(per_launch_ms)) // 10] * 1e3, 2)},
+                     "kernel": roofline_kernel(wl, lazy, filt, draft is not None, n_launches),
+                     "kernel_us": round(ms_per_step * 1e3, 2),
+                     "timing": "HIP events on the launch stream around the timed region, / steps",
+                     "call_us_median": round(per_launch_ms[len(per_launch_ms) // 2] * 1e3, 2),
+                     "call_us_p10": round(per_launch_ms[len(per_launch_ms) // 10] * 1e3, 2),
+                     "call_us_p90": round(per_launch_ms[(9 * len(per_launch_ms)) // 10] * 1e3, 2),
+                     "call_us_mean": round(mean_launch_ms * 1e3, 2),
+                     "call_timing": "a second pass with an event pair around every call"},
         # the probe reads the target logits; with draft logits the call reads
         # more than that, and early exit reads less, so no ratio is given
         "stream_ceiling": dict(stream, call_logical_gbps=round(
@@ -451,8 +636,10 @@ def main():
         "accept_len_hist": np.bincount(accept, minlength=(K + 2) if mode != "tree" else 5).tolist(),
         "source_digest": source_digest(),
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if pool is not None:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, pool, last_offset, gpu_out)
+        pool.close()
+        pool.join()
     print(json.dumps(line), flush=True)
 
 

@@ -27,9 +27,10 @@ __all__ = [
     "spec_verify_tree", "spec_verify_sample_ragged", "spec_verify_greedy_ragged",
     "spec_verify_sample_masked", "spec_verify_greedy_masked", "spec_verify_sample_lazy",
     "spec_verify_sample_filtered",
-    "spec_verify_workspace_size", "spec_verify_workspace_init",
+    "spec_verify_workspace_size", "spec_verify_workspace_init", "spec_verify_workspace_errors",
+    "spec_verify_errors",
     "spec_verify_status_string", "SV_OK", "SV_ERR_NULL", "SV_ERR_SHAPE", "SV_ERR_DTYPE",
-    "SV_ERR_STRIDE", "SV_ERR_WORKSPACE", "SV_ERR_TREE", "SV_ERR_HIP", "SV_OP_SAMPLE",
+    "SV_ERR_STRIDE", "SV_ERR_WORKSPACE", "SV_ERR_TREE", "SV_ERR_HIP", "SV_ERR_NO_DEVICE", "SV_OP_SAMPLE",
     "SV_OP_GREEDY", "SV_OP_TREE", "SVLogits",
 ]
 
@@ -37,7 +38,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE = 0, -1, -2, -3
-SV_ERR_STRIDE, SV_ERR_WORKSPACE, SV_ERR_TREE, SV_ERR_HIP = -4, -5, -6, -7
+SV_ERR_STRIDE, SV_ERR_WORKSPACE, SV_ERR_TREE, SV_ERR_HIP, SV_ERR_NO_DEVICE = -4, -5, -6, -7, -8
 SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_OP_SAMPLE, SV_OP_GREEDY, SV_OP_TREE = 0, 1, 2
 
@@ -55,6 +56,7 @@ _PSV = ctypes.POINTER(SVLogits)
 _SIGNATURES = {
     "spec_verify_workspace_size": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "spec_verify_workspace_init": (ctypes.c_int, [_vp, _c_size, _vp]),
+    "spec_verify_workspace_errors": (ctypes.c_int, [_vp, _c_size, _vp, _c_i32, _vp]),
     "spec_verify_sample": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _c_u64, _c_i32, _c_i32,
                                           _c_i32, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "spec_verify_sample_lazy": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _c_u64, _c_i32, _c_i32,
@@ -128,8 +130,30 @@ def spec_verify_workspace_init(ws: torch.Tensor) -> None:
         raise SpecVerifyError(rc, "spec_verify_workspace_init")
 
 
+def spec_verify_workspace_errors(ws: torch.Tensor, reset: bool = True) -> int:
+    """Number of requests whose one-launch rule gave up waiting (and refused
+    the request) since `ws` was zero-filled or last reset. Synchronises with
+    the workspace's device. A working device always returns 0."""
+    out = torch.zeros(1, dtype=torch.int32, device=ws.device)
+    rc = load_library().spec_verify_workspace_errors(ws.data_ptr(), ws.numel() * ws.element_size(),
+                                                     out.data_ptr(), int(bool(reset)),
+                                                     _stream_ptr(ws.device))
+    if rc:
+        raise SpecVerifyError(rc, "spec_verify_workspace_errors")
+    return int(out.item())
+
+
+def spec_verify_errors(device=None, reset: bool = True) -> int:
+    """spec_verify_workspace_errors of the workspace this module keeps for
+    the current stream of `device` (0 when it has none yet)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    ws = _workspaces.get((dev.index, _stream_ptr(dev)))
+    return 0 if ws is None else spec_verify_workspace_errors(ws, reset)
+
+
 # One zero-initialised workspace per (device, stream): the library leaves its
-# counter words zero after every call, so reuse on the same stream is safe.
+# counter and tagged words zero after every call, so reuse on the same stream
+# is safe.
 _workspaces: dict = {}
 
 

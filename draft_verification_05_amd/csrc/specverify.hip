@@ -48,6 +48,7 @@ enum Mode { kOneHot = 0, kExplicit = 1, kGreedy = 2, kTree = 3 };
 
 constexpr int kMaxRows = 2 * SV_MAX_DRAFT + 1;
 constexpr int kMaxChunksPerWg = 256;
+constexpr size_t kHeaderBytes = 256;              // workspace header: the give-up count
 constexpr size_t kCounterBytes = 4u * SV_MAX_BATCH;
 
 // Hand-off from the row pass to the residual pass (explicit draft logits).
@@ -108,6 +109,9 @@ struct Args {
   uint64_t* tz_unif;    // [B * R][2]: (u_accept, u_sample) of each position
   uint32_t tag;         // this call's tag
   int n_rowwg;          // row-pass workgroups; the B tail workgroups follow them in the grid
+  unsigned* err;        // workspace header: count of one-launch waits that gave up
+  int spin_limit;       // polls before a one-launch tail gives up
+  int drop_req;         // test hook: request whose row-pass workgroups skip their tagged stores, else -1
   int no_tail;          // two-launch explicit calls: the residual pass runs the rule
   int n_nodes;
   int8_t parent[SV_MAX_TREE_NODES];
@@ -245,9 +249,23 @@ __device__ inline bool has_tag(uint64_t w, uint32_t tag) { return (uint32_t)(w >
 __device__ inline float tag_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // A tail workgroup gives up after this many polls (far beyond any row pass:
-// every poll is at least one trip to memory) and refuses its request, so
-// every wave of the launch ends whatever the workspace holds.
+// every poll is at least one trip to memory), refuses its request and
+// counts the event in the workspace header, so every wave of the launch
+// ends whatever the workspace holds and the caller can see that it
+// happened (spec_verify_workspace_errors).
 constexpr int kSpinLimit = 1 << 20;
+
+// Tail workgroups clear every tagged word their request's row pass wrote,
+// once they have seen all of them carry the call's tag: after a call that
+// gave up no wait, the tagged region holds zeros only, so a word of an
+// earlier call can never pass for one of a later call, whatever their tags.
+__device__ inline void clear_tag(uint64_t* p) {
+  __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void count_give_up(const Args& A) {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(A.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Tagged words per lane a one-launch tail loads (per kind of value).
 constexpr int kFusedQ = 8;
 
@@ -256,8 +274,8 @@ constexpr int kFusedQ = 8;
 // workgroup, which is dispatched last and usually finishes last, and only
 // then loads all its slots, so requests still streaming cost one word per
 // poll instead of every slot. Returns false when the wait gave up.
-__device__ inline bool wait_tag(const uint64_t* p, uint32_t tag) {
-  for (int spin = 0; spin < kSpinLimit; ++spin) {
+__device__ inline bool wait_tag(const uint64_t* p, uint32_t tag, int limit) {
+  for (int spin = 0; spin < limit; ++spin) {
     if (has_tag(get_tag(p), tag)) return true;
     __builtin_amdgcn_s_sleep(8);
   }
@@ -490,13 +508,14 @@ __device__ inline bool wstage_tagged(const Args& A, int b, int n_live, float2 id
   t.G = G;
   t.per = 64 / G;
   t.passes = (A.rows + t.per - 1) / t.per;
-  const uint64_t* wp = A.tz_part + 2 * (int64_t)b * A.rows * A.wpr;
+  uint64_t* wp = A.tz_part + 2 * (int64_t)b * A.rows * A.wpr;
   const int w = lane & (G - 1), rsub = lane / G;
   uint64_t hv[8], hi[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) { hv[q] = 0ull; hi[q] = 0ull; }
   // the last live row's last workgroup first (see wait_tag)
-  if (n_live > 0 && !wait_tag(wp + 2 * ((n_live - 1) * A.wpr + A.wpr - 1) + 1, A.tag)) return false;
+  if (n_live > 0 && !wait_tag(wp + 2 * ((n_live - 1) * A.wpr + A.wpr - 1) + 1, A.tag, A.spin_limit))
+    return false;
   for (int spin = 0;; ++spin) {
     bool miss = false;
 #pragma unroll
@@ -510,16 +529,33 @@ __device__ inline bool wstage_tagged(const Args& A, int b, int n_live, float2 id
       }
     }
     if (__ballot(miss) == 0ull) break;
-    if (spin >= kSpinLimit) return false;
+    if (spin >= A.spin_limit) return false;
     __builtin_amdgcn_s_sleep(2);
   }
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int rr = q * t.per + rsub;
-    t.v[q] = (q < t.passes && rr < n_live && w < A.wpr) ? make_float2(tag_val(hv[q]), tag_val(hi[q]))
-                                                        : identity;
+    const bool mine = q < t.passes && rr < n_live && w < A.wpr;
+    t.v[q] = mine ? make_float2(tag_val(hv[q]), tag_val(hi[q])) : identity;
   }
   return true;
+}
+
+// Clears the words wstage_tagged read (all of the call's rows, seen), for
+// later calls; issued after the tail's last loads.
+__device__ inline void wclear_tagged(const Args& A, int b, int n_live, const WStaged& t) {
+  const int lane = threadIdx.x & 63;
+  uint64_t* wp = A.tz_part + 2 * (int64_t)b * A.rows * A.wpr;
+  const int w = lane & (t.G - 1), rsub = lane / t.G;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int rr = q * t.per + rsub;
+    if (q < t.passes && rr < n_live && w < A.wpr) {
+      uint64_t* slot = wp + 2 * (rr * A.wpr + w);
+      clear_tag(slot);
+      clear_tag(slot + 1);
+    }
+  }
 }
 
 // Per-row (max, sum) into S.rowM / S.rowS.
@@ -690,16 +726,33 @@ __device__ Record sample_tail(const Args& A, int b, TailLds& S, bool write_out =
 }
 
 // sample_tail in a one-launch call (one-hot drafts; calls with draft logits
-// decide in the residual pass): the request's chunk partials (row rr,
-// chunk s in lane s % 64, load rr * npl + s / 64), gathered logits and
-// uniforms come from tagged slots, loaded together and polled until all
-// carry this call's tag; rows merge from the chunk partials, and the draw
-// locates its chunk among the partials already in registers. The host
-// admits a call only when rows * npl <= kFusedQ.
+// decide in the residual pass), spread over the tail workgroup's waves so
+// that the chain after a request's last row-pass workgroup stays short:
+//   wave 0  polls the request's tagged words (chunk partials of row rr,
+//           chunk s in lane s % 64, load rr * npl + s / 64; the draft
+//           tokens' logits; the uniforms) until all carry this call's tag,
+//           hands row 0's to wave 1 through LDS as soon as they are in,
+//           merges every row (max, then one rescaled sum) and runs the
+//           acceptance scan; it draws itself only when the scan stops past
+//           position 0;
+//   wave 1  draws from row 0 as soon as its words are in: the draw of every
+//           request that stops at position 0 (with one-hot drafts nearly
+//           all of them) or has no drafts, made while row 1.. still stream;
+//   wave 2  clears every tagged word once wave 0 has seen them all (their
+//           stores in flight while the rule runs).
+// The host admits a call only when rows * npl <= kFusedQ.
+constexpr int kTailNotDrawn = -2;                 // wave 1 made no draw
+
 template <int DT, bool kVec, bool kMask>
 __device__ void fused_sample_tail(const Args& A, int b) {
   __shared__ float s_rowM[kFusedQ], s_rowS[kFusedQ];
+  __shared__ float2 s_p0[64 * kFusedQ];            // row 0's chunk partials
+  __shared__ float s_u0, s_lx0;                    // row 0's draw uniform, draft logit
+  __shared__ int s_row0;                           // 0: row 0 not in yet, 1: in, 2: never
+  __shared__ int s_seen;                           // 0: wave 0 still polling, 1: saw all words, 2: did not
+  __shared__ int s_y0;                             // wave 1's draw, or kTailNotDrawn
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const Req rq = request(A, b);
   const int K = rq.k, V = A.V, R = A.R, nch = A.n_chunk;
   const int npl = (nch + 63) >> 6;
@@ -710,43 +763,142 @@ __device__ void fused_sample_tail(const Args& A, int b) {
   const bool valid = lane < K && (unsigned)x < (unsigned)V;
   const float T = A.temperature[b];
   const bool refused = !rq.ok || !(T > 0.f && T < __builtin_inff());
-  // what this request needs from the row pass (nothing when refused)
+  // Every word the row pass writes for this request: the chunk partials of
+  // its live rows, the uniforms of every position and the draft tokens'
+  // logits. Wave 0 waits for all of them (also when the temperature refuses
+  // the request); a ragged request with bad offsets has none.
   bool need[kFusedQ];
 #pragma unroll
   for (int q = 0; q < kFusedQ; ++q) {
-    const int rr = q < nq ? q / npl : 0, s = (q < nq ? q % npl : 0) * 64 + lane;
-    need[q] = !refused && q < nq && (rr < R ? rr <= K : rr - R < K) && s < nch;
+    const int rr = q < nq ? q / npl : 0, sc = (q < nq ? q % npl : 0) * 64 + lane;
+    need[q] = rq.ok && q < nq && (rr < R ? rr <= K : rr - R < K) && sc < nch;
   }
-  const bool need_u = !refused && lane <= K;
-  const bool need_g = !refused && valid;
-  uint64_t pm[kFusedQ], ps[kFusedQ], hx = 0ull, hu0 = 0ull, hu1 = 0ull;
+  const bool need_u = rq.ok && lane < R;
+  const bool need_g = rq.ok && valid;
+  uint64_t* const us = A.tz_unif + 2 * ((int64_t)b * R + lane);
+  auto slot_of = [&](int q) { return A.tz_part + 2 * ((rowg0 + q / npl) * nch + (q % npl) * 64 + lane); };
+  if (threadIdx.x == 0) { s_row0 = 0; s_seen = 0; s_y0 = kTailNotDrawn; }
+  __syncthreads();
+  auto flag_set = [](int* f, int v) { __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); };
+  auto flag_get = [](int* f) { return __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); };
+
+  bool got = false;
+  float uacc = 0.f, usmp = 0.f, lx = kNegInf;
+  uint64_t pm[kFusedQ], ps[kFusedQ];
+  if (wave == 0) {
+    uint64_t hx = 0ull, hu0 = 0ull, hu1 = 0ull;
 #pragma unroll
-  for (int q = 0; q < kFusedQ; ++q) { pm[q] = 0ull; ps[q] = 0ull; }
-  // the last chunk of the last live row (row K) belongs to the request's last workgroup
-  bool got = refused || wait_tag(A.tz_part + 2 * ((rowg0 + K) * nch + nch - 1) + 1, tag);
-  for (int spin = 0; got && !refused; ++spin) {
-    bool miss = false;
+    for (int q = 0; q < kFusedQ; ++q) { pm[q] = 0ull; ps[q] = 0ull; }
+    got = !rq.ok;
+    bool row0 = refused;                           // row 0 handed over (or never will be)
+    if (refused && lane == 0) flag_set(&s_row0, 2);
+    for (int spin = 0; rq.ok; ++spin) {
+      bool miss = false, miss0 = false;
 #pragma unroll
-    for (int q = 0; q < kFusedQ; ++q) {
-      if (need[q]) {
-        const uint64_t* slot = A.tz_part + 2 * ((rowg0 + q / npl) * nch + (q % npl) * 64 + lane);
-        if (!has_tag(pm[q], tag)) pm[q] = get_tag(slot);
-        if (!has_tag(ps[q], tag)) ps[q] = get_tag(slot + 1);
-        miss |= !(has_tag(pm[q], tag) && has_tag(ps[q], tag));
+      for (int q = 0; q < kFusedQ; ++q) {
+        if (need[q]) {
+          const uint64_t* sl = slot_of(q);
+          if (!has_tag(pm[q], tag)) pm[q] = get_tag(sl);
+          if (!has_tag(ps[q], tag)) ps[q] = get_tag(sl + 1);
+          const bool m = !(has_tag(pm[q], tag) && has_tag(ps[q], tag));
+          miss |= m;
+          if (q < npl) miss0 |= m;
+        }
+      }
+      if (need_g && !has_tag(hx, tag)) hx = get_tag(A.tz_gath + rowg0 + lane);
+      if (need_u) {
+        if (!has_tag(hu0, tag)) hu0 = get_tag(us);
+        if (!has_tag(hu1, tag)) hu1 = get_tag(us + 1);
+      }
+      const bool mg = need_g && !has_tag(hx, tag);
+      const bool mu = need_u && !(has_tag(hu0, tag) && has_tag(hu1, tag));
+      miss |= mg || mu;
+      miss0 |= (lane == 0) && (mg || mu);
+      if (!row0 && __ballot(miss0) == 0ull) {      // row 0 complete: hand it to wave 1
+        row0 = true;
+#pragma unroll
+        for (int q = 0; q < kFusedQ; ++q)
+          if (q < npl)                             // uniform
+            s_p0[q * 64 + lane] = need[q] ? make_float2(tag_val(pm[q]), tag_val(ps[q]))
+                                          : make_float2(kNegInf, 0.f);
+        if (lane == 0) {
+          s_u0 = tag_val(hu1);
+          s_lx0 = need_g ? tag_val(hx) : kNegInf;
+          flag_set(&s_row0, 1);
+        }
+      }
+      if (__ballot(miss) == 0ull) { got = true; break; }
+      if (spin >= A.spin_limit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (!row0 && lane == 0) flag_set(&s_row0, 2);
+    if (lane == 0) flag_set(&s_seen, got && rq.ok ? 1 : 2);
+    if (!got) count_give_up(A);
+    uacc = tag_val(hu0);
+    usmp = tag_val(hu1);
+    lx = need_g ? tag_val(hx) : kNegInf;
+  } else if (wave == 1) {
+    // the draw from row 0: the residual of a rejection at position 0, or the
+    // bonus token when there are no drafts
+    int st;
+    while ((st = flag_get(&s_row0)) == 0) __builtin_amdgcn_s_sleep(1);
+    if (st == 1) {
+      const float c = kLog2e / T;
+      float mi = kNegInf;
+#pragma unroll
+      for (int q = 0; q < kFusedQ; ++q)
+        if (q < npl) mi = fmaxf(mi, s_p0[q * 64 + lane].x);
+      mi = wave_max_all(mi);
+      const int x0 = lane_i(x, 0);
+      const float M = K > 0 ? fmaxf(mi, s_lx0 * c) : mi;
+      const int xe = K > 0 ? x0 : -1;
+      auto part_of = [&](int sc) { return s_p0[(sc >> 6) * 64 + (sc & 63)]; };
+      int y = draw_from_partials<DT, kVec, kMask, false>(A, b, rq, 0, c, M, xe, s_u0, kNegInf, part_of);
+      if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_0's mode
+      if (lane == 0) s_y0 = y;
+    }
+  } else if (wave == 2) {
+    // clear every tagged word for later calls once wave 0 has seen them all
+    int st;
+    while ((st = flag_get(&s_seen)) == 0) __builtin_amdgcn_s_sleep(1);
+    if (st == 1) {
+#pragma unroll
+      for (int q = 0; q < kFusedQ; ++q) {
+        if (need[q]) {
+          uint64_t* sl = slot_of(q);
+          clear_tag(sl);
+          clear_tag(sl + 1);
+        }
+      }
+      if (need_g) clear_tag(A.tz_gath + rowg0 + lane);
+      if (need_u) {
+        clear_tag(us);
+        clear_tag(us + 1);
       }
     }
-    if (need_g && !has_tag(hx, tag)) hx = get_tag(A.tz_gath + rowg0 + lane);
-    if (need_u) {
-      const uint64_t* us = A.tz_unif + 2 * ((int64_t)b * R + lane);
-      if (!has_tag(hu0, tag)) hu0 = get_tag(us);
-      if (!has_tag(hu1, tag)) hu1 = get_tag(us + 1);
-    }
-    miss |= need_g && !has_tag(hx, tag);
-    miss |= need_u && !(has_tag(hu0, tag) && has_tag(hu1, tag));
-    if (__ballot(miss) == 0ull) break;
-    if (spin >= kSpinLimit) got = false;
-    else __builtin_amdgcn_s_sleep(2);
   }
+  if (wave == 0 && got && !refused) {
+    // per-row (max, sum): the row's largest chunk max, then the sum of the
+    // chunk sums rescaled to it
+    for (int rr = 0; rr < A.rows; ++rr) {          // uniform
+      float m = kNegInf;
+#pragma unroll
+      for (int q = 0; q < kFusedQ; ++q)
+        if (q >= rr * npl && q < (rr + 1) * npl && need[q]) m = fmaxf(m, tag_val(pm[q]));
+      const float Mr = wave_max_all(m);
+      float sr = 0.f;
+#pragma unroll
+      for (int q = 0; q < kFusedQ; ++q)
+        if (q >= rr * npl && q < (rr + 1) * npl && need[q]) {
+          const float mq = tag_val(pm[q]);
+          sr += mq == kNegInf ? 0.f : tag_val(ps[q]) * fast_exp2(mq - Mr);
+        }
+      sr = wave_sum_all(sr);
+      if (lane == 0) { s_rowM[rr] = Mr; s_rowS[rr] = sr; }
+    }
+  }
+  __syncthreads();                                 // wave 1's draw is in s_y0
+  if (wave != 0) return;
   int32_t* otok = A.out_tokens + (int64_t)b * A.out_cols;
   for (int j = K + 1 + lane; j < A.out_cols; j += 64) otok[j] = -1;   // columns past this request's drafts
   if (refused || !got) {
@@ -756,20 +908,7 @@ __device__ void fused_sample_tail(const Args& A, int b) {
     if (lane == 0) A.out_len[b] = 0;
     return;
   }
-  // per-row (max, sum): a lane's npl partials of the row, then the wave
-  for (int rr = 0; rr < A.rows; ++rr) {            // uniform
-    float m = kNegInf, sr = 0.f;
-#pragma unroll
-    for (int q = 0; q < kFusedQ; ++q)
-      if (q >= rr * npl && q < (rr + 1) * npl)     // uniform
-        ms_merge(m, sr, need[q] ? tag_val(pm[q]) : kNegInf, need[q] ? tag_val(ps[q]) : 0.f);
-    seg_reduce_ms(64, m, sr);
-    if (lane == 0) { s_rowM[rr] = m; s_rowS[rr] = sr; }
-  }
-  __builtin_amdgcn_wave_barrier();   // one wave: order the LDS traffic
   const float c = kLog2e / T;
-  const float uacc = tag_val(hu0), usmp = tag_val(hu1);
-  const float lx = need_g ? tag_val(hx) : kNegInf;
   float p = 0.f, q = 0.f, Mx = kNegInf;
   if (lane < K) {
     // row `lane`'s sums leave x out: add its own term back for p(x)
@@ -788,21 +927,24 @@ __device__ void fused_sample_tail(const Args& A, int b) {
   const int a = rej < 0 ? K : rej;
   if (lane <= K && lane != a) otok[lane] = lane < a ? x : -1;
   if (lane == 0) A.out_len[b] = a + 1;
-  const float ua = lane_f(usmp, a);
-  const bool resid = a < K;
-  const float M = resid ? lane_f(Mx, a) : s_rowM[a];
-  const int xe = resid ? lane_i(x, a) : -1;
-  // chunk s of row a sits in this lane's load a * npl + s / 64 (s = lane mod 64)
-  auto part_of = [&](int s) {
-    const int qa = a * npl + (s >> 6);             // uniform
-    float2 v = make_float2(kNegInf, 0.f);
+  int y = a == 0 ? s_y0 : kTailNotDrawn;
+  if (y == kTailNotDrawn) {                        // stopped past position 0: draw here
+    const float ua = lane_f(usmp, a);
+    const bool resid = a < K;
+    const float M = resid ? lane_f(Mx, a) : s_rowM[a];
+    const int xe = resid ? lane_i(x, a) : -1;
+    // chunk s of row a sits in this lane's load a * npl + s / 64 (s = lane mod 64)
+    auto part_of = [&](int sc) {
+      const int qa = a * npl + (sc >> 6);          // uniform
+      float2 v = make_float2(kNegInf, 0.f);
 #pragma unroll
-    for (int qq = 0; qq < kFusedQ; ++qq)
-      if (qq == qa && need[qq]) v = make_float2(tag_val(pm[qq]), tag_val(ps[qq]));
-    return v;
-  };
-  int y = draw_from_partials<DT, kVec, kMask, false>(A, b, rq, a, c, M, xe, ua, kNegInf, part_of);
-  if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
+      for (int qq = 0; qq < kFusedQ; ++qq)
+        if (qq == qa && need[qq]) v = make_float2(tag_val(pm[qq]), tag_val(ps[qq]));
+      return v;
+    };
+    y = draw_from_partials<DT, kVec, kMask, false>(A, b, rq, a, c, M, xe, ua, kNegInf, part_of);
+    if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
+  }
   if (lane == 0) otok[a] = y;
 }
 
@@ -816,8 +958,12 @@ __device__ void greedy_tail(const Args& A, int b, int* sg) {
   WStaged ws;
   const float2 identity = make_float2(kNegInf, __int_as_float(INT_MAX));
   bool got = true;
-  if constexpr (kTagged) got = wstage_tagged(A, b, rq.ok ? K + 1 : 0, identity, ws);
-  else wstage_issue(A, b, A.rows, identity, ws);
+  if constexpr (kTagged) {
+    got = wstage_tagged(A, b, rq.ok ? K + 1 : 0, identity, ws);
+    if (!got) count_give_up(A);
+  } else {
+    wstage_issue(A, b, A.rows, identity, ws);
+  }
   merge_argmax_rows(A, b, A.rows, sg, ws);
   const int g = lane <= K ? sg[lane] : -1;
   const int mis = first_lane(lane < K && x != g);
@@ -834,6 +980,7 @@ __device__ void greedy_tail(const Args& A, int b, int* sg) {
     if (A.out_aux) A.out_aux[rq.g0 + lane] = g;
   }
   if (lane == 0) A.out_len[b] = a + 1;
+  if constexpr (kTagged) wclear_tagged(A, b, K + 1, ws);
 }
 
 // The tree's acceptance in parallel, one lane per node: a node is accepted
@@ -848,6 +995,7 @@ __device__ void tree_tail(const Args& A, int b, int* sg) {
   const float2 identity = make_float2(kNegInf, __int_as_float(INT_MAX));
   if constexpr (kTagged) {
     if (!wstage_tagged(A, b, N, identity, ws)) {   // the wait gave up: refuse the request
+      count_give_up(A);
       if (lane < N) A.out_tokens[(int64_t)b * A.out_cols + lane] = -1;
       if (lane == 0) {
         A.out_len[b] = 0;
@@ -885,6 +1033,7 @@ __device__ void tree_tail(const Args& A, int b, int* sg) {
     A.out_len[b] = len + 1;
     if (A.out_aux) A.out_aux[b] = best;
   }
+  if constexpr (kTagged) wclear_tagged(A, b, N, ws);
 }
 
 // ------------------------------------------------- early-exit rounds ---
@@ -1206,18 +1355,16 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   if constexpr (kFused) {
-    if (blockIdx.x >= (unsigned)A.n_rowwg) {      // a tail workgroup: one wave does the work
-      if (wave == 0) {
-        const int bt = (int)(blockIdx.x - (unsigned)A.n_rowwg);
-        if constexpr (MODE == kOneHot) {
-          fused_sample_tail<DT, kVec, kMask>(A, bt);
-        } else if constexpr (MODE == kExplicit) {
-          static_assert(MODE != kExplicit, "calls with draft logits never take one launch");
-        } else {
-          __shared__ int s_g[SV_MAX_TREE_NODES];
-          if constexpr (MODE == kGreedy) greedy_tail<true>(A, bt, s_g);
-          else tree_tail<true>(A, bt, s_g);
-        }
+    if (blockIdx.x >= (unsigned)A.n_rowwg) {      // a tail workgroup
+      const int bt = (int)(blockIdx.x - (unsigned)A.n_rowwg);
+      if constexpr (MODE == kOneHot) {
+        fused_sample_tail<DT, kVec, kMask>(A, bt);   // every wave takes part
+      } else if constexpr (MODE == kExplicit) {
+        static_assert(MODE != kExplicit, "calls with draft logits never take one launch");
+      } else if (wave == 0) {                     // one wave does the work
+        __shared__ int s_g[SV_MAX_TREE_NODES];
+        if constexpr (MODE == kGreedy) greedy_tail<true>(A, bt, s_g);
+        else tree_tail<true>(A, bt, s_g);
       }
       return;
     }
@@ -1322,6 +1469,7 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
     // token's logit (by the workgroup whose run holds it) and the uniforms;
     // greedy / tree: the workgroup's argmax.
     const uint32_t tag = A.tag;
+    if (b == A.drop_req) return;                  // test hook: this request's tail must give up
     if constexpr (MODE == kOneHot || MODE == kExplicit) {
       uint64_t* tp = A.tz_part + 2 * ((int64_t)rowg * A.n_chunk + c_lo);
       for (int i = tid; i < c_hi - c_lo; i += kThreads) {
@@ -2015,6 +2163,15 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + a] = y;
 }
 
+// The workspace header's give-up count, copied to out (and cleared when
+// reset is set) in stream order.
+__global__ void sv_errors_kernel(unsigned* err, uint32_t* out, int reset) {
+  if (threadIdx.x == 0) {
+    *out = reset ? __hip_atomic_exchange(err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 __global__ void sv_zero_kernel(unsigned char* p, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -2041,7 +2198,8 @@ struct Layout {
   size_t part, wpart, gath, rec, res, unif, alive, rf, fpart, tz, total;
 };
 
-// Workspace: [counters: 4 * SV_MAX_BATCH][chunk partials][workgroup
+// Workspace: [header: the give-up count][counters: 4 * SV_MAX_BATCH]
+//            [chunk partials][workgroup
 //            partials][gathered logits][records][residual partials]
 //            [uniforms][alive flags][row cuts][kept weight per chunk]
 //            [tagged slots of one-launch calls]
@@ -2049,7 +2207,7 @@ Layout layout(int64_t B, int64_t rows, int64_t V) {
   const int64_t ce = Chunk<kF32>::kElems;          // the smaller chunk: a bound for both dtypes
   const int64_t nch = (V + ce - 1) / ce;
   Layout L;
-  L.part = align_up(kCounterBytes, 256);
+  L.part = align_up(kHeaderBytes + kCounterBytes, 256);
   L.wpart = align_up(L.part + (size_t)(B * rows * nch) * sizeof(float2), 256);
   L.gath = align_up(L.wpart + (size_t)(B * rows * nch) * sizeof(float2), 256);   // wpr <= nch
   L.rec = align_up(L.gath + (size_t)(B * rows) * sizeof(float), 256);
@@ -2116,6 +2274,37 @@ int round_chunks_per_wg(int64_t rows_total, int n_chunk) {
   return (n_chunk + wpr - 1) / wpr;
 }
 
+// Test hooks, read at every call (unset in normal use):
+//   SPECVERIFY_SPIN_LIMIT  polls before a one-launch tail gives up (default 2^20)
+//   SPECVERIFY_DROP_TAGGED_REQUEST  a request whose row-pass workgroups skip
+//                          their tagged stores in one-launch calls, so its tail
+//                          gives up (exercises the give-up count)
+//   SPECVERIFY_TAG         the tag of every one-launch call (hex; exercises tag
+//                          repeats between calls)
+int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return (e && *e) ? atoi(e) : dflt;
+}
+int spin_limit() {
+  const int v = env_int("SPECVERIFY_SPIN_LIMIT", kSpinLimit);
+  return v > 0 ? v : kSpinLimit;
+}
+int drop_request() { return env_int("SPECVERIFY_DROP_TAGGED_REQUEST", -1); }
+
+// The first call that finds a device remembers it; until then every entry
+// point asks the runtime (and clears the error a failed query leaves).
+int device_status() {
+  static std::atomic<int> found{0};
+  if (found.load(std::memory_order_relaxed)) return SV_OK;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return SV_ERR_NO_DEVICE;
+  }
+  found.store(1, std::memory_order_relaxed);
+  return SV_OK;
+}
+
 void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int rows, void* ws) {
   const int64_t es = elem_bytes(t->dtype);
   A.tgt = static_cast<const char*>(t->data);
@@ -2133,7 +2322,8 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.wpr = (A.n_chunk + A.cpw - 1) / A.cpw;
   const Layout L = layout(B, rows, V);
   unsigned char* base = static_cast<unsigned char*>(ws);
-  A.counters = reinterpret_cast<unsigned*>(base);
+  A.err = reinterpret_cast<unsigned*>(base);
+  A.counters = reinterpret_cast<unsigned*>(base + kHeaderBytes);
   A.part = reinterpret_cast<float2*>(base + L.part);
   A.wpart = reinterpret_cast<float2*>(base + L.wpart);
   A.gath = reinterpret_cast<float*>(base + L.gath);
@@ -2148,6 +2338,8 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.tz_unif = A.tz_gath + (size_t)(B * rows);
   A.tag = 0;
   A.n_rowwg = 0;
+  A.spin_limit = spin_limit();
+  A.drop_req = drop_request();
   A.no_tail = 0;
   A.filtered = 0;
   A.top_k = nullptr;
@@ -2277,7 +2469,9 @@ constexpr int kFusedMaxBatch = 1024;
 uint32_t next_tag() {
   static std::atomic<uint32_t> counter{
       (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count()};
-  return 0xFF800000u | (1u + counter.fetch_add(1u, std::memory_order_relaxed) % 0x7FFFFFu);
+  uint32_t v = counter.fetch_add(1u, std::memory_order_relaxed);
+  if (const char* e = getenv("SPECVERIFY_TAG")) v = (uint32_t)strtoul(e, nullptr, 16) - 1u;   // test hook
+  return 0xFF800000u | (1u + v % 0x7FFFFFu);
 }
 
 bool one_launch_enabled() {
@@ -2350,6 +2544,7 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
   const int R = K + 1;
   const int rows = R + (explicit_q ? K : 0);
   if (workspace_bytes < layout(B, rows, V).total) return SV_ERR_WORKSPACE;
+  if ((st = device_status())) return st;
 
   Args A;
   fill_common(A, target, B, K, V, R, rows, workspace);
@@ -2450,6 +2645,7 @@ int greedy_impl(const sv_logits* target, const int32_t* cu, int32_t total_k, con
   if (!workspace) return SV_ERR_WORKSPACE;
   const int R = K + 1;
   if (workspace_bytes < layout(B, R, V).total) return SV_ERR_WORKSPACE;
+  if ((st = device_status())) return st;
   Args A;
   fill_common(A, target, B, K, V, R, R, workspace);
   A.tokens = draft_tokens;
@@ -2495,6 +2691,7 @@ size_t spec_verify_workspace_size(int32_t op, int32_t B, int32_t K_or_N, int32_t
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace) return SV_ERR_NULL;
   if (workspace_bytes == 0) return SV_OK;
+  if (const int st = device_status()) return st;
   size_t blocks = (workspace_bytes / 4 + kThreads - 1) / kThreads;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
@@ -2615,6 +2812,7 @@ int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
     if (parents[n] < 0 || parents[n] >= n) return SV_ERR_TREE;
   if (!workspace) return SV_ERR_WORKSPACE;
   if (workspace_bytes < layout(B, N, V).total) return SV_ERR_WORKSPACE;
+  if ((st = device_status())) return st;
   Args A;
   fill_common(A, target, B, 0, V, N, N, workspace);
   A.tokens = node_tokens;
@@ -2636,6 +2834,16 @@ int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
   return hip_status();
 }
 
+int spec_verify_workspace_errors(void* workspace, size_t workspace_bytes, uint32_t* out_count,
+                                 int32_t reset, void* stream) {
+  if (!workspace || !out_count) return SV_ERR_NULL;
+  if (workspace_bytes < kHeaderBytes) return SV_ERR_WORKSPACE;
+  if (const int st = device_status()) return st;
+  hipLaunchKernelGGL(sv_errors_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     static_cast<unsigned*>(workspace), out_count, reset);
+  return hip_status();
+}
+
 const char* spec_verify_status_string(int status) {
   switch (status) {
     case SV_OK: return "ok";
@@ -2646,6 +2854,7 @@ const char* spec_verify_status_string(int status) {
     case SV_ERR_WORKSPACE: return "workspace missing or smaller than spec_verify_workspace_size()";
     case SV_ERR_TREE: return "malformed parent array (need parents[0] == -1, 0 <= parents[n] < n)";
     case SV_ERR_HIP: return "HIP launch failed";
+    case SV_ERR_NO_DEVICE: return "no HIP device visible";
     default: return "unknown status";
   }
 }

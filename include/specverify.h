@@ -15,29 +15,35 @@
  *    described by sv_logits; strides are in ELEMENTS and may be 0
  *    (broadcast). Rows whose address and strides are 16-byte aligned take
  *    the 128-bit load path, others a scalar path with identical results.
- *  - The caller owns every buffer. The library allocates nothing, keeps no
- *    state between calls beyond a per-process call counter (below), never
+ *  - The caller owns every buffer. The library allocates nothing, never
  *    synchronises and launches only on `stream` (a hipStream_t; NULL = the
- *    default stream). Results are ready when the stream reaches them.
+ *    default stream). Results are ready when the stream reaches them. Its
+ *    only state is a per-process counter that numbers one-launch calls
+ *    (below) and a flag that remembers that a device was found.
  *  - Argument errors are detected on the host before anything is launched
- *    and returned as a negative status; nothing is written then.
- *    Device-resident values are not checked on the host; their handling is
- *    stated per entry point.
+ *    and returned as a negative status; nothing is written then. With
+ *    valid arguments and no HIP device visible a call returns
+ *    SV_ERR_NO_DEVICE. Device-resident values are not checked on the host;
+ *    their handling is stated per entry point.
  *  - Workspace: size from spec_verify_workspace_size(), zero-filled ONCE by
  *    spec_verify_workspace_init() (or any zero fill) before its first use.
  *    Every call leaves the workspace's counter words zero again, so it can
  *    be reused by any later call that fits; it must not be shared by calls
  *    that may run concurrently (different streams). Calls that run the
  *    row pass and the per-request rule in one launch hand results over
- *    through workspace words tagged with a value unique to the call (a
- *    per-process counter), so a later call never mistakes an earlier
- *    call's words for its own and nothing needs clearing between calls.
- *    Setting SPECVERIFY_ONE_LAUNCH=0 in the environment makes every call
- *    use two launches (the same results up to fp32 summation order). The
- *    wait for those words is bounded (2^20 polls, each at least one trip to
- *    memory); a request whose words never arrive, which a working device
- *    does not produce, is refused (accept length 0, tokens -1) rather than
- *    left hanging.
+ *    through workspace words tagged with the call's number (a per-process
+ *    counter with period 2^23 - 1); the rule's workgroups clear every such
+ *    word once they have read it, so after each call the tagged words are
+ *    zero again and a word of an earlier call can never be taken for a
+ *    later call's, even when their numbers repeat. Setting
+ *    SPECVERIFY_ONE_LAUNCH=0 in the environment makes every call use two
+ *    launches (the same results up to fp32 summation order). The wait for
+ *    those words is bounded (2^20 polls, each at least one trip to memory);
+ *    a request whose words never arrive, which a working device does not
+ *    produce, is refused (accept length 0, tokens -1) rather than left
+ *    hanging, and the event is counted in the workspace header, readable
+ *    with spec_verify_workspace_errors(); a workspace with a nonzero count
+ *    may hold stale words and should be zero-filled again.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -58,6 +64,7 @@ extern "C" {
 #define SV_ERR_WORKSPACE -5   /* workspace NULL or smaller than required */
 #define SV_ERR_TREE      -6   /* malformed parent array */
 #define SV_ERR_HIP       -7   /* a HIP launch failed (hipGetLastError) */
+#define SV_ERR_NO_DEVICE -8   /* no HIP device is visible */
 
 /* logits element types */
 #define SV_DTYPE_F32  0
@@ -96,6 +103,22 @@ size_t spec_verify_workspace_size(int32_t op, int32_t B, int32_t K_or_N, int32_t
 /* Zero-fill `workspace_bytes` bytes of a workspace on `stream` (a fill
  * kernel, no memset node). SV_ERR_NULL for a NULL workspace. */
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Health of a workspace (not an operation of the pages: it reports on the
+ * library's own one-launch hand-off). Writes to out_count (a DEVICE
+ * uint32) the number of requests, over every call since the workspace was
+ * zero-filled (or since the last reset), whose rule gave up waiting for
+ * the row pass's words and refused the request; with reset != 0 the count
+ * is cleared at the same time. Runs in stream order: the value covers the
+ * calls enqueued before it. A working device never gives up, so a nonzero
+ * count means the refusals it counts were not the caller's doing and the
+ * workspace should be zero-filled again (spec_verify_workspace_init).
+ * SV_ERR_NULL for a NULL workspace or out_count, SV_ERR_WORKSPACE when
+ * workspace_bytes is below the 256-byte header.
+ */
+int spec_verify_workspace_errors(void* workspace, size_t workspace_bytes, uint32_t* out_count,
+                                 int32_t reset, void* stream);
 
 /*
  * Stochastic verification ("推测解码与 MTP" §2.1; exactness: the

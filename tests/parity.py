@@ -86,18 +86,23 @@ def near_cut_invalid(wl, b, tok, n, top_k, top_p, draft_dtype):
 
 
 def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32", report=None,
-                    bitmask=None, lazy=False, top_k=None, top_p=None):
+                    bitmask=None, lazy=False, top_k=None, top_p=None, oracle_out=None):
     """Run the oracle on `requests` and fold the comparison into a report dict.
 
     lazy: the outputs of early-exit verification, which computes p and q only
-    up to the position where a request stopped and leaves 0 after it."""
+    up to the position where a request stopped and leaves 0 after it.
+    g_p / g_q may be None (a call that returned tokens only): p and q are then
+    not compared. oracle_out: the oracle's (tokens, accept_len, p, q, traces)
+    for these requests, already computed with keep_trace (it is not run again)."""
     rep = new_report() if report is None else report
     B, K, V = wl["B"], wl["K"], wl["V"]
     reqs = list(range(B)) if requests is None else list(requests)
-    o_tok, o_len, o_p, o_q, traces = oracle.spec_verify_sample(
-        wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"], wl["seeds"],
-        wl["offset"], target_dtype=wl["dtype"], draft_dtype=draft_dtype, requests=reqs,
-        keep_trace=True, bitmask=bitmask, top_k=top_k, top_p=top_p)
+    if oracle_out is None:
+        oracle_out = oracle.spec_verify_sample(
+            wl["target"], wl["draft"], wl["draft_tokens"], wl["temperature"], wl["seeds"],
+            wl["offset"], target_dtype=wl["dtype"], draft_dtype=draft_dtype, requests=reqs,
+            keep_trace=True, bitmask=bitmask, top_k=top_k, top_p=top_p)
+    o_tok, o_len, o_p, o_q, traces = oracle_out
     for b in reqs:
         rep["requests"] += 1
         if b not in traces:                               # refused by the oracle
@@ -114,10 +119,12 @@ def classify_sample(wl, g_tok, g_len, g_p, g_q, requests=None, draft_dtype="f32"
                 rep["mismatches"].append((b, "invalid output near a top-p cut: " + bad, g_tok[b].tolist()))
             continue
         n = min(max(int(g_len[b]), 0), K) if lazy else K
-        if n:
+        if g_p is None:
+            n = 0
+        elif n:
             rep["max_p_err"] = max(rep["max_p_err"], float(np.max(np.abs(g_p[b, :n] - o_p[b, :n]))))
             rep["max_q_err"] = max(rep["max_q_err"], float(np.max(np.abs(g_q[b, :n] - o_q[b, :n]))))
-        if n < K and (np.any(g_p[b, n:] != 0) or np.any(g_q[b, n:] != 0)):
+        if g_p is not None and n < K and (np.any(g_p[b, n:] != 0) or np.any(g_q[b, n:] != 0)):
             rep["mismatches"].append((b, "p/q after the stop", g_p[b, n:].tolist(), g_q[b, n:].tolist()))
             continue
         a_o, a_g = int(o_len[b]) - 1, int(g_len[b]) - 1

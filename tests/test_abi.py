@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = sv.spec_verify_status_string(code)
         assert s and s != "unknown status"
     assert sv.spec_verify_status_string(-99) == "unknown status"
@@ -210,3 +210,27 @@ def test_filtered_argument_errors(lib):
     assert call(wsb=need - 1) == sv.SV_ERR_WORKSPACE
     assert call(d=desc(dtype=1)) == sv.SV_ERR_DTYPE
     assert call(tk=None, tp=None, t=desc(dtype=9)) == sv.SV_ERR_DTYPE   # both filters optional
+
+
+def no_device_here():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not no_device_here(), reason="a device is visible: valid calls would launch")
+def test_valid_calls_without_a_device_return_no_device(lib):
+    """Arguments that pass every host check reach the device query last: with
+    no GPU the call returns SV_ERR_NO_DEVICE and launches nothing."""
+    assert call_sample(lib) == sv.SV_ERR_NO_DEVICE
+    t = desc()
+    assert lib.spec_verify_greedy(ctypes.byref(t), FAKE, 1, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS,
+                                  None) == sv.SV_ERR_NO_DEVICE
+    assert lib.spec_verify_workspace_init(FAKE, 1024, None) == sv.SV_ERR_NO_DEVICE
+    assert lib.spec_verify_workspace_errors(FAKE, 1024, FAKE, 1, None) == sv.SV_ERR_NO_DEVICE
+
+
+def test_workspace_errors_argument_errors(lib):
+    f = lib.spec_verify_workspace_errors
+    assert f(None, 1024, FAKE, 1, None) == sv.SV_ERR_NULL
+    assert f(FAKE, 1024, None, 0, None) == sv.SV_ERR_NULL
+    assert f(FAKE, 255, FAKE, 0, None) == sv.SV_ERR_WORKSPACE

@@ -142,3 +142,68 @@ def test_two_launch_fallback_shapes():
     with two_launch():
         res = run_sample(wl)
     assert_report(classify_sample(wl, *res), "two launches, V=2^20")
+
+
+@contextmanager
+def env(**kv):
+    old = {k: os.environ.get(k) for k in kv}
+    os.environ.update({k: str(v) for k, v in kv.items()})
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
+
+
+def test_repeated_tags_never_match_an_earlier_calls_words():
+    """The call tag repeats after 2^23 - 1 calls; the test hook SPECVERIFY_TAG
+    gives consecutive calls the same tag, of the same shape with new data and
+    of other shapes. The rule's workgroups clear every tagged word they read,
+    so each call still waits for its own row pass and matches the oracle."""
+    ws_errs = sv.spec_verify_errors(DEV)            # start from a clean count
+    assert ws_errs == 0, ws_errs
+    shapes = [("c3_onehot", dict(B=64, V=3 * 8192 + 1232)), ("c3_onehot", dict(B=64, V=3 * 8192 + 1232)),
+              ("c3_onehot", dict(B=40, K=3, V=9000)), ("c3_onehot", dict(B=64, V=3 * 8192 + 1232))]
+    with env(SPECVERIFY_TAG="7ffff0"):
+        for i, (cfg, kw) in enumerate(shapes):
+            wl = make(cfg, data_seed=520 + i, offset=i, **kw)
+            print(f"[case] repeated tag, call {i} B={wl['B']} K={wl['K']} V={wl['V']}", flush=True)
+            assert_report(classify_sample(wl, *run_sample(wl)), f"repeated tag call {i}")
+            c = make("c4_greedy", data_seed=530 + i, B=16 + 8 * i, V=20000 + 1000 * i)
+            d = to_device(c, DEV)
+            g_tok, g_len, _ = sv.spec_verify_greedy(d["target"], d["tokens"])
+            o_tok, o_len, _ = oracle.spec_verify_greedy(c["target"], c["draft_tokens"], c["dtype"])
+            np.testing.assert_array_equal(g_tok.cpu().numpy(), o_tok)
+            np.testing.assert_array_equal(g_len.cpu().numpy(), o_len)
+    assert sv.spec_verify_errors(DEV) == 0
+
+
+def test_a_wait_that_gives_up_is_counted():
+    """Test hook: the row pass of one request skips its tagged stores, so that
+    request's rule gives up after a short bounded wait (every kernel still
+    ends). It is refused, the workspace's give-up count reads 1, and every
+    other request is unchanged; the next normal call counts nothing."""
+    wl = make("c3_onehot", data_seed=540, B=24, V=2 * 8192 + 100, offset=4)
+    assert sv.spec_verify_errors(DEV) == 0
+    ref = run_sample(wl)
+    print("[case] give-up: one request's tagged stores dropped", flush=True)
+    with env(SPECVERIFY_DROP_TAGGED_REQUEST=5, SPECVERIFY_SPIN_LIMIT=4096):
+        got = run_sample(wl)
+    assert sv.spec_verify_errors(DEV) == 1
+    assert got[1][5] == 0 and np.all(got[0][5] == -1)
+    keep = np.arange(wl["B"]) != 5
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a[keep], b[keep])
+    c = make("c4_greedy", data_seed=541, B=16, V=20000)
+    d = to_device(c, DEV)
+    with env(SPECVERIFY_DROP_TAGGED_REQUEST=3, SPECVERIFY_SPIN_LIMIT=4096):
+        g_tok, g_len, _ = sv.spec_verify_greedy(d["target"], d["tokens"])
+    g_len = g_len.cpu().numpy()
+    assert sv.spec_verify_errors(DEV) == 1 and g_len[3] == 0
+    o_tok, o_len, _ = oracle.spec_verify_greedy(c["target"], c["draft_tokens"], c["dtype"])
+    np.testing.assert_array_equal(g_len[np.arange(16) != 3], o_len[np.arange(16) != 3])
+    assert_report(classify_sample(wl, *run_sample(wl)), "after a give-up")
+    assert sv.spec_verify_errors(DEV) == 0
