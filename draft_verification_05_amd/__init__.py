@@ -30,7 +30,8 @@ __all__ = [
     "spec_verify_workspace_size", "spec_verify_workspace_init", "spec_verify_workspace_errors",
     "spec_verify_errors",
     "spec_verify_status_string", "SV_OK", "SV_ERR_NULL", "SV_ERR_SHAPE", "SV_ERR_DTYPE",
-    "SV_ERR_STRIDE", "SV_ERR_WORKSPACE", "SV_ERR_TREE", "SV_ERR_HIP", "SV_ERR_NO_DEVICE", "SV_OP_SAMPLE",
+    "SV_ERR_STRIDE", "SV_ERR_WORKSPACE", "SV_ERR_TREE", "SV_ERR_HIP", "SV_ERR_NO_DEVICE",
+    "SV_ERR_SCRATCH", "spec_verify_sample_noalloc", "SV_OP_SAMPLE",
     "SV_OP_GREEDY", "SV_OP_TREE", "SVLogits",
 ]
 
@@ -39,6 +40,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE = 0, -1, -2, -3
 SV_ERR_STRIDE, SV_ERR_WORKSPACE, SV_ERR_TREE, SV_ERR_HIP, SV_ERR_NO_DEVICE = -4, -5, -6, -7, -8
+SV_ERR_SCRATCH = -9
 SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_OP_SAMPLE, SV_OP_GREEDY, SV_OP_TREE = 0, 1, 2
 
@@ -61,6 +63,8 @@ _SIGNATURES = {
                                           _c_i32, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "spec_verify_sample_lazy": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _c_u64, _c_i32, _c_i32,
                                                _c_i32, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "spec_verify_sample_noalloc": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _c_u64, _c_i32, _c_i32,
+                                                  _c_i32, _vp, _vp, _vp, _vp, _vp]),
     "spec_verify_sample_filtered": (ctypes.c_int, [_PSV, _PSV, _vp, _vp, _vp, _vp, _vp, _c_u64,
                                                    _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp,
                                                    _c_size, _vp]),
@@ -226,6 +230,43 @@ def spec_verify_sample(target: torch.Tensor, draft: torch.Tensor | None, draft_t
     """Stochastic verification. Returns (tokens [B,K+1], accept_len [B], p_draft [B,K], q_draft [B,K])."""
     return _sample("spec_verify_sample", target, draft, draft_tokens, temperature, seeds, offset,
                    want_probs)
+
+
+def spec_verify_sample_noalloc(target: torch.Tensor, draft: torch.Tensor | None,
+                               draft_tokens: torch.Tensor, temperature: torch.Tensor,
+                               seeds: torch.Tensor, offset: int = 0, *, want_probs: bool = True):
+    """spec_verify_sample through the entry point that allocates nothing: its
+    workspace is the library's static per-device scratch (16 MiB; larger calls
+    raise SV_ERR_SCRATCH). Calls that may overlap on one device race on that
+    scratch. The outputs here are allocated by torch; the C entry point itself
+    allocates nothing."""
+    lib = load_library()
+    B, R, V = target.shape
+    K = R - 1
+    dev = target.device
+    tdesc = _desc(target, "target")
+    ddesc = None
+    if draft is not None:
+        ddesc = _desc(draft, "draft")
+        if draft.shape[0] != B or draft.shape[1] < K or draft.shape[2] != V or draft.device != dev:
+            raise ValueError("draft must be [B, >=K, V] on the target's device")
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    seeds = _seeds_u64(seeds)
+    _check(seeds, "seeds", torch.int64, (B,), dev)
+    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    p = torch.empty((B, K), dtype=torch.float32, device=dev) if want_probs else None
+    q = torch.empty((B, K), dtype=torch.float32, device=dev) if want_probs else None
+    with torch.cuda.device(dev):
+        rc = lib.spec_verify_sample_noalloc(ctypes.byref(tdesc), ctypes.byref(ddesc) if ddesc else None,
+                                            draft_tokens.data_ptr() if K else None,
+                                            temperature.data_ptr(), seeds.data_ptr(),
+                                            int(offset) & (2**64 - 1), B, K, V, tokens.data_ptr(),
+                                            alen.data_ptr(), _ptr(p), _ptr(q), _stream_ptr(dev))
+    if rc:
+        raise SpecVerifyError(rc, "spec_verify_sample_noalloc")
+    return tokens, alen, p, q
 
 
 def spec_verify_sample_lazy(target: torch.Tensor, draft: torch.Tensor | None,

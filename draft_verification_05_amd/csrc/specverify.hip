@@ -38,6 +38,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "specverify.h"
 #include "sv_device.hpp"
@@ -2187,6 +2188,14 @@ __global__ void sv_zero_kernel(unsigned char* p, size_t n) {
 
 }  // namespace sv
 
+// Scratch of spec_verify_sample_noalloc, for callers that cannot allocate:
+// the workspace of one call lives in this array (every device the library
+// runs on holds its own copy until the process ends). Host code never uses
+// its name as an address: each device's address comes from
+// hipGetSymbolAddress (see scratch_on_current_device).
+constexpr size_t kScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // ================================================================ host ===
 namespace {
 
@@ -2474,6 +2483,36 @@ uint32_t next_tag() {
   return 0xFF800000u | (1u + v % 0x7FFFFFu);
 }
 
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; the first lookup also zero-
+// fills the array on `st` (a fill kernel), so the counters and tagged words
+// start at zero. Every later call leaves them zero again.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_on_current_device(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return SV_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return SV_ERR_HIP;
+    }
+    hipLaunchKernelGGL(sv_zero_kernel, dim3(4096), dim3(kThreads), 0, st,
+                       static_cast<unsigned char*>(p), kScratchBytes);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SV_OK;
+}
+
 bool one_launch_enabled() {
   const char* e = getenv("SPECVERIFY_ONE_LAUNCH");
   return !(e && e[0] == '0');
@@ -2521,6 +2560,22 @@ int check_grid(int64_t wgs) {
 
 int hip_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
+// Host checks of a sampling call's arguments (everything but the workspace).
+int check_sample_args(const sv_logits* target, const sv_logits* draft, const int32_t* cu,
+                      int32_t total_k, const int32_t* draft_tokens, const float* temperature,
+                      const uint64_t* seeds, int32_t B, int32_t K, int32_t V,
+                      const int32_t* out_tokens, const int32_t* out_accept_len) {
+  int st = check_desc(target);
+  if (st) return st;
+  if (draft && (st = check_desc(draft))) return st;
+  if (!temperature || !seeds || !out_tokens || !out_accept_len) return SV_ERR_NULL;
+  if (B < 1 || B > SV_MAX_BATCH || K < 0 || K > SV_MAX_DRAFT || V < 1 || V > SV_MAX_VOCAB)
+    return SV_ERR_SHAPE;
+  if ((cu ? total_k > 0 : K > 0) && !draft_tokens) return SV_ERR_NULL;
+  if (draft && draft->dtype != target->dtype) return SV_ERR_DTYPE;
+  return SV_OK;
+}
+
 // Sampling, dense (cu null: [B, K + 1] rows by the two strides) or ragged
 // (cu [B + 1] device prefix sums, packed rows by stride_k, stride_b unused).
 int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* cu, int32_t total_k,
@@ -2531,14 +2586,9 @@ int sample_impl(const sv_logits* target, const sv_logits* draft, const int32_t* 
                 int32_t* out_tokens, int32_t* out_accept_len,
                 float* out_p_draft, float* out_q_draft,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_desc(target);
+  int st = check_sample_args(target, draft, cu, total_k, draft_tokens, temperature, seeds, B, K, V,
+                             out_tokens, out_accept_len);
   if (st) return st;
-  if (draft && (st = check_desc(draft))) return st;
-  if (!temperature || !seeds || !out_tokens || !out_accept_len) return SV_ERR_NULL;
-  if (B < 1 || B > SV_MAX_BATCH || K < 0 || K > SV_MAX_DRAFT || V < 1 || V > SV_MAX_VOCAB)
-    return SV_ERR_SHAPE;
-  if ((cu ? total_k > 0 : K > 0) && !draft_tokens) return SV_ERR_NULL;
-  if (draft && draft->dtype != target->dtype) return SV_ERR_DTYPE;
   if (!workspace) return SV_ERR_WORKSPACE;
   const bool explicit_q = draft != nullptr && K > 0;
   const int R = K + 1;
@@ -2713,6 +2763,26 @@ int spec_verify_sample(const sv_logits* target, const sv_logits* draft,
                      out_q_draft, workspace, workspace_bytes, stream);
 }
 
+int spec_verify_sample_noalloc(const sv_logits* target, const sv_logits* draft,
+                               const int32_t* draft_tokens, const float* temperature,
+                               const uint64_t* seeds, uint64_t offset,
+                               int32_t B, int32_t K, int32_t V,
+                               int32_t* out_tokens, int32_t* out_accept_len,
+                               float* out_p_draft, float* out_q_draft, void* stream) {
+  int st = check_sample_args(target, draft, nullptr, 0, draft_tokens, temperature, seeds, B, K, V,
+                             out_tokens, out_accept_len);
+  if (st) return st;
+  const int rows = K + 1 + ((draft && K > 0) ? K : 0);
+  if (layout(B, rows, V).total > kScratchBytes) return SV_ERR_SCRATCH;
+  if ((st = device_status())) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(s, &ws))) return st;
+  return sample_impl(target, draft, nullptr, 0, nullptr, false, nullptr, nullptr, false, draft_tokens,
+                     temperature, seeds, offset, B, K, V, out_tokens, out_accept_len, out_p_draft,
+                     out_q_draft, ws, kScratchBytes, stream);
+}
+
 int spec_verify_sample_lazy(const sv_logits* target, const sv_logits* draft,
                             const int32_t* draft_tokens, const float* temperature,
                             const uint64_t* seeds, uint64_t offset,
@@ -2855,6 +2925,7 @@ const char* spec_verify_status_string(int status) {
     case SV_ERR_TREE: return "malformed parent array (need parents[0] == -1, 0 <= parents[n] < n)";
     case SV_ERR_HIP: return "HIP launch failed";
     case SV_ERR_NO_DEVICE: return "no HIP device visible";
+    case SV_ERR_SCRATCH: return "the call needs more than the 16 MiB of spec_verify_sample_noalloc's scratch";
     default: return "unknown status";
   }
 }

@@ -65,6 +65,7 @@ extern "C" {
 #define SV_ERR_TREE      -6   /* malformed parent array */
 #define SV_ERR_HIP       -7   /* a HIP launch failed (hipGetLastError) */
 #define SV_ERR_NO_DEVICE -8   /* no HIP device is visible */
+#define SV_ERR_SCRATCH   -9   /* a no-allocation call needs more than its scratch holds */
 
 /* logits element types */
 #define SV_DTYPE_F32  0
@@ -215,6 +216,32 @@ int spec_verify_sample_filtered(const sv_logits* target, const sv_logits* draft,
                                 int32_t* out_tokens, int32_t* out_accept_len,
                                 float* out_p_draft, float* out_q_draft,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_sample without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The call's workspace is a static
+ * device array of 16 MiB (SV_NOALLOC_SCRATCH_BYTES) inside the library; each
+ * device the library runs on holds its own copy until the process ends.
+ * The call allocates nothing; its first call on a device (with that device
+ * current, `stream` on it) looks the array's address up once and zero-fills
+ * it on `stream`. Calls leave its counter and tagged words zero again, so
+ * every call starts clean; the array keeps the rest of the last call's
+ * contents. All such calls on one device share the one array: calls that
+ * may overlap on a device (different streams, different threads) race, and
+ * must be serialised by the caller.
+ * Arguments, results and errors are those of spec_verify_sample; a call
+ * whose workspace (spec_verify_workspace_size) would exceed the scratch
+ * returns SV_ERR_SCRATCH before anything is launched (B=256, K=5, V=128256
+ * one-hot needs 7.1 MiB).
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int spec_verify_sample_noalloc(const sv_logits* target, const sv_logits* draft,
+                               const int32_t* draft_tokens, const float* temperature,
+                               const uint64_t* seeds, uint64_t offset,
+                               int32_t B, int32_t K, int32_t V,
+                               int32_t* out_tokens, int32_t* out_accept_len,
+                               float* out_p_draft, float* out_q_draft, void* stream);
 
 /*
  * Early-exit ("lazy") stochastic verification. The rule stops at the first

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = sv.spec_verify_status_string(code)
         assert s and s != "unknown status"
     assert sv.spec_verify_status_string(-99) == "unknown status"
@@ -234,3 +234,14 @@ def test_workspace_errors_argument_errors(lib):
     assert f(None, 1024, FAKE, 1, None) == sv.SV_ERR_NULL
     assert f(FAKE, 1024, None, 0, None) == sv.SV_ERR_NULL
     assert f(FAKE, 255, FAKE, 0, None) == sv.SV_ERR_WORKSPACE
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_on_the_host(lib):
+    """The entry point for callers that cannot allocate refuses, before any
+    launch, a call whose workspace would not fit its 16 MiB scratch."""
+    t = sv.SVLogits(0x10000, 1, 0, 6 * 128256, 128256)
+    rc = lib.spec_verify_sample_noalloc(ctypes.byref(t), None, FAKE, FAKE, FAKE, 0, 1024, 5, 128256,
+                                        FAKE, FAKE, None, None, None)
+    assert rc == sv.SV_ERR_SCRATCH
+    assert lib.spec_verify_sample_noalloc(None, None, FAKE, FAKE, FAKE, 0, 1, 1, 5, FAKE, FAKE, None,
+                                          None, None) == sv.SV_ERR_NULL
