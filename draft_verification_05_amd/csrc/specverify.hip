@@ -105,7 +105,9 @@ struct Args {
   float* fpart;         // [B * rows * n_chunk]: kept weight per chunk
   // one-launch calls: the row pass hands its results to tail workgroups of
   // the same grid through tagged slots (value bits, call tag), see put_tag
-  uint64_t* tz_part;    // sampling [B * rows * n_chunk][2]: chunk (M, S); argmax [B * rows * wpr][2]
+  uint64_t* tz_part;    // sampling: row_words words per row (run_words); argmax [B * rows * wpr][2]
+  int64_t row_words;    // one-launch sampling: words per row in tz_part
+  int run_block;        // one-launch sampling: words per run block in tz_part
   uint64_t* tz_gath;    // [B * rows]: logit of the row's draft token
   uint64_t* tz_unif;    // [B * R][2]: (u_accept, u_sample) of each position
   uint32_t tag;         // this call's tag
@@ -248,6 +250,15 @@ __device__ inline uint64_t get_tag(const uint64_t* p) {
 }
 __device__ inline bool has_tag(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 __device__ inline float tag_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// One-launch sampling: run wi of row rowg has a block of run_block words at
+// rowg * row_words + wi * run_block: one per chunk (the chunk's sum rescaled
+// to the run's largest chunk max), then that max. Blocks are whole 128-byte
+// lines when the workspace has room (the host's plan): writes during the
+// row pass cost per line written, far more than per byte.
+__device__ inline uint64_t* run_words(const Args& A, int64_t rowg, int wi) {
+  return A.tz_part + rowg * A.row_words + (int64_t)wi * A.run_block;
+}
 
 // A tail workgroup gives up after this many polls (far beyond any row pass:
 // every poll is at least one trip to memory), refuses its request and
@@ -777,7 +788,14 @@ __device__ void fused_sample_tail(const Args& A, int b) {
   const bool need_u = rq.ok && lane < R;
   const bool need_g = rq.ok && valid;
   uint64_t* const us = A.tz_unif + 2 * ((int64_t)b * R + lane);
-  auto slot_of = [&](int q) { return A.tz_part + 2 * ((rowg0 + q / npl) * nch + (q % npl) * 64 + lane); };
+  // chunk sc of row rr: its word in run sc / cpw, and that run's max word
+  const int cpw = A.cpw;
+  auto word_of = [&](int q, bool max_word) {
+    const int rr = q / npl, sc = (q % npl) * 64 + lane;
+    const int w = sc / cpw;
+    const int at = max_word ? min(cpw, nch - w * cpw) : sc - w * cpw;
+    return run_words(A, rowg0 + rr, w) + at;
+  };
   if (threadIdx.x == 0) { s_row0 = 0; s_seen = 0; s_y0 = kTailNotDrawn; }
   __syncthreads();
   auto flag_set = [](int* f, int v) { __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); };
@@ -798,9 +816,8 @@ __device__ void fused_sample_tail(const Args& A, int b) {
 #pragma unroll
       for (int q = 0; q < kFusedQ; ++q) {
         if (need[q]) {
-          const uint64_t* sl = slot_of(q);
-          if (!has_tag(pm[q], tag)) pm[q] = get_tag(sl);
-          if (!has_tag(ps[q], tag)) ps[q] = get_tag(sl + 1);
+          if (!has_tag(pm[q], tag)) pm[q] = get_tag(word_of(q, true));
+          if (!has_tag(ps[q], tag)) ps[q] = get_tag(word_of(q, false));
           const bool m = !(has_tag(pm[q], tag) && has_tag(ps[q], tag));
           miss |= m;
           if (q < npl) miss0 |= m;
@@ -866,9 +883,8 @@ __device__ void fused_sample_tail(const Args& A, int b) {
 #pragma unroll
       for (int q = 0; q < kFusedQ; ++q) {
         if (need[q]) {
-          uint64_t* sl = slot_of(q);
-          clear_tag(sl);
-          clear_tag(sl + 1);
+          clear_tag(word_of(q, true));
+          clear_tag(word_of(q, false));
         }
       }
       if (need_g) clear_tag(A.tz_gath + rowg0 + lane);
@@ -878,7 +894,29 @@ __device__ void fused_sample_tail(const Args& A, int b) {
       }
     }
   }
-  if (wave == 0 && got && !refused) {
+  if (wave == 0 && got && !refused && npl == 1) {
+    // per-row (max, sum) with one partial per lane and row: every row's
+    // reduction at once, independent chains the scheduler interleaves
+    float mx[kFusedQ], sr[kFusedQ];
+#pragma unroll
+    for (int q = 0; q < kFusedQ; ++q) mx[q] = need[q] ? tag_val(pm[q]) : kNegInf;
+#pragma unroll
+    for (int q = 0; q < kFusedQ; ++q) mx[q] = q < A.rows ? wave_max_all(mx[q]) : kNegInf;
+#pragma unroll
+    for (int q = 0; q < kFusedQ; ++q) {
+      const float mq = need[q] ? tag_val(pm[q]) : kNegInf;
+      sr[q] = mq == kNegInf ? 0.f : tag_val(ps[q]) * fast_exp2(mq - mx[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kFusedQ; ++q) sr[q] = q < A.rows ? wave_sum_all(sr[q]) : 0.f;
+    if (lane < A.rows) {
+      float m = kNegInf, sm = 0.f;
+#pragma unroll
+      for (int q = 0; q < kFusedQ; ++q) if (lane == q) { m = mx[q]; sm = sr[q]; }
+      s_rowM[lane] = m;
+      s_rowS[lane] = sm;
+    }
+  } else if (wave == 0 && got && !refused) {
     // per-row (max, sum): the row's largest chunk max, then the sum of the
     // chunk sums rescaled to it
     for (int rr = 0; rr < A.rows; ++rr) {          // uniform
@@ -1472,10 +1510,20 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Args A) {
     const uint32_t tag = A.tag;
     if (b == A.drop_req) return;                  // test hook: this request's tail must give up
     if constexpr (MODE == kOneHot || MODE == kExplicit) {
-      uint64_t* tp = A.tz_part + 2 * ((int64_t)rowg * A.n_chunk + c_lo);
-      for (int i = tid; i < c_hi - c_lo; i += kThreads) {
-        put_tag(tp + 2 * i, s_part[i].x, tag);
-        put_tag(tp + 2 * i + 1, s_part[i].y, tag);
+      // one word per chunk, its sum rescaled to the run's largest chunk max,
+      // then that max: n + 1 words from one store instruction (a wave's
+      // stores hold its slot until they are acknowledged, so they are few)
+      if (wave == 0) {
+        const int n = c_hi - c_lo;
+        float m = kNegInf;
+        for (int i = lane; i < n; i += 64) m = fmaxf(m, s_part[i].x);
+        const float mw = wave_max_all(m);
+        uint64_t* tp = run_words(A, rowg, wi);
+        for (int i = lane; i <= n; i += 64) {
+          float v = mw;
+          if (i < n) v = s_part[i].x == kNegInf ? 0.f : s_part[i].y * fast_exp2(s_part[i].x - mw);
+          put_tag(tp + i, v, tag);
+        }
       }
       if (tid == 0 && (unsigned)xe < (unsigned)A.V && xe / kCE >= c_lo && xe / kCE < c_hi)
         put_tag(A.tz_gath + rowg, s_gx, tag);
@@ -2205,6 +2253,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
   size_t part, wpart, gath, rec, res, unif, alive, rf, fpart, tz, total;
+  int64_t nch;     // chunks per row of the smaller (fp32) chunk: a bound for both dtypes
 };
 
 // Workspace: [header: the give-up count][counters: 4 * SV_MAX_BATCH]
@@ -2216,6 +2265,7 @@ Layout layout(int64_t B, int64_t rows, int64_t V) {
   const int64_t ce = Chunk<kF32>::kElems;          // the smaller chunk: a bound for both dtypes
   const int64_t nch = (V + ce - 1) / ce;
   Layout L;
+  L.nch = nch;
   L.part = align_up(kHeaderBytes + kCounterBytes, 256);
   L.wpart = align_up(L.part + (size_t)(B * rows * nch) * sizeof(float2), 256);
   L.gath = align_up(L.wpart + (size_t)(B * rows * nch) * sizeof(float2), 256);   // wpr <= nch
@@ -2314,6 +2364,22 @@ int device_status() {
   return SV_OK;
 }
 
+// One-launch sampling stores a run's words in one block (run_words): whole
+// 128-byte lines when every row's blocks fit the 2 * nch words the layout
+// gives a row, else packed (cpw + 1 words; wpr * (cpw + 1) <= 2 * n_chunk
+// because runs are balanced: cpw <= n_chunk / wpr + 1, and wpr <= n_chunk / 4
+// + 1 when cpw >= 4, else wpr = 1). Called again when cpw / wpr change.
+void plan_run_blocks(Args& A, int64_t nch) {
+  const int lines = (A.cpw + 1 + 15) / 16;
+  if ((int64_t)A.wpr * 16 * lines <= 2 * nch) {
+    A.run_block = 16 * lines;
+    A.row_words = (int64_t)A.wpr * A.run_block;
+  } else {
+    A.run_block = A.cpw + 1;
+    A.row_words = 2 * (int64_t)A.n_chunk;
+  }
+}
+
 void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int rows, void* ws) {
   const int64_t es = elem_bytes(t->dtype);
   A.tgt = static_cast<const char*>(t->data);
@@ -2343,8 +2409,9 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.rf = reinterpret_cast<RowFilter*>(base + L.rf);
   A.fpart = reinterpret_cast<float*>(base + L.fpart);
   A.tz_part = reinterpret_cast<uint64_t*>(base + L.tz);
-  A.tz_gath = A.tz_part + 2 * (size_t)(B * rows * A.n_chunk);
+  A.tz_gath = A.tz_part + 2 * (size_t)(B * rows * L.nch);
   A.tz_unif = A.tz_gath + (size_t)(B * rows);
+  plan_run_blocks(A, L.nch);
   A.tag = 0;
   A.n_rowwg = 0;
   A.spin_limit = spin_limit();
