@@ -61,6 +61,8 @@ struct Record {
   float Mp, Sp;   // target row a: max and sum in units of 2^(y - Mp)
   float Mq, Sq;   // draft row a
   float tp, tq;   // top-k / top-p cuts of the two rows (filtered verification)
+  int draw;       // filtered verification: 1 when the token at a is still to be drawn
+  int xe;         // ... leaving out this token (a one-hot draft's; -1: none)
 };
 
 // A row's top-k / top-p cut: kept logits l >= thr, weights 2^(l c - mref),
@@ -642,6 +644,8 @@ template <int DT, bool kVec, int MODE, bool kMask>
 __device__ Record sample_tail(const Args& A, int b, TailLds& S, bool write_out = true) {
   Record rc;
   rc.pending = 0;
+  rc.draw = 0;
+  rc.xe = -1;
   const int lane = threadIdx.x & 63;
   const Req rq = request(A, b);
   const int K = rq.k, V = A.V, R = A.R;
@@ -1619,16 +1623,37 @@ constexpr int kSelBuckets = 256;                  // refinement levels
 constexpr int kSelCap = 2048;
 constexpr int kSelLevels = 3;
 
-struct SelLds {
-  unsigned cnt[kSelBuckets0];
-  double mass[kSelBuckets0];
-  uint32_t key[kSelCap];
-  double w[kSelCap];
+// bf16 rows: the one-pass search's table (see hist_pass).
+constexpr int kHBins = 4096;                      // per sign: magnitudes [2^-16, 2^16)
+constexpr uint32_t kHMagLo = 0x3780u;             // bf16 magnitude bits of 2^-16
+constexpr int kHOrd = 2 * kHBins + 2;             // ordered positions (hist_value)
+// Word of magnitude m (table: kHMagLo <= m < kHMagLo + kHBins) and sign s:
+// kHOff + (m - kHMagLo) + s * kHNeg; values below / above the table land in
+// the spare words just before / after their sign's table (kHOff - 1,
+// kHOff + kHBins). Both tables start 16-byte aligned.
+constexpr int kHOff = 4, kHNeg = kHBins + 8;
+constexpr int kHWords = kHOff + kHNeg + kHBins + 4;
+
+struct alignas(16) SelLds {
+  union {
+    struct {
+      unsigned cnt[kSelBuckets0];
+      double mass[kSelBuckets0];
+      uint32_t key[kSelCap];
+      double w[kSelCap];
+    };
+    uint32_t hcnt[kHWords];                        // the two tables and their spare words
+  };
   double scan[kThreads];
   double tab[64];                                  // 2^(j / 64)
+  double wtot[kWaves];
+  double at;
   float wsum[kWaves];
+  float tiny_w[kWaves][3];                         // per wave: sums of tiny l, l^2, l^3
   int n, sel;
   uint32_t kfloor;
+  unsigned tiny_n, ninf_n, tiny_max;               // tiny count, -inf count, largest tiny order key
+  int big;                                         // a value outside the table that is not -inf
 };
 
 // Total order of logit values as unsigned keys (-0 sorts with +0).
@@ -1782,6 +1807,224 @@ __device__ uint32_t scan_collected(SelLds& L, int n, double above, double target
   return k;
 }
 
+// ----------------------------------------------------- bf16 one pass ---
+// A bf16 logit is one of at most 65536 values, so a histogram with a
+// counter per distinct value holds a row exactly, and needs no reference
+// value before the pass: one pass over the row fills it, and the row's
+// largest value, the top-k cut, and the top-p cut with its kept mass (a
+// value's mass is its count times its weight 2^(l c - Mref), in fp64) are
+// read off descending scans of the counters. Each magnitude in
+// [2^-16, 2^16) has a counter per sign, indexed by its bits (32 binades of
+// 128 values); the word of a counter holds the count of the row's even
+// positions in its low half and of the odd ones in its high half, so each
+// logit adds a constant (a total that does not come to V shows a carry
+// between the halves: the general search then runs). Magnitudes below
+// 2^-16 ("tiny") share one count with the sums of their values, squares
+// and cubes, which give their mass 2^-Mref sum e^x, x = l c ln 2,
+// |x| < 2^-16 c ln 2, to O(x^4). -inf logits are counted apart (they weigh
+// nothing). A row holding any other value outside the table (NaN, +inf,
+// |l| >= 2^16), and a cut that falls among the tiny magnitudes, take the
+// general search.
+
+// Every 16-byte vector of a bf16 row once, raw: wave w of the workgroup
+// streams chunks w, w + kWaves, ... with the next chunk's loads in flight
+// while the current one is used (as in the row pass); f(word, e) gets each
+// 32-bit word (logits e and e + 1) once. Logits at or past V read as bf16
+// -inf (0xFF80).
+template <bool kVec, class F>
+__device__ __forceinline__ void for_each_word_bf16(const char* row, int n_chunk, int V, F f) {
+  constexpr int kCE = Chunk<kBF16>::kElems;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int n_full = V / kCE;
+  auto use = [&](ChunkRaw& r, int ch) {
+#pragma unroll
+    for (int j = 0; j < kLoadsPerLane; ++j) {
+      const int64_t e = (int64_t)ch * kCE + (int64_t)(j * 64 + lane) * 8;
+      f(r.v[j].x, e);
+      f(r.v[j].y, e + 2);
+      f(r.v[j].z, e + 4);
+      f(r.v[j].w, e + 6);
+    }
+  };
+  int ch = wave;
+  const int ch_end = kVec ? n_full : 0;
+  ChunkRaw ra, rb;
+  if (ch < ch_end) {
+    issue_chunk<kBF16>(row, (int64_t)ch * kCE, ra);
+    while (true) {
+      int nx = ch + kWaves;
+      bool more = nx < ch_end;
+      issue_chunk<kBF16>(row, (int64_t)(more ? nx : ch) * kCE, rb);
+      use(ra, ch);
+      ch = nx;
+      if (!more) break;
+      nx = ch + kWaves;
+      more = nx < ch_end;
+      issue_chunk<kBF16>(row, (int64_t)(more ? nx : ch) * kCE, ra);
+      use(rb, ch);
+      ch = nx;
+      if (!more) break;
+    }
+  }
+  for (; ch < n_chunk; ch += kWaves) {
+    ChunkRaw r;
+    load_chunk_checked<kBF16, kVec>(row, (int64_t)ch * kCE, V, r);
+    use(r, ch);
+  }
+}
+
+
+// One lane's tallies of the logits outside the table.
+struct HistRare {
+  float s1, s2, s3;                                // sums of l, l^2, l^3 over tiny magnitudes
+  unsigned n, ninf, kmax;                          // tiny count, -inf count, largest tiny order key
+  bool big;                                        // NaN, +inf or |l| >= 2^16
+  __device__ __forceinline__ void add(uint32_t h) {
+    if ((h & 0x7FFFu) < kHMagLo) {
+      const float v = __uint_as_float(h << 16);
+      s1 += v;
+      s2 += v * v;
+      s3 += v * v * v;
+      ++n;
+      kmax = max(kmax, order_key(v));
+    } else if (h == 0xFF80u) {
+      ++ninf;
+    } else {
+      big = true;
+    }
+  }
+};
+
+// One pass over a bf16 row into the counters (zeroed by the caller, with
+// the tallies), then the lanes' tallies folded into L. A magnitude is
+// clamped to the table's range plus one spare word each side, so a value
+// outside the table costs no extra instruction on the common path; the
+// lanes holding one also take the rare path.
+template <bool kVec>
+__device__ __forceinline__ void hist_pass(const char* row, int n_chunk, int V, SelLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr uint32_t lo = kHMagLo - 1u, hi = kHMagLo + kHBins;
+  HistRare t{0.f, 0.f, 0.f, 0u, 0u, 0u, false};
+  for_each_word_bf16<kVec>(row, n_chunk, V, [&](uint32_t w, int64_t) {
+    const uint32_t m0 = w & 0x7FFFu, m1 = (w >> 16) & 0x7FFFu;
+    const uint32_t c0 = min(max(m0, lo), hi), c1 = min(max(m1, lo), hi);
+    const uint32_t i0 = c0 + ((w >> 15) & 1u) * (uint32_t)kHNeg, i1 = c1 + (w >> 31) * (uint32_t)kHNeg;
+    atomicAdd(&L.hcnt[i0 - (kHMagLo - kHOff)], 1u);
+    atomicAdd(&L.hcnt[i1 - (kHMagLo - kHOff)], 0x10000u);
+    if (c0 != m0 || c1 != m1) {
+      if (c0 != m0) t.add(w & 0xFFFFu);
+      if (c1 != m1) t.add(w >> 16);
+    }
+  });
+  const float s1 = wave_sum_all(t.s1), s2 = wave_sum_all(t.s2), s3 = wave_sum_all(t.s3);
+  if (lane == 0) {
+    L.tiny_w[wave][0] = s1;
+    L.tiny_w[wave][1] = s2;
+    L.tiny_w[wave][2] = s3;
+  }
+  if (t.n) {
+    atomicAdd(&L.tiny_n, t.n);
+    atomicMax(&L.tiny_max, t.kmax);
+  }
+  if (t.ninf) atomicAdd(&L.ninf_n, t.ninf);
+  if (t.big) L.big = 1;
+  __syncthreads();
+}
+
+// Ordered positions, largest value first: [0, kHBins) the positive table
+// from just below 2^16 down to 2^-16, kHBins the tiny magnitudes, then the
+// negative table from -2^-16 down, and last (kHOrd - 1) -inf.
+// The logit value of an ordered position (not the tiny one).
+__device__ __forceinline__ float hist_value(int o) {
+  if (o < kHBins) return __uint_as_float((kHMagLo + (uint32_t)(kHBins - 1 - o)) << 16);
+  if (o < kHOrd - 1) return __uint_as_float((0x8000u | (kHMagLo + (uint32_t)(o - kHBins - 1))) << 16);
+  return kNegInf;
+}
+
+// One thread's run of ordered positions: kHPerT table counters in order
+// (a quarter of one binade, so consecutive values differ by the binade's
+// spacing u and their weights by the factor 2^(-u c)), then for thread
+// kThreads / 2 - 1 the tiny position and for the last thread the -inf one.
+constexpr int kHPerT = 2 * kHBins / kThreads;
+static_assert(kHPerT == 32 && kHBins % kHPerT == 0, "a run is a quarter binade");
+static_assert(kHOff % 4 == 0 && kHNeg % 4 == 0 && kHWords % 4 == 0, "16-byte aligned runs");
+struct HBlock {
+  uint32_t n[kHPerT];                              // counts
+  int o0;                                          // ordered position of n[0]
+  float v0, u;                                     // value of n[0], spacing
+  unsigned nx;                                     // count of the extra position (0: none)
+  int ox;                                          // its ordered position
+};
+
+__device__ __forceinline__ void hist_block_load(const SelLds& L, unsigned n_tiny, unsigned n_ninf, HBlock& hb) {
+  const int t = threadIdx.x;
+  const bool pos = t < kThreads / 2;
+  const int rel = pos ? kHBins - kHPerT * (t + 1) : kHPerT * (t - kThreads / 2);   // magnitude - kHMagLo
+  const uint4* q = reinterpret_cast<const uint4*>(L.hcnt + kHOff + rel + (pos ? 0 : kHNeg));
+  uint32_t w[kHPerT];
+#pragma unroll
+  for (int k = 0; k < kHPerT / 4; ++k) {
+    const uint4 x = q[k];
+    w[4 * k] = x.x;
+    w[4 * k + 1] = x.y;
+    w[4 * k + 2] = x.z;
+    w[4 * k + 3] = x.w;
+  }
+#pragma unroll
+  for (int j = 0; j < kHPerT; ++j) {
+    const uint32_t x = pos ? w[kHPerT - 1 - j] : w[j];   // positive values: descending bits
+    hb.n[j] = (x & 0xFFFFu) + (x >> 16);
+  }
+  const uint32_t mag0 = kHMagLo + (uint32_t)(pos ? rel + kHPerT - 1 : rel);
+  hb.o0 = pos ? kHPerT * t : kHBins + 1 + kHPerT * (t - kThreads / 2);
+  hb.v0 = __uint_as_float(((pos ? 0u : 0x8000u) | mag0) << 16);
+  hb.u = __uint_as_float(((mag0 & 0x7F80u) - (7u << 7)) << 16);   // 2^(e - 7)
+  hb.nx = t == kThreads / 2 - 1 ? n_tiny : (t == kThreads - 1 ? n_ninf : 0u);
+  hb.ox = t == kThreads / 2 - 1 ? kHBins : kHOrd - 1;
+}
+
+// After a block_scan_x: every thread passes its candidate position (INT_MAX:
+// none) and the running sum there; all get the smallest candidate and its
+// sum.
+__device__ __forceinline__ void hist_pick(SelLds& L, int mine, double mine_at, int* pos, double* at) {
+  if (threadIdx.x == 0) L.sel = INT_MAX;
+  __syncthreads();
+  if (mine != INT_MAX) atomicMin(&L.sel, mine);
+  __syncthreads();
+  if (mine != INT_MAX && mine == L.sel) L.at = mine_at;
+  __syncthreads();
+  *pos = L.sel == INT_MAX ? -1 : L.sel;
+  *at = L.at;
+  __syncthreads();                                 // L.sel and L.at are free again
+}
+
+// Inclusive scan of one double per thread (lanes in order within a wave,
+// waves in order). *excl gets the previous thread's result bit for bit and
+// *total the last thread's, so that exactly the thread whose range holds a
+// crossing of a threshold sees excl < t <= incl (up to the order of equal
+// partial sums).
+__device__ __forceinline__ double block_scan_x(double v, SelLds& L, double* excl, double* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  __syncthreads();                                 // earlier readers of L.wtot are done
+  if (lane == 63) L.wtot[wave] = v;
+  __syncthreads();
+  double pre = 0.0, tot = 0.0;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w == wave) pre = tot;
+    tot += L.wtot[w];
+  }
+  const double incl = pre + v;
+  const double prev = __shfl_up(incl, 1);
+  *excl = lane == 0 ? pre : prev;
+  *total = tot;
+  return incl;
+}
+
 // The cut for one criterion among the logits with key >= kfloor: the
 // largest logit value t whose upper set holds at least `want` logits
 // (kMass false) or `want` of their mass (kMass true). Returns the key of t,
@@ -1886,9 +2129,35 @@ __device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, d
   return scan_collected(L, min(L.n, kSelCap), above, target, nullptr);
 }
 
-// Per row: the cut (top-k, then top-p), and the fp32 chunk sums of the kept
-// weights 2^(l c - Mref) for the draw (without the draft token on one-hot
-// rows, as in the row pass), and their total.
+// The general search's cut of one row (top-k, then top-p, each by
+// select_cut) and its kept mass: the fp32 sum of the kept weights
+// 2^(l c - mref), without token xe (a one-hot draft's, as the row pass
+// leaves it out; -1: none).
+template <int DT, bool kVec>
+__device__ void general_cut(const char* row, int n_chunk, int V, SelLds& L, float c, double cd, float mref,
+                            int tk, float tp, int xe, float* thr_out, float* s_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t cut = 0u;
+  if (tk > 0 && tk < V) cut = select_cut<DT, kVec, false>(row, n_chunk, V, L, cd, mref, (double)tk, 0u);
+  if (tp < 1.f) {                                  // NaN compares false: off
+    const uint32_t cp = select_cut<DT, kVec, true>(row, n_chunk, V, L, cd, mref, (double)tp, cut);
+    if (cp) cut = cp;
+  }
+  const float thr = cut ? key_value(cut) : kNegInf;
+  float sm = 0.f;
+  for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t e) {
+    sm += (l >= thr && e != xe) ? fast_exp2(fmaf(l, c, -mref)) : 0.f;
+  });
+  sm = wave_sum_all(sm);
+  __syncthreads();                                 // earlier readers of L.wsum are done
+  if (lane == 0) L.wsum[wave] = sm;
+  __syncthreads();
+  *s_out = (L.wsum[0] + L.wsum[1]) + (L.wsum[2] + L.wsum[3]);
+  *thr_out = thr;
+}
+
+// fp32 rows, after the row pass: per row the cut (general_cut) and the kept
+// mass, as a RowFilter for the filtered rule.
 // Four workgroups per CU: the passes are latency-bound, and the occupancy
 // this buys outweighs the few registers it spills.
 template <int MODE, int DT, bool kVec>
@@ -1898,15 +2167,16 @@ __global__ __launch_bounds__(kThreads, 4) void sv_select_kernel(Args A) {
   const int rowg = blockIdx.x;
   const int b = rowg / A.rows, r = rowg % A.rows;
   const Req rq = request(A, b);
+  // Rows past a certain rejection are never drawn from (one-hot drafts,
+  // top-k off): the kept mass of a top-p cut is at least top_p, so the
+  // filtered p'(x) <= p(x) / top_p, and u * top_p >= p(x) (with a margin for
+  // fp32 rounding) rejects position j whatever the cut; the rule stops at or
+  // before it. p(x) is the unfiltered probability from the row pass; a
+  // draft token outside [0, V) is always rejected. When the caller takes
+  // only tokens (no p / q outputs) such a row needs no cut.
+  bool past_reject = false;
   if constexpr (MODE == kOneHot) {
-    // Rows past a certain rejection are not cut when the caller takes only
-    // tokens (no p / q outputs) and top-k is off: the kept mass of a top-p
-    // cut is at least top_p, so the filtered p'(x) <= p(x) / top_p, and
-    // u * top_p >= p(x) (with a margin for fp32 rounding) rejects position j
-    // whatever the cut; the rule stops at or before it and never reads the
-    // cuts of later rows. p(x) is the unfiltered probability from the row
-    // pass. A draft token outside [0, V) is always rejected.
-    if (!A.out_p && !A.out_q && r > 0 && r <= A.K) {
+    if (r > 0 && r <= A.K) {
       __shared__ int s_skip;
       if (wave == 0) {
         const int tk0 = A.top_k ? A.top_k[b] : 0;
@@ -1941,11 +2211,11 @@ __global__ __launch_bounds__(kThreads, 4) void sv_select_kernel(Args A) {
         if (lane == 0) s_skip = skip ? 1 : 0;
       }
       __syncthreads();
-      if (s_skip) return;
+      past_reject = s_skip != 0;
+      if (past_reject && !A.out_p && !A.out_q) return;
     }
   }
   const char* row = row_ptr(A, rq, r);
-  float* fp = A.fpart + (int64_t)rowg * A.n_chunk;
   const float T = A.temperature[b];
   // the row's largest scaled logit, from the row pass (which leaves a
   // one-hot draft token out of its sums)
@@ -1963,53 +2233,237 @@ __global__ __launch_bounds__(kThreads, 4) void sv_select_kernel(Args A) {
     if ((unsigned)xe < (unsigned)A.V) mref = fmaxf(mref, A.gath[rowg] * c);
     else xe = -1;
   }
-  __syncthreads();
   if (!(T > 0.f && T < __builtin_inff()) || mref == kNegInf || mref != mref) {
-    for (int ch = tid; ch < A.n_chunk; ch += kThreads) fp[ch] = 0.f;
     if (tid == 0) A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
     return;
   }
   const double cd = 1.4426950408889634 / (double)T;
   const int tk = A.top_k ? A.top_k[b] : 0;
   const float tp = A.top_p ? A.top_p[b] : 1.f;
-  uint32_t cut = 0u;
-  if (tk > 0 && tk < A.V)
-    cut = select_cut<DT, kVec, false>(row, A.n_chunk, A.V, L, cd, mref, (double)tk, 0u);
-  if (tp < 1.f) {
-    const uint32_t cp = select_cut<DT, kVec, true>(row, A.n_chunk, A.V, L, cd, mref, (double)tp, cut);
-    if (cp) cut = cp;
+  float thr, s;
+  general_cut<DT, kVec>(row, A.n_chunk, A.V, L, c, cd, mref, tk, tp, xe, &thr, &s);
+  if (tid == 0) A.rf[rowg] = RowFilter{mref, thr, s, 0.f};
+}
+
+// bf16 rows, one workgroup per row and no row pass before it: the one-pass
+// histogram, then the row's largest value, its cuts and kept mass, as a
+// RowFilter; also the row's draft-token logit, and (row 0's workgroup) the
+// request's uniforms, which the row pass draws on unfiltered calls.
+template <int MODE, bool kVec>
+__global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
+  constexpr int kCE = Chunk<kBF16>::kElems;
+  __shared__ SelLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rowg = blockIdx.x;
+  const int b = rowg / A.rows, r = rowg % A.rows;
+  const Req rq = request(A, b);
+  const char* row = row_ptr(A, rq, r);
+  if (r == 0 && wave == 0 && lane < A.R) {
+    const Philox4 rnd = philox4x64_10((uint64_t)lane, (uint64_t)b, A.offset, 0ull, A.seeds[b], 0ull);
+    A.unif[(int64_t)b * A.R + lane] = make_float2(top24(rnd.w0), top24(rnd.w1));
   }
-  const float thr = cut ? key_value(cut) : kNegInf;
-  // chunk sums of the kept weights, one wave per chunk, in the draw's layout
-  constexpr int E = Chunk<DT>::kElems / 64;
-  float tot = 0.f;
-  for (int ch = wave; ch < A.n_chunk; ch += kWaves) {
-    const int64_t c0 = (int64_t)ch * Chunk<DT>::kElems;
-    float x[E];
-    load_lane_run<DT, kVec, E>(row, c0, A.V, x);
-    const int64_t e0 = c0 + (int64_t)lane * E;
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < E; ++k)
-      s += (x[k] >= thr && e0 + k != xe) ? fast_exp2(fmaf(x[k], c, -mref)) : 0.f;
-    s = wave_sum_all(s);
-    if (lane == 0) fp[ch] = s;
-    tot += s;
+  // this row's draft token (target rows 0..K-1, draft rows) and its logit
+  const int i = r < A.R ? r : r - A.R;
+  int xt = i < rq.k ? A.tokens[rq.x0 + i] : -1;
+  if ((unsigned)xt >= (unsigned)A.V) xt = -1;
+  float lx = kNegInf;
+  if (tid == 0 && xt >= 0) {
+    lx = load_one<kBF16>(row, xt);
+    A.gath[rowg] = lx;
   }
-  if (lane == 0) L.wsum[wave] = tot;
+  const int xe = MODE == kOneHot ? xt : -1;        // left out of a one-hot row's sums
+  const float T = A.temperature[b];
+  if (!(T > 0.f && T < __builtin_inff())) {
+    if (tid == 0) A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
+    return;
+  }
+  const float c = kLog2e / T;
+  const double cd = 1.4426950408889634 / (double)T;
+  const int tk = A.top_k ? A.top_k[b] : 0;
+  const float tp = A.top_p ? A.top_p[b] : 1.f;
+
+  {
+    uint4* z = reinterpret_cast<uint4*>(L.hcnt);
+    for (int j = tid; j < kHWords / 4; j += kThreads) z[j] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (tid == 0) {
+    L.tiny_n = 0u;
+    L.ninf_n = 0u;
+    L.tiny_max = 0u;
+    L.big = 0;
+  }
+  if (tid < 64) L.tab[tid] = exp2((double)tid / 64.0);
   __syncthreads();
-  if (tid == 0)
-    A.rf[rowg] = RowFilter{mref, thr, (L.wsum[0] + L.wsum[1]) + (L.wsum[2] + L.wsum[3]), 0.f};
+  hist_pass<kVec>(row, A.n_chunk, A.V, L);
+
+  const unsigned n_tiny = L.tiny_n;
+  const unsigned n_ninf = L.ninf_n - (unsigned)((int64_t)A.n_chunk * kCE - A.V);   // less the padding
+  bool general = L.big != 0;
+  if (!general) {
+    HBlock hb;
+    hist_block_load(L, n_tiny, n_ninf, hb);
+    uint32_t cl = hb.nx;                           // this run's count
+#pragma unroll
+    for (int j = 0; j < kHPerT; ++j) cl += hb.n[j];
+    int j1 = kHPerT;                               // its first counted table position
+#pragma unroll
+    for (int j = kHPerT - 1; j >= 0; --j) j1 = hb.n[j] ? j : j1;
+    int o_max, o_k = -1;
+    double at;
+    // the largest value: the first counted position
+    hist_pick(L, j1 < kHPerT ? hb.o0 + j1 : (hb.nx ? hb.ox : INT_MAX), 0.0, &o_max, &at);
+    // counts: the top-k cut, and the total (a carry between the halves of a
+    // word, possible only when V / 2 > 65535, shows as a total other than V)
+    const bool k_on = tk > 0 && tk < A.V;
+    if (k_on || A.V > 2 * 65535) {
+      double ce, ct;
+      const double ci = block_scan_x((double)cl, L, &ce, &ct);
+      general = ct != (double)A.V;
+      if (k_on && !general) {
+        const double target = (double)tk;
+        int mine = INT_MAX;
+        if (ce < target && ci >= target) {         // exact: integer sums
+          double run = ce;
+#pragma unroll
+          for (int j = 0; j < kHPerT; ++j) {
+            run += (double)hb.n[j];
+            if (mine == INT_MAX && hb.n[j] && run >= target) mine = hb.o0 + j;
+          }
+          if (mine == INT_MAX) mine = hb.ox;       // the extra position completes it
+        }
+        hist_pick(L, mine, 0.0, &o_k, &at);
+      }
+    }
+    if (!general && (o_max < 0 || o_max == kHOrd - 1)) {   // nothing but -inf: no mass
+      if (tid == 0) A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
+      return;
+    }
+    if (o_k == kHOrd - 1) o_k = -1;                // the k-th largest is -inf: keep all
+    if (!general && o_k != kHBins) {
+      const float lmax = o_max == kHBins ? key_value(L.tiny_max) : hist_value(o_max);
+      const float mref = lmax * c;
+      const int o_lim = o_k >= 0 ? o_k : kHOrd - 1;   // positions past it weigh nothing
+      // tiny magnitudes: 2^-mref sum (1 + x + x^2/2 + x^3/6), x = l cd ln 2
+      double s1 = 0.0, s2 = 0.0, s3 = 0.0;
+      for (int w = 0; w < kWaves; ++w) {
+        s1 += (double)L.tiny_w[w][0];
+        s2 += (double)L.tiny_w[w][1];
+        s3 += (double)L.tiny_w[w][2];
+      }
+      const double a = cd * 0.69314718055994530942;
+      const double m_tiny = exp2_weight(-(double)mref, L.tab) *
+                            ((double)n_tiny + a * s1 + a * a * s2 * 0.5 + a * a * a * s3 * (1.0 / 6.0));
+      const double mx = (hb.nx && hb.ox == kHBins && hb.ox <= o_lim) ? m_tiny : 0.0;
+      // The run's mass. Its weights fall by the factor 2^(-u c) per
+      // position: with the whole run below the cut limit and its weights
+      // spanning at most 2^960, Horner's rule from the largest value down,
+      // scaled by the smallest value's weight (at most the largest's, about
+      // 1 or less); otherwise, per position from the first counted one.
+      const double ucd = (double)hb.u * cd;
+      const int lim = o_lim - hb.o0;               // positions j <= lim count
+      double ml = 0.0;
+      if (j1 < kHPerT && lim >= kHPerT - 1 && ucd * (kHPerT - 1) <= 960.0) {
+        const double g = exp2_weight(ucd, L.tab);
+        double acc = 0.0;
+#pragma unroll
+        for (int j = 0; j < kHPerT; ++j) acc = fma(acc, g, (double)hb.n[j]);
+        ml = acc * exp2_weight((double)(hb.v0 - (float)(kHPerT - 1) * hb.u) * cd - (double)mref, L.tab);
+      } else if (j1 < kHPerT && lim >= j1) {
+        const double rr = exp2_weight(-ucd, L.tab);
+        double w = exp2_weight((double)(hb.v0 - (float)j1 * hb.u) * cd - (double)mref, L.tab);
+#pragma unroll
+        for (int j = 0; j < kHPerT; ++j) {
+          if (j >= j1) {
+            ml += j <= lim ? (double)hb.n[j] * w : 0.0;
+            w *= rr;
+          }
+        }
+      }
+      ml += mx;
+      double me, zk;
+      const double mi = block_scan_x(ml, L, &me, &zk);
+      const bool p_on = tp < 1.f;                  // NaN compares false: off
+      int o_p = -1;
+      double at_p = 0.0;
+      if (p_on) {
+        const double target = fmax((double)tp * zk, __DBL_MIN__);
+        int mine = INT_MAX;
+        double mine_at = 0.0;
+        if (me < target && mi >= target) {
+          const double rr = exp2_weight(-ucd, L.tab);
+          double run = me, w = j1 < kHPerT ? exp2_weight((double)(hb.v0 - (float)j1 * hb.u) * cd - (double)mref, L.tab)
+                                           : 0.0;
+          int last = -1;
+#pragma unroll
+          for (int j = 0; j < kHPerT; ++j) {
+            if (j >= j1) {
+              const double x = j <= lim ? (double)hb.n[j] * w : 0.0;
+              w *= rr;
+              if (x > 0.0 && run < target) {
+                run += x;
+                last = hb.o0 + j;
+              }
+            }
+          }
+          if (run < target && mx > 0.0) {
+            run += mx;
+            last = hb.ox;
+          }
+          // a sequential sum that rounds short of the scan's: the run's
+          // last position of positive mass
+          if (last >= 0) {
+            mine = last;
+            mine_at = run >= target ? run : mi;
+          }
+        }
+        hist_pick(L, mine, mine_at, &o_p, &at_p);
+      }
+      if (!(p_on && o_p == kHBins)) {              // a cut among the tiny magnitudes: general search
+        int o_c = o_k;
+        double kept = zk;
+        if (p_on && o_p >= 0) {
+          o_c = o_p;
+          kept = at_p;
+        }
+        if (tid == 0) {
+          const float thr = o_c >= 0 ? hist_value(o_c) : kNegInf;
+          double sk = kept;
+          if (xe >= 0 && lx >= thr) sk -= exp2_weight((double)lx * cd - (double)mref, L.tab);
+          A.rf[rowg] = RowFilter{mref, thr, (float)fmax(sk, 0.0), 0.f};
+        }
+        return;
+      }
+    }
+  }
+  // the general search, with the row's largest logit from one more pass
+  float m = kNegInf;
+  for_each_logit<kBF16, kVec>(row, A.n_chunk, A.V, [&](float l, int64_t) { m = fmaxf(m, l); });
+  m = wave_max_all(m);
+  __syncthreads();
+  if (lane == 0) L.wsum[wave] = m;
+  __syncthreads();
+  const float mref = fmaxf(fmaxf(L.wsum[0], L.wsum[1]), fmaxf(L.wsum[2], L.wsum[3])) * c;
+  if (mref == kNegInf || mref != mref) {
+    if (tid == 0) A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
+    return;
+  }
+  float thr, s;
+  general_cut<kBF16, kVec>(row, A.n_chunk, A.V, L, c, cd, mref, tk, tp, xe, &thr, &s);
+  if (tid == 0) A.rf[rowg] = RowFilter{mref, thr, s, 0.f};
 }
 
 // The rule on filtered rows, one wave per request: p_i(x_i) = w(x_i) / S'_i
-// with the kept weights and sums of the select pass.
+// with the kept weights and sums of the select pass. A token still to be
+// drawn from a filtered target row (a one-hot residual, the bonus token)
+// is left to the caller: rc.draw = 1, with its position, uniform, the row's
+// reference and cut, and the token to leave out.
 // write_out: as for sample_tail (false: only return the decision, for the
 // residual pass's other workgroups).
 template <int DT, bool kVec, int MODE>
 __device__ Record filtered_tail(const Args& A, int b, bool write_out = true) {
   Record rc;
   rc.pending = 0;
+  rc.draw = 0;
   const int lane = threadIdx.x & 63;
   const Req rq = request(A, b);
   const int K = A.K, V = A.V, R = A.R;
@@ -2081,18 +2535,76 @@ __device__ Record filtered_tail(const Args& A, int b, bool write_out = true) {
     if (write_out && lane == 0) A.rec[b].pending = 0;
     if (!write_out) return rc;                     // the bonus draw is the writer's
   }
-  const int xe = (MODE == kOneHot && a < K) ? lane_i(x, a) : -1;
-  const float* fpa = A.fpart + (rowg0 + a) * A.n_chunk;
-  int y = draw_from_partials<DT, kVec, false, true>(A, b, rq, a, c, Ma, xe, ua, ta,
-                                                    [&](int s) { return make_float2(Ma, fpa[s]); });
-  if (y < 0) y = ((unsigned)xe < (unsigned)V) ? xe : 0;    // residual without mass: p_a's mode
-  if (lane == 0) otok[a] = y;
+  // the token at a is drawn from the filtered target row a (one-hot: without
+  // x_a), by the caller's workgroup (filtered_draw)
+  rc.draw = 1;
+  rc.a = a;
+  rc.c = c;
+  rc.u = ua;
+  rc.Mp = Ma;
+  rc.tp = ta;
+  rc.xe = (MODE == kOneHot && a < K) ? lane_i(x, a) : -1;
   return rc;
 }
 
+// Sums of the kept weights 2^(l c - M) (l >= thr, token xe left out) of
+// chunks w, w + nw, ... of one row, published to out[chunk]; lane l sums
+// the E consecutive logits of the chunk that draw_from_partials gives it.
+template <int DT, bool kVec>
+__device__ void kept_chunk_sums(const char* row, int n_chunk, int V, float c, float M, float thr, int xe,
+                                float* out, int w, int nw) {
+  constexpr int E = Chunk<DT>::kElems / 64;
+  const int lane = threadIdx.x & 63;
+  for (int ch = w; ch < n_chunk; ch += nw) {
+    const int64_t c0 = (int64_t)ch * Chunk<DT>::kElems;
+    float x[E];
+    load_lane_run<DT, kVec, E>(row, c0, V, x);
+    const int64_t e0 = c0 + (int64_t)lane * E;
+    float sm = 0.f;
+#pragma unroll
+    for (int k = 0; k < E; ++k) sm += (x[k] >= thr && e0 + k != xe) ? fast_exp2(fmaf(x[k], c, -M)) : 0.f;
+    sm = wave_sum_all(sm);
+    if (lane == 0) publish(out + ch, sm);
+  }
+}
+
+// The token at rc.a of request b, drawn from its filtered target row (the
+// kept weights; one-hot: without rc.xe) by nw waves of the calling
+// workgroup, all of whose threads call when nw > 1: the chunk sums go to
+// the row's workspace slice, then wave 0 finds the chunk and the token.
+// Only the one row a request draws from is read.
+template <int DT, bool kVec>
+__device__ void filtered_draw(const Args& A, int b, const Record& rc, int nw) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const Req rq = request(A, b);
+  float* fp = A.fpart + ((int64_t)b * A.rows + rc.a) * A.n_chunk;
+  kept_chunk_sums<DT, kVec>(row_ptr(A, rq, rc.a), A.n_chunk, A.V, rc.c, rc.Mp, rc.tp, rc.xe, fp, wave, nw);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);                   // this wave's sums are in memory
+  if (nw > 1) __syncthreads();
+  if (wave != 0) return;
+  int y = draw_from_partials<DT, kVec, false, true>(A, b, rq, rc.a, rc.c, rc.Mp, rc.xe, rc.u, rc.tp,
+                                                    [&](int s) { return make_float2(rc.Mp, fetch(fp + s)); });
+  if (y < 0) y = ((unsigned)rc.xe < (unsigned)A.V) ? rc.xe : 0;   // no kept mass: p_a's mode
+  if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + rc.a] = y;
+}
+
+// One workgroup per request: wave 0 runs the filtered rule, then the whole
+// workgroup draws the request's token.
+constexpr int kDrawThreads = 1024;
+
 template <int MODE, int DT, bool kVec>
-__global__ __launch_bounds__(64) void sv_ftail_kernel(Args A) {
-  filtered_tail<DT, kVec, MODE>(A, blockIdx.x);
+__global__ __launch_bounds__(kDrawThreads) void sv_ftail_kernel(Args A) {
+  __shared__ Record s_rc;
+  const int b = blockIdx.x;
+  if (threadIdx.x < 64) {
+    const Record rc = filtered_tail<DT, kVec, MODE>(A, b);
+    if (threadIdx.x == 0) s_rc = rc;
+  }
+  __syncthreads();
+  const Record rc = s_rc;
+  if (rc.draw) filtered_draw<DT, kVec>(A, b, rc, kDrawThreads / 64);
 }
 
 // ------------------------------------------------------ residual pass ---
@@ -2124,6 +2636,12 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
     }
     __syncthreads();
     rc = s_rc;
+    if constexpr (kFilt) {
+      if (rc.draw) {                               // all accepted: the bonus token, by this workgroup
+        filtered_draw<DT, kVec>(A, b, rc, kWaves);
+        return;
+      }
+    }
   } else {
     rc = A.rec[b];
   }
@@ -2199,11 +2717,12 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
     y = wave_pick<E>(w, c0, t_in);
   }
   if (y < 0) {
-    // p_a and q_a agree everywhere: draw from p_a with the row pass's partials
+    // p_a and q_a agree everywhere: draw from p_a
     if constexpr (kFilt) {
-      const float* fpa = A.fpart + ((int64_t)b * A.rows + a) * A.n_chunk;
-      y = draw_from_partials<DT, kVec, false, true>(A, b, req, a, c, rc.Mp, -1, rc.u, rc.tp,
-                                                    [&](int s) { return make_float2(rc.Mp, fpa[s]); });
+      Record d = rc;
+      d.xe = -1;
+      filtered_draw<DT, kVec>(A, b, d, 1);         // this wave alone
+      return;
     } else {
       y = draw_softmax_row<DT, kVec, kMask>(A, b, req, a, c, rc.Mp, -1, rc.u, S, false);
     }
@@ -2490,20 +3009,29 @@ void launch_residual_dt(const Args& A, bool vec, unsigned grid, hipStream_t st, 
   else        launch_residual_dd<DT, false>(A, vec, grid, st);
 }
 
-// Filtered verification: the row pass, the select pass (one workgroup per
-// row), then the filtered rule (one wave per request); with draft logits
-// the residual pass that follows runs the rule itself.
+// Filtered verification: per row the cut and kept mass (bf16: the one-pass
+// histogram kernel; fp32: the row pass, then the select pass), one
+// workgroup per row; then the filtered rule and the draw, one workgroup per
+// request. With draft logits the residual pass that follows runs the rule
+// itself.
 template <int MODE, int DT>
 void launch_filtered_dt(const Args& A, bool vec, unsigned grid, hipStream_t st) {
-  const dim3 rows((unsigned)((int64_t)A.B * A.rows)), reqs((unsigned)A.B), wave(64), wg(kThreads);
-  if (vec) {
-    SV_LAUNCH((sv_rows_kernel<MODE, DT, true, false, false, false>), grid, st, A);
-    hipLaunchKernelGGL((sv_select_kernel<MODE, DT, true>), rows, wg, 0, st, A);
-    if (MODE != kExplicit) hipLaunchKernelGGL((sv_ftail_kernel<MODE, DT, true>), reqs, wave, 0, st, A);
+  const dim3 rows((unsigned)((int64_t)A.B * A.rows)), reqs((unsigned)A.B), wg(kThreads), dwg(kDrawThreads);
+  if constexpr (DT == kBF16) {
+    if (vec) hipLaunchKernelGGL((sv_hselect_kernel<MODE, true>), rows, wg, 0, st, A);
+    else     hipLaunchKernelGGL((sv_hselect_kernel<MODE, false>), rows, wg, 0, st, A);
   } else {
-    SV_LAUNCH((sv_rows_kernel<MODE, DT, false, false, false, false>), grid, st, A);
-    hipLaunchKernelGGL((sv_select_kernel<MODE, DT, false>), rows, wg, 0, st, A);
-    if (MODE != kExplicit) hipLaunchKernelGGL((sv_ftail_kernel<MODE, DT, false>), reqs, wave, 0, st, A);
+    if (vec) {
+      SV_LAUNCH((sv_rows_kernel<MODE, DT, true, false, false, false>), grid, st, A);
+      hipLaunchKernelGGL((sv_select_kernel<MODE, DT, true>), rows, wg, 0, st, A);
+    } else {
+      SV_LAUNCH((sv_rows_kernel<MODE, DT, false, false, false, false>), grid, st, A);
+      hipLaunchKernelGGL((sv_select_kernel<MODE, DT, false>), rows, wg, 0, st, A);
+    }
+  }
+  if constexpr (MODE != kExplicit) {
+    if (vec) hipLaunchKernelGGL((sv_ftail_kernel<MODE, DT, true>), reqs, dwg, 0, st, A);
+    else     hipLaunchKernelGGL((sv_ftail_kernel<MODE, DT, false>), reqs, dwg, 0, st, A);
   }
 }
 

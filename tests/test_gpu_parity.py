@@ -712,6 +712,46 @@ def test_filtered_ties_and_flat_rows():
     check_filtered(wl, "ties", top_k, top_p, near_frac=0.5)
 
 
+def test_filtered_bf16_rows_outside_the_table():
+    """bf16 rows whose values leave the one-pass table or strain it: an all-equal
+    row, few distinct values (wide ties), zeros and magnitudes below 2^-16
+    mixed in (and a row of zeros only, whose cut falls among them), half the
+    vocabulary at -inf, and a logit beyond 2^16; each under a spread of top-k
+    and top-p."""
+    B, K, V = 12, 3, 3 * 8192 + 5
+    wl = make("c3_onehot", data_seed=431, B=B, K=K, V=V)
+    vals = oracle.logits_f64(wl["target"].reshape(-1), "bf16").reshape(wl["target"].shape)
+    rng = np.random.default_rng(432)
+    vals[0] = 1.5
+    vals[1] = np.round(vals[1])
+    tiny = rng.choice([0.0, -0.0, 2.0 ** -20, -(2.0 ** -18), 3.0 * 2.0 ** -17], size=vals[2].shape)
+    vals[2] = np.where(rng.random(vals[2].shape) < 0.3, tiny, vals[2])
+    vals[3] = 0.0
+    vals[4, :, : V // 2] = -np.inf
+    vals[5, :, 17] = 70000.0
+    vals[6] = np.where(rng.random(vals[6].shape) < 0.5, 0.0, vals[6])
+    vals[7, :, :100] = -np.inf
+    vals[7, :, 100:] = np.round(vals[7, :, 100:] * 4) / 4
+    wl = dict(wl, target=f32_to_bf16_bits(vals.astype(np.float32)))
+    top_k = np.array([1, 10, 50, 7, 3, 0, 20000, 2, 0, 5, 100, V], np.int32)
+    top_p = np.array([0.9, 0.5, 0.95, 0.3, 0.8, 0.95, 1.0, 0.99, 0.95, 0.0, 0.7, 0.6], np.float32)
+    check_filtered(wl, "bf16 rows outside the table", top_k, top_p, near_frac=0.5)
+    check_filtered(wl, "bf16 rows outside the table, top-p only", None, np.full(B, 0.9, np.float32),
+                   near_frac=0.5)
+
+
+def test_filtered_bf16_counter_carry():
+    """V > 2 * 65535 with every logit equal: each half of a counter word would
+    pass 65535 (a carry into the other half); the row takes the general search."""
+    wl = make("c3_onehot", data_seed=433, B=3, K=1, V=140001)
+    vals = oracle.logits_f64(wl["target"].reshape(-1), "bf16").reshape(wl["target"].shape)
+    vals[0] = -2.25
+    vals[1, :, ::2] = 0.75
+    wl = dict(wl, target=f32_to_bf16_bits(vals.astype(np.float32)))
+    check_filtered(wl, "bf16 counter carry", np.array([0, 3, 70000], np.int32),
+                   np.array([0.9, 0.95, 0.5], np.float32), near_frac=1.0)
+
+
 def test_filtered_bf16_explicit_draft():
     wl = make("c2_stoch", data_seed=422, B=12, V=8192 + 100)
     wl = dict(wl, target=f32_to_bf16_bits(wl["target"]), dtype="bf16",
