@@ -307,7 +307,7 @@ __device__ inline bool wait_tag(const uint64_t* p, uint32_t tag, int limit) {
 // positive weight when rounding leaves none, with *t_in = +inf; -1 if no
 // weight at all) and *t_in = t minus the weight before it.
 template <class WFn>
-__device__ float wave_locate(int n, float u, WFn W, int* found, float* t_in) {
+__device__ __forceinline__ float wave_locate(int n, float u, WFn W, int* found, float* t_in) {
   const int lane = threadIdx.x & 63;
   if (n <= 64) {                                   // one weight per lane: a single pass
     const float w = lane < n ? W(lane) : 0.f;
@@ -355,7 +355,7 @@ __device__ float wave_locate(int n, float u, WFn W, int* found, float* t_in) {
 // c0 + l * E ... + E - 1: the smallest logit whose running weight sum
 // exceeds t_in, else the last logit of positive weight, else -1.
 template <int E>
-__device__ int wave_pick(const float (&w)[E], int64_t c0, float t_in) {
+__device__ __forceinline__ int wave_pick(const float (&w)[E], int64_t c0, float t_in) {
   const int lane = threadIdx.x & 63;
   float vs = 0.f;
 #pragma unroll
@@ -386,6 +386,24 @@ __device__ __forceinline__ void load_lane_run(const char* row, int64_t c0, int V
   } else {
 #pragma unroll
     for (int k = 0; k < E; ++k) x[k] = (e0 + k < V) ? load_one<DT>(row, e0 + k) : kNegInf;
+  }
+}
+
+// load_lane_run for the filtered draw: off the 16-byte path every load is
+// issued (at a clamped index) before any is used, so that they are in
+// flight together; logits past V then read as -inf.
+template <int DT, bool kVec, int E>
+__device__ __forceinline__ void load_lane_run_all(const char* row, int64_t c0, int V, float (&x)[E]) {
+  constexpr int kPer = Elem<DT>::kPerVec;
+  const int64_t e0 = c0 + (int64_t)(threadIdx.x & 63) * E;
+  if (kVec && e0 + E <= V) {
+#pragma unroll
+    for (int j = 0; j < E / kPer; ++j) load_vec16<DT>(row + (e0 + j * kPer) * Elem<DT>::kBytes, &x[j * kPer]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < E; ++k) x[k] = load_one<DT>(row, min(e0 + k, (int64_t)V - 1));
+#pragma unroll
+    for (int k = 0; k < E; ++k) x[k] = e0 + k < V ? x[k] : kNegInf;
   }
 }
 
@@ -1646,14 +1664,14 @@ struct alignas(16) SelLds {
   };
   double scan[kThreads];
   double tab[64];                                  // 2^(j / 64)
-  double wtot[kWaves];
-  double at;
+  double wtot[kWaves], wtot2[kWaves];             // wave totals of the count and mass scans
   float wsum[kWaves];
   float tiny_w[kWaves][3];                         // per wave: sums of tiny l, l^2, l^3
   int n, sel;
   uint32_t kfloor;
   unsigned tiny_n, ninf_n, tiny_max;               // tiny count, -inf count, largest tiny order key
   int big;                                         // a value outside the table that is not -inf
+  int sel_max, sel_k, sel_p;                       // picked positions (INT_MAX: none)
 };
 
 // Total order of logit values as unsigned keys (-0 sorts with +0).
@@ -1828,11 +1846,12 @@ __device__ uint32_t scan_collected(SelLds& L, int n, double above, double target
 
 // Every 16-byte vector of a bf16 row once, raw: wave w of the workgroup
 // streams chunks w, w + kWaves, ... with the next chunk's loads in flight
-// while the current one is used (as in the row pass); f(word, e) gets each
+// while the current one is used (as in the row pass); pre() runs in every
+// thread once the first loads are in flight; f(word, e) gets each
 // 32-bit word (logits e and e + 1) once. Logits at or past V read as bf16
 // -inf (0xFF80).
-template <bool kVec, class F>
-__device__ __forceinline__ void for_each_word_bf16(const char* row, int n_chunk, int V, F f) {
+template <bool kVec, class P, class F>
+__device__ __forceinline__ void for_each_word_bf16(const char* row, int n_chunk, int V, P pre, F f) {
   constexpr int kCE = Chunk<kBF16>::kElems;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -1850,8 +1869,10 @@ __device__ __forceinline__ void for_each_word_bf16(const char* row, int n_chunk,
   int ch = wave;
   const int ch_end = kVec ? n_full : 0;
   ChunkRaw ra, rb;
-  if (ch < ch_end) {
-    issue_chunk<kBF16>(row, (int64_t)ch * kCE, ra);
+  const bool piped = ch < ch_end;
+  if (piped) issue_chunk<kBF16>(row, (int64_t)ch * kCE, ra);
+  pre();
+  if (piped) {
     while (true) {
       int nx = ch + kWaves;
       bool more = nx < ch_end;
@@ -1896,8 +1917,9 @@ struct HistRare {
   }
 };
 
-// One pass over a bf16 row into the counters (zeroed by the caller, with
-// the tallies), then the lanes' tallies folded into L. A magnitude is
+// One pass over a bf16 row into the counters (zeroed, with the tallies and
+// pick slots, while the first loads are in flight), then the lanes'
+// tallies folded into L. A magnitude is
 // clamped to the table's range plus one spare word each side, so a value
 // outside the table costs no extra instruction on the common path; the
 // lanes holding one also take the rare path.
@@ -1906,7 +1928,22 @@ __device__ __forceinline__ void hist_pass(const char* row, int n_chunk, int V, S
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr uint32_t lo = kHMagLo - 1u, hi = kHMagLo + kHBins;
   HistRare t{0.f, 0.f, 0.f, 0u, 0u, 0u, false};
-  for_each_word_bf16<kVec>(row, n_chunk, V, [&](uint32_t w, int64_t) {
+  auto zero = [&]() {
+    uint4* z = reinterpret_cast<uint4*>(L.hcnt);
+    for (int j = threadIdx.x; j < kHWords / 4; j += kThreads) z[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x == 0) {
+      L.tiny_n = 0u;
+      L.ninf_n = 0u;
+      L.tiny_max = 0u;
+      L.big = 0;
+      L.sel_max = INT_MAX;
+      L.sel_k = INT_MAX;
+      L.sel_p = INT_MAX;
+    }
+    if (threadIdx.x < 64) L.tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+    __syncthreads();
+  };
+  for_each_word_bf16<kVec>(row, n_chunk, V, zero, [&](uint32_t w, int64_t) {
     const uint32_t m0 = w & 0x7FFFu, m1 = (w >> 16) & 0x7FFFu;
     const uint32_t c0 = min(max(m0, lo), hi), c1 = min(max(m1, lo), hi);
     const uint32_t i0 = c0 + ((w >> 15) & 1u) * (uint32_t)kHNeg, i1 = c1 + (w >> 31) * (uint32_t)kHNeg;
@@ -1948,6 +1985,7 @@ __device__ __forceinline__ float hist_value(int o) {
 // kThreads / 2 - 1 the tiny position and for the last thread the -inf one.
 constexpr int kHPerT = 2 * kHBins / kThreads;
 static_assert(kHPerT == 32 && kHBins % kHPerT == 0, "a run is a quarter binade");
+static_assert(kThreads == 4 * 64 && kWaves == 4, "two waves per table");
 static_assert(kHOff % 4 == 0 && kHNeg % 4 == 0 && kHWords % 4 == 0, "16-byte aligned runs");
 struct HBlock {
   uint32_t n[kHPerT];                              // counts
@@ -1959,7 +1997,9 @@ struct HBlock {
 
 __device__ __forceinline__ void hist_block_load(const SelLds& L, unsigned n_tiny, unsigned n_ninf, HBlock& hb) {
   const int t = threadIdx.x;
-  const bool pos = t < kThreads / 2;
+  // waves 0 and 1 hold the positive table, 2 and 3 the negative one: a
+  // uniform branch, so that the runs' words are picked by constant indices
+  const bool pos = __builtin_amdgcn_readfirstlane(t >> 6) < kWaves / 2;
   const int rel = pos ? kHBins - kHPerT * (t + 1) : kHPerT * (t - kThreads / 2);   // magnitude - kHMagLo
   const uint4* q = reinterpret_cast<const uint4*>(L.hcnt + kHOff + rel + (pos ? 0 : kHNeg));
   uint32_t w[kHPerT];
@@ -1971,10 +2011,12 @@ __device__ __forceinline__ void hist_block_load(const SelLds& L, unsigned n_tiny
     w[4 * k + 2] = x.z;
     w[4 * k + 3] = x.w;
   }
+  if (pos) {                                       // positive values: descending bits
 #pragma unroll
-  for (int j = 0; j < kHPerT; ++j) {
-    const uint32_t x = pos ? w[kHPerT - 1 - j] : w[j];   // positive values: descending bits
-    hb.n[j] = (x & 0xFFFFu) + (x >> 16);
+    for (int j = 0; j < kHPerT; ++j) hb.n[j] = (w[kHPerT - 1 - j] & 0xFFFFu) + (w[kHPerT - 1 - j] >> 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kHPerT; ++j) hb.n[j] = (w[j] & 0xFFFFu) + (w[j] >> 16);
   }
   const uint32_t mag0 = kHMagLo + (uint32_t)(pos ? rel + kHPerT - 1 : rel);
   hb.o0 = pos ? kHPerT * t : kHBins + 1 + kHPerT * (t - kThreads / 2);
@@ -1984,39 +2026,48 @@ __device__ __forceinline__ void hist_block_load(const SelLds& L, unsigned n_tiny
   hb.ox = t == kThreads / 2 - 1 ? kHBins : kHOrd - 1;
 }
 
-// After a block_scan_x: every thread passes its candidate position (INT_MAX:
-// none) and the running sum there; all get the smallest candidate and its
-// sum.
-__device__ __forceinline__ void hist_pick(SelLds& L, int mine, double mine_at, int* pos, double* at) {
-  if (threadIdx.x == 0) L.sel = INT_MAX;
+// The thread holding ordered position o.
+__device__ __forceinline__ int hist_owner(int o) {
+  if (o < kHBins) return o / kHPerT;
+  if (o == kHBins) return kThreads / 2 - 1;
+  if (o == kHOrd - 1) return kThreads - 1;
+  return kThreads / 2 + (o - kHBins - 1) / kHPerT;
+}
+
+// Every thread passes its candidate position (INT_MAX: none) and the
+// running sum there; returns the smallest candidate over the workgroup (-1:
+// none), gathered in *slot (INT_MAX since the row's start), and its sum in
+// *at (from L.scan, where each candidate leaves its own).
+__device__ __forceinline__ int hist_pick(SelLds& L, int* slot, int mine, double mine_at, double* at) {
+  if (mine != INT_MAX) {
+    atomicMin(slot, mine);
+    L.scan[threadIdx.x] = mine_at;
+  }
   __syncthreads();
-  if (mine != INT_MAX) atomicMin(&L.sel, mine);
-  __syncthreads();
-  if (mine != INT_MAX && mine == L.sel) L.at = mine_at;
-  __syncthreads();
-  *pos = L.sel == INT_MAX ? -1 : L.sel;
-  *at = L.at;
-  __syncthreads();                                 // L.sel and L.at are free again
+  const int o = *slot;
+  if (o == INT_MAX) return -1;
+  *at = L.scan[hist_owner(o)];
+  return o;
 }
 
 // Inclusive scan of one double per thread (lanes in order within a wave,
 // waves in order). *excl gets the previous thread's result bit for bit and
 // *total the last thread's, so that exactly the thread whose range holds a
 // crossing of a threshold sees excl < t <= incl (up to the order of equal
-// partial sums).
-__device__ __forceinline__ double block_scan_x(double v, SelLds& L, double* excl, double* total) {
+// partial sums). wtot: kWaves doubles that no thread reads at the call
+// (each scan of a row takes its own).
+__device__ __forceinline__ double block_scan_x(double v, double* wtot, double* excl, double* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int off = 1; off < 64; off <<= 1) {
     const double t = __shfl_up(v, off);
     if (lane >= off) v += t;
   }
-  __syncthreads();                                 // earlier readers of L.wtot are done
-  if (lane == 63) L.wtot[wave] = v;
+  if (lane == 63) wtot[wave] = v;
   __syncthreads();
   double pre = 0.0, tot = 0.0;
   for (int w = 0; w < kWaves; ++w) {
     if (w == wave) pre = tot;
-    tot += L.wtot[w];
+    tot += wtot[w];
   }
   const double incl = pre + v;
   const double prev = __shfl_up(incl, 1);
@@ -2258,23 +2309,29 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
   const int b = rowg / A.rows, r = rowg % A.rows;
   const Req rq = request(A, b);
   const char* row = row_ptr(A, rq, r);
-  if (r == 0 && wave == 0 && lane < A.R) {
-    const Philox4 rnd = philox4x64_10((uint64_t)lane, (uint64_t)b, A.offset, 0ull, A.seeds[b], 0ull);
-    A.unif[(int64_t)b * A.R + lane] = make_float2(top24(rnd.w0), top24(rnd.w1));
-  }
-  // this row's draft token (target rows 0..K-1, draft rows) and its logit
+  // row 0's workgroup: the request's uniforms, by wave 0 once the others
+  // are done (nothing here waits for them)
+  auto draw_uniforms = [&]() {
+    if (r == 0 && wave == 0 && lane < A.R) {
+      const Philox4 rnd = philox4x64_10((uint64_t)lane, (uint64_t)b, A.offset, 0ull, A.seeds[b], 0ull);
+      A.unif[(int64_t)b * A.R + lane] = make_float2(top24(rnd.w0), top24(rnd.w1));
+    }
+  };
+  // this row's draft token (target rows 0..K-1, draft rows); its logit's
+  // load stays in flight during the pass
   const int i = r < A.R ? r : r - A.R;
   int xt = i < rq.k ? A.tokens[rq.x0 + i] : -1;
   if ((unsigned)xt >= (unsigned)A.V) xt = -1;
   float lx = kNegInf;
-  if (tid == 0 && xt >= 0) {
-    lx = load_one<kBF16>(row, xt);
-    A.gath[rowg] = lx;
-  }
+  if (tid == 0 && xt >= 0) lx = load_one<kBF16>(row, xt);
   const int xe = MODE == kOneHot ? xt : -1;        // left out of a one-hot row's sums
   const float T = A.temperature[b];
   if (!(T > 0.f && T < __builtin_inff())) {
-    if (tid == 0) A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
+    if (tid == 0) {
+      A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
+      if (xt >= 0) A.gath[rowg] = lx;
+    }
+    draw_uniforms();
     return;
   }
   const float c = kLog2e / T;
@@ -2282,19 +2339,8 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
   const int tk = A.top_k ? A.top_k[b] : 0;
   const float tp = A.top_p ? A.top_p[b] : 1.f;
 
-  {
-    uint4* z = reinterpret_cast<uint4*>(L.hcnt);
-    for (int j = tid; j < kHWords / 4; j += kThreads) z[j] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  if (tid == 0) {
-    L.tiny_n = 0u;
-    L.ninf_n = 0u;
-    L.tiny_max = 0u;
-    L.big = 0;
-  }
-  if (tid < 64) L.tab[tid] = exp2((double)tid / 64.0);
-  __syncthreads();
   hist_pass<kVec>(row, A.n_chunk, A.V, L);
+  if (tid == 0 && xt >= 0) A.gath[rowg] = lx;
 
   const unsigned n_tiny = L.tiny_n;
   const unsigned n_ninf = L.ninf_n - (unsigned)((int64_t)A.n_chunk * kCE - A.V);   // less the padding
@@ -2311,13 +2357,13 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
     int o_max, o_k = -1;
     double at;
     // the largest value: the first counted position
-    hist_pick(L, j1 < kHPerT ? hb.o0 + j1 : (hb.nx ? hb.ox : INT_MAX), 0.0, &o_max, &at);
+    o_max = hist_pick(L, &L.sel_max, j1 < kHPerT ? hb.o0 + j1 : (hb.nx ? hb.ox : INT_MAX), 0.0, &at);
     // counts: the top-k cut, and the total (a carry between the halves of a
     // word, possible only when V / 2 > 65535, shows as a total other than V)
     const bool k_on = tk > 0 && tk < A.V;
     if (k_on || A.V > 2 * 65535) {
       double ce, ct;
-      const double ci = block_scan_x((double)cl, L, &ce, &ct);
+      const double ci = block_scan_x((double)cl, L.wtot, &ce, &ct);
       general = ct != (double)A.V;
       if (k_on && !general) {
         const double target = (double)tk;
@@ -2331,11 +2377,12 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
           }
           if (mine == INT_MAX) mine = hb.ox;       // the extra position completes it
         }
-        hist_pick(L, mine, 0.0, &o_k, &at);
+        o_k = hist_pick(L, &L.sel_k, mine, 0.0, &at);
       }
     }
     if (!general && (o_max < 0 || o_max == kHOrd - 1)) {   // nothing but -inf: no mass
       if (tid == 0) A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
+      draw_uniforms();
       return;
     }
     if (o_k == kHOrd - 1) o_k = -1;                // the k-th largest is -inf: keep all
@@ -2381,7 +2428,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
       }
       ml += mx;
       double me, zk;
-      const double mi = block_scan_x(ml, L, &me, &zk);
+      const double mi = block_scan_x(ml, L.wtot2, &me, &zk);
       const bool p_on = tp < 1.f;                  // NaN compares false: off
       int o_p = -1;
       double at_p = 0.0;
@@ -2416,7 +2463,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
             mine_at = run >= target ? run : mi;
           }
         }
-        hist_pick(L, mine, mine_at, &o_p, &at_p);
+        o_p = hist_pick(L, &L.sel_p, mine, mine_at, &at_p);
       }
       if (!(p_on && o_p == kHBins)) {              // a cut among the tiny magnitudes: general search
         int o_c = o_k;
@@ -2431,6 +2478,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
           if (xe >= 0 && lx >= thr) sk -= exp2_weight((double)lx * cd - (double)mref, L.tab);
           A.rf[rowg] = RowFilter{mref, thr, (float)fmax(sk, 0.0), 0.f};
         }
+        draw_uniforms();
         return;
       }
     }
@@ -2445,11 +2493,13 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
   const float mref = fmaxf(fmaxf(L.wsum[0], L.wsum[1]), fmaxf(L.wsum[2], L.wsum[3])) * c;
   if (mref == kNegInf || mref != mref) {
     if (tid == 0) A.rf[rowg] = RowFilter{kNegInf, kNegInf, 0.f, 0.f};
+    draw_uniforms();
     return;
   }
   float thr, s;
   general_cut<kBF16, kVec>(row, A.n_chunk, A.V, L, c, cd, mref, tk, tp, xe, &thr, &s);
   if (tid == 0) A.rf[rowg] = RowFilter{mref, thr, s, 0.f};
+  draw_uniforms();
 }
 
 // The rule on filtered rows, one wave per request: p_i(x_i) = w(x_i) / S'_i
@@ -2460,7 +2510,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
 // write_out: as for sample_tail (false: only return the decision, for the
 // residual pass's other workgroups).
 template <int DT, bool kVec, int MODE>
-__device__ Record filtered_tail(const Args& A, int b, bool write_out = true) {
+__device__ __forceinline__ Record filtered_tail(const Args& A, int b, bool write_out = true) {
   Record rc;
   rc.pending = 0;
   rc.draw = 0;
@@ -2547,24 +2597,78 @@ __device__ Record filtered_tail(const Args& A, int b, bool write_out = true) {
   return rc;
 }
 
+// Lane l's 64-byte run of logits c0 + l * E ... (E = 32 bf16 or 16 fp32) of
+// a chunk wholly inside the row, as raw words of four 16-byte loads;
+// raw_logit reads logit k of it.
+template <int DT>
+__device__ __forceinline__ void lane_run_raw(const char* row, int64_t c0, uint32_t (&wd)[16]) {
+  constexpr int E = Chunk<DT>::kElems / 64;
+  static_assert(E * Elem<DT>::kBytes == 64, "a lane's run is 64 bytes");
+  const int64_t e0 = c0 + (int64_t)(threadIdx.x & 63) * E;
+  const uint4* p = reinterpret_cast<const uint4*>(row + e0 * Elem<DT>::kBytes);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = p[q];
+    wd[4 * q] = v.x;
+    wd[4 * q + 1] = v.y;
+    wd[4 * q + 2] = v.z;
+    wd[4 * q + 3] = v.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float raw_logit(const uint32_t (&wd)[16], int k) {
+  if (DT == kBF16) return __uint_as_float((k & 1) ? (wd[k >> 1] & 0xFFFF0000u) : (wd[k >> 1] << 16));
+  return __uint_as_float(wd[k]);
+}
+
 // Sums of the kept weights 2^(l c - M) (l >= thr, token xe left out) of
 // chunks w, w + nw, ... of one row, published to out[chunk]; lane l sums
-// the E consecutive logits of the chunk that draw_from_partials gives it.
-template <int DT, bool kVec>
-__device__ void kept_chunk_sums(const char* row, int n_chunk, int V, float c, float M, float thr, int xe,
-                                float* out, int w, int nw) {
-  constexpr int E = Chunk<DT>::kElems / 64;
+// the E consecutive logits of the chunk that the draw gives it. Each wave
+// has the loads of G chunks in flight at once.
+template <int DT, bool kVec, int G = 4>
+__device__ __forceinline__ void kept_chunk_sums(const char* row, int n_chunk, int V, float c, float M, float thr, int xe,
+                                                float* out, int w, int nw) {
+  constexpr int kCE = Chunk<DT>::kElems, E = kCE / 64;
   const int lane = threadIdx.x & 63;
-  for (int ch = w; ch < n_chunk; ch += nw) {
-    const int64_t c0 = (int64_t)ch * Chunk<DT>::kElems;
+  auto put = [&](int ch, float sm) {
+    sm = wave_sum_all(sm);
+    if (lane == 0) publish(out + ch, sm);
+  };
+  // chunks wholly inside an aligned row: G at a time, raw 16-byte loads
+  const int n_full = kVec ? V / kCE : 0;
+  for (int ch0 = w; ch0 < n_full; ch0 += G * nw) {
+    uint32_t wd[G][16];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int ch = ch0 + g * nw;
+      if (ch < n_full) lane_run_raw<DT>(row, (int64_t)ch * kCE, wd[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int ch = ch0 + g * nw;
+      if (ch >= n_full) break;
+      const int64_t e0 = (int64_t)ch * kCE + (int64_t)lane * E;
+      float sm = 0.f;
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const float x = raw_logit<DT>(wd[g], k);
+        sm += (x >= thr && e0 + k != xe) ? fast_exp2(fmaf(x, c, -M)) : 0.f;
+      }
+      put(ch, sm);
+    }
+  }
+  // the rest (the row's partial last chunk; every chunk of an unaligned
+  // row), one at a time; chunk ch stays with wave ch mod nw
+  for (int ch = n_full + (((w - n_full) % nw) + nw) % nw; ch < n_chunk; ch += nw) {
+    const int64_t c0 = (int64_t)ch * kCE;
     float x[E];
-    load_lane_run<DT, kVec, E>(row, c0, V, x);
+    load_lane_run_all<DT, kVec, E>(row, c0, V, x);
     const int64_t e0 = c0 + (int64_t)lane * E;
     float sm = 0.f;
 #pragma unroll
     for (int k = 0; k < E; ++k) sm += (x[k] >= thr && e0 + k != xe) ? fast_exp2(fmaf(x[k], c, -M)) : 0.f;
-    sm = wave_sum_all(sm);
-    if (lane == 0) publish(out + ch, sm);
+    put(ch, sm);
   }
 }
 
@@ -2574,12 +2678,13 @@ __device__ void kept_chunk_sums(const char* row, int n_chunk, int V, float c, fl
 // the row's workspace slice, then wave 0 finds the chunk and the token.
 // Only the one row a request draws from is read.
 template <int DT, bool kVec>
-__device__ void filtered_draw(const Args& A, int b, const Record& rc, int nw) {
+__device__ __forceinline__ void filtered_draw(const Args& A, int b, const Record& rc, int nw) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const Req rq = request(A, b);
+  const char* row = row_ptr(A, rq, rc.a);
   float* fp = A.fpart + ((int64_t)b * A.rows + rc.a) * A.n_chunk;
-  kept_chunk_sums<DT, kVec>(row_ptr(A, rq, rc.a), A.n_chunk, A.V, rc.c, rc.Mp, rc.tp, rc.xe, fp, wave, nw);
+  kept_chunk_sums<DT, kVec>(row, A.n_chunk, A.V, rc.c, rc.Mp, rc.tp, rc.xe, fp, wave, nw);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);                   // this wave's sums are in memory
   if (nw > 1) __syncthreads();
@@ -2590,9 +2695,11 @@ __device__ void filtered_draw(const Args& A, int b, const Record& rc, int nw) {
   if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + rc.a] = y;
 }
 
-// One workgroup per request: wave 0 runs the filtered rule, then the whole
-// workgroup draws the request's token.
+// One workgroup per request (one-hot drafts): wave 0 runs the filtered
+// rule, then every wave sums the kept weights of the row the token is
+// drawn from, per chunk, and wave 0 draws it (filtered_draw).
 constexpr int kDrawThreads = 1024;
+constexpr int kDrawWaves = kDrawThreads / 64;
 
 template <int MODE, int DT, bool kVec>
 __global__ __launch_bounds__(kDrawThreads) void sv_ftail_kernel(Args A) {
@@ -2604,7 +2711,7 @@ __global__ __launch_bounds__(kDrawThreads) void sv_ftail_kernel(Args A) {
   }
   __syncthreads();
   const Record rc = s_rc;
-  if (rc.draw) filtered_draw<DT, kVec>(A, b, rc, kDrawThreads / 64);
+  if (rc.draw) filtered_draw<DT, kVec>(A, b, rc, kDrawWaves);
 }
 
 // ------------------------------------------------------ residual pass ---
