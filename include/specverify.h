@@ -199,14 +199,16 @@ int spec_verify_greedy(const sv_logits* target, const int32_t* draft_tokens,
  * then renormalise, and run the rule of spec_verify_sample on the filtered
  * rows. One-hot drafts stay one-hot. top_k and top_p are device arrays [B]
  * (int32, fp32); either may be NULL (that filter off for every request).
- * The cut is exact among logits whose weight is within 2^-64 of the row's
- * largest; a cut below that keeps the whole row. out_p_draft / out_q_draft
- * hold the filtered p_i(x_i) / q_i(x_i). When both are NULL, drafts are
- * one-hot and top-k is off for a request, rows past its first certain
- * rejection (u * top_p >= p_j(x_j), which rejects whatever the cut) are not
- * cut: the tokens and accept lengths are the same, the call is faster.
- * Other arguments, limits and errors as spec_verify_sample; the workspace
- * is sized as for it.
+ * Precision of the cut: bf16 rows count every distinct value, so the cut is
+ * exact at any depth (masses are counts times fp64 weights); fp32 rows find
+ * it exactly among logits whose weight is within 2^-64 of the row's largest,
+ * and a cut below that keeps the whole row. out_p_draft / out_q_draft hold
+ * the filtered p_i(x_i) / q_i(x_i). fp32 rows only: when both are NULL,
+ * drafts are one-hot and top-k is off for a request, rows past its first
+ * certain rejection (u * top_p >= p_j(x_j), which rejects whatever the cut)
+ * are not cut: the tokens and accept lengths are the same, the call is
+ * faster. Other arguments, limits and errors as spec_verify_sample; the
+ * workspace is sized as for it.
  */
 int spec_verify_sample_filtered(const sv_logits* target, const sv_logits* draft,
                                 const int32_t* draft_tokens, const float* temperature,
