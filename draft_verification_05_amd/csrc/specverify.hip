@@ -1949,9 +1949,12 @@ __device__ __forceinline__ void hist_pass(const char* row, int n_chunk, int V, S
     const uint32_t i0 = c0 + ((w >> 15) & 1u) * (uint32_t)kHNeg, i1 = c1 + (w >> 31) * (uint32_t)kHNeg;
     atomicAdd(&L.hcnt[i0 - (kHMagLo - kHOff)], 1u);
     atomicAdd(&L.hcnt[i1 - (kHMagLo - kHOff)], 0x10000u);
-    if (c0 != m0 || c1 != m1) {
-      if (c0 != m0) t.add(w & 0xFFFFu);
-      if (c1 != m1) t.add(w >> 16);
+    // outside the table: the offset decides, not the clamp (the magnitudes
+    // next to the table clamp to themselves)
+    const bool o0 = m0 - kHMagLo >= (uint32_t)kHBins, o1 = m1 - kHMagLo >= (uint32_t)kHBins;
+    if (o0 || o1) {
+      if (o0) t.add(w & 0xFFFFu);
+      if (o1) t.add(w >> 16);
     }
   });
   const float s1 = wave_sum_all(t.s1), s2 = wave_sum_all(t.s2), s3 = wave_sum_all(t.s3);

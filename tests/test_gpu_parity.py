@@ -716,8 +716,9 @@ def test_filtered_bf16_rows_outside_the_table():
     """bf16 rows whose values leave the one-pass table or strain it: an all-equal
     row, few distinct values (wide ties), zeros and magnitudes below 2^-16
     mixed in (and a row of zeros only, whose cut falls among them), half the
-    vocabulary at -inf, and a logit beyond 2^16; each under a spread of top-k
-    and top-p."""
+    vocabulary at -inf, a logit beyond 2^16, and the magnitudes just outside
+    the table (the largest below 2^-16, and 2^16); each under a spread of
+    top-k and top-p."""
     B, K, V = 12, 3, 3 * 8192 + 5
     wl = make("c3_onehot", data_seed=431, B=B, K=K, V=V)
     vals = oracle.logits_f64(wl["target"].reshape(-1), "bf16").reshape(wl["target"].shape)
@@ -732,6 +733,14 @@ def test_filtered_bf16_rows_outside_the_table():
     vals[6] = np.where(rng.random(vals[6].shape) < 0.5, 0.0, vals[6])
     vals[7, :, :100] = -np.inf
     vals[7, :, 100:] = np.round(vals[7, :, 100:] * 4) / 4
+    # the magnitudes just outside the table, which a clamp maps to themselves:
+    # the bf16 value below 2^-16 (0x377F) and 2^16 itself (0x4780), both signs
+    below = float(np.array([0x377F << 16], np.uint32).view(np.float32)[0])
+    vals[8, :, ::3] = below
+    vals[8, :, 1::3] = -below
+    vals[9, :, 5] = 65536.0
+    vals[10, :, 7] = -65536.0
+    vals[10, :, 8] = below
     wl = dict(wl, target=f32_to_bf16_bits(vals.astype(np.float32)))
     top_k = np.array([1, 10, 50, 7, 3, 0, 20000, 2, 0, 5, 100, V], np.int32)
     top_p = np.array([0.9, 0.5, 0.95, 0.3, 0.8, 0.95, 1.0, 0.99, 0.95, 0.0, 0.7, 0.6], np.float32)
