@@ -318,13 +318,14 @@ def launches_per_call(wl, workload, lazy, filt, explicit) -> int:
     """Kernel launches one call makes (the library's launch plan for these
     shapes: one-launch calls for one-hot, greedy and tree batches up to 1024
     requests whose rule fits in registers; draft logits add a residual pass;
-    early exit takes two rounds; filtered bf16 rows take the one-pass select
-    kernel and then the rule with its draw (or the residual pass), filtered
-    fp32 rows the row pass, the select pass and the rule)."""
+    early exit takes two rounds; filtered bf16 rows, and fp32 rows of at most
+    32768 logits, take one select kernel and then the rule with its draw (or
+    the residual pass), longer filtered fp32 rows the row pass, the select
+    pass and the rule)."""
     if lazy:
         return 2 + (1 if explicit else 0)
     if filt:
-        return 2 if wl["dtype"] == "bf16" else 3
+        return 2 if wl["dtype"] == "bf16" or wl["V"] <= 32768 else 3
     if wl["mode"] == "sample" and explicit:
         return 2
     return 1 if wl["B"] <= 1024 else 2
@@ -334,8 +335,9 @@ def roofline_kernel(wl, lazy, filt, explicit, n) -> str:
     if n == 1:
         return ("sv_rows_kernel, one launch per call (row pass + per-request rule); "
                 "algorithmic bytes of the call / its kernel time")
-    if filt and wl["dtype"] == "bf16":
-        what = "one-pass select + " + ("residual pass (rule and draw)" if explicit else "rule and draw")
+    if filt and (wl["dtype"] == "bf16" or wl["V"] <= 32768):
+        sel = "one-pass select" if wl["dtype"] == "bf16" else "LDS-resident select"
+        what = sel + " + " + ("residual pass (rule and draw)" if explicit else "rule and draw")
         return f"whole call, {n} launches ({what}); algorithmic bytes / call time"
     what = ("early-exit rounds over position windows [0], [1, K]" if lazy else
             "row pass + select pass + rule" if filt else "row pass + rule")

@@ -1632,9 +1632,10 @@ __global__ __launch_bounds__(64) void sv_tail_kernel(Args A) {
 //   D = l * log2(e) / T - Mref   (fp64; Mref = the row's largest l * log2(e) / T)
 // in 1024 buckets of width 1/16 over [0, 64), refined 256-fold per level
 // (at most three levels) until the bucket holding the cut has at most
-// kSelCap logits. Those are sorted by value and scanned exactly. A cut more than
-// 64 below the largest log2 weight keeps the whole row (the weights it
-// would drop are below 2^-64 of the largest).
+// kSelCap logits. Those are cut exactly: the mass of each one's upper set
+// among them (rank_cut), or a sort and a scan. A cut more than 64 below
+// the largest log2 weight keeps the whole row (the weights it would drop
+// are below 2^-64 of the largest).
 
 constexpr int kSelBuckets0 = 1024;                // first level: width 1/16 over [0, 64)
 constexpr int kSelBuckets = 256;                  // refinement levels
@@ -1672,6 +1673,7 @@ struct alignas(16) SelLds {
   unsigned tiny_n, ninf_n, tiny_max;               // tiny count, -inf count, largest tiny order key
   int big;                                         // a value outside the table that is not -inf
   int sel_max, sel_k, sel_p;                       // picked positions (INT_MAX: none)
+  uint32_t kcut, kmin;                             // rank_cut's picks
 };
 
 // Total order of logit values as unsigned keys (-0 sorts with +0).
@@ -1715,20 +1717,52 @@ __device__ __forceinline__ int sel_bucket(double D, int level, int64_t parent) {
   return (int)(t - lo);
 }
 
-// Inclusive scan of one value per thread; buf keeps the result (the total
-// in its last entry) until the next call.
-__device__ double block_scan(double v, double* buf) {
-  const int tid = threadIdx.x;
-  __syncthreads();                                 // earlier readers of buf are done
-  buf[tid] = v;
+// Inclusive scan of one double per thread over a workgroup of NT threads
+// (lanes in order within a wave, then waves in order). *excl gets the
+// previous thread's result bit for bit (0 for thread 0) and *total the
+// workgroup's sum, so that exactly the thread whose range holds a crossing
+// of a threshold sees excl < t <= incl (up to the order of equal partial
+// sums). wtot: NT / 64 doubles; kFree: no thread reads them at the call
+// (else a barrier comes first).
+template <int kCtrl, int kRows = 0xF>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, kRows, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl, kRows, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive scan over the wave's lanes: shifts within rows of 16 lanes,
+// then the broadcasts of row ends (lanes without a source add 0).
+__device__ __forceinline__ double wave_scan_incl_d(double v) {
+  v += dpp_d<0x111>(v);
+  v += dpp_d<0x112>(v);
+  v += dpp_d<0x114>(v);
+  v += dpp_d<0x118>(v);
+  v += dpp_d<0x142, 0xA>(v);
+  v += dpp_d<0x143, 0xC>(v);
+  return v;
+}
+
+template <int NT, bool kFree = false>
+__device__ __forceinline__ double wg_scan(double v, double* wtot, double* excl, double* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_scan_incl_d(v);
+  if (!kFree) __syncthreads();                     // earlier readers of wtot are done
+  if (lane == 63) wtot[wave] = v;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const double t = tid >= off ? buf[tid - off] : 0.0;
-    __syncthreads();
-    buf[tid] += t;
-    __syncthreads();
+  double pre = 0.0, tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w == wave) pre = tot;
+    tot += wtot[w];
   }
-  return buf[tid];
+  const double incl = pre + v;
+  const double prev = __shfl_up(incl, 1);
+  *excl = lane == 0 ? pre : prev;
+  *total = tot;
+  return incl;
 }
 
 // Every logit of a row once (f(l, index)), chunk by chunk, the next chunk's
@@ -1758,19 +1792,59 @@ __device__ void for_each_logit(const char* row, int n_chunk, int V, F f) {
   }
 }
 
+// The cut search's two views of a row. StreamRow reads it from memory
+// with a workgroup of kThreads (for_each_logit); LdsRow is a row that a
+// workgroup of NT threads has copied to LDS as 16-byte vectors, -inf past
+// the row's end. each(f) calls f(l, index) once for every logit of the row
+// (and the padding of its last vector).
+template <int DT, bool kVec>
+struct StreamRow {
+  static constexpr int kNT = kThreads;
+  const char* row;
+  int n_chunk, V;
+  template <class F>
+  __device__ __forceinline__ void each(F f) const { for_each_logit<DT, kVec>(row, n_chunk, V, f); }
+};
+
+template <int NT, int NV>
+struct LdsRow {
+  static constexpr int kNT = NT;
+  const float4* vec;
+  int n_vec;                                       // at most NV * NT
+  template <class F>
+  __device__ __forceinline__ void each(F f) const {
+    float4 q[NV];                                  // every read of the pass in flight at once
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = j * NT + threadIdx.x;
+      q[j] = v < n_vec ? vec[v] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t e = (int64_t)(j * NT + threadIdx.x) * 4;
+      f(q[j].x, e);
+      f(q[j].y, e + 1);
+      f(q[j].z, e + 2);
+      f(q[j].w, e + 3);
+    }
+  }
+};
+
 // Descending bitonic sort of the first n collected entries (padded to a
-// power of two with key 0, below every logit's key).
-__device__ void sort_collected(SelLds& L, int n) {
+// power of two with key 0, below every logit's key), by the NT threads of
+// the workgroup.
+template <int NT, class LT>
+__device__ void sort_collected(LT& L, int n) {
   int np = 2;
   while (np < n) np <<= 1;
-  for (int i = n + threadIdx.x; i < np; i += kThreads) {
+  for (int i = n + threadIdx.x; i < np; i += NT) {
     L.key[i] = 0u;
     L.w[i] = 0.0;
   }
   __syncthreads();
   for (int size = 2; size <= np; size <<= 1)
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (np >> 1); i += kThreads) {
+      for (int i = threadIdx.x; i < (np >> 1); i += NT) {
         const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
         const bool desc = (lo & size) == 0;
         const uint32_t a = L.key[lo], c = L.key[hi];
@@ -1787,25 +1861,24 @@ __device__ void sort_collected(SelLds& L, int n) {
 }
 
 // Sorts the n collected logits (key, weight) by value, largest first, and
-// returns the key at which above + their running sum first reaches target.
-// *where (optional): -1 when above alone reaches it (the cut lies above
-// these logits), +1 when even all of them fall short (below), else 0; with
-// where null, falling short keeps them all (rounding at the row's end).
-__device__ uint32_t scan_collected(SelLds& L, int n, double above, double target, int* where) {
+// returns the key at which above + their running sum first reaches target
+// (falling short keeps them all: rounding at the row's end).
+template <int NT, class LT>
+__device__ uint32_t scan_collected(LT& L, int n, double above, double target) {
   const int tid = threadIdx.x;
-  sort_collected(L, n);
-  constexpr int kPer = kSelCap / kThreads;
+  sort_collected<NT>(L, n);
+  constexpr int kPer = kSelCap / NT;
   double loc = 0.0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = tid * kPer + j;
     loc += e < n ? L.w[e] : 0.0;
   }
-  const double incl = block_scan(loc, L.scan);
-  const double all = L.scan[kThreads - 1];
+  double excl, all;
+  wg_scan<NT>(loc, L.wtot, &excl, &all);
   if (tid == 0) L.sel = INT_MAX;
   __syncthreads();
-  double run = above + incl - loc;
+  double run = above + excl;
   for (int j = 0; j < kPer; ++j) {
     const int e = tid * kPer + j;
     if (e >= n) break;
@@ -1818,9 +1891,52 @@ __device__ uint32_t scan_collected(SelLds& L, int n, double above, double target
   __syncthreads();
   const int sel = L.sel;
   uint32_t k = 0u;
-  if (where) *where = above >= target ? -1 : (above + all < target ? 1 : 0);
   if (sel != INT_MAX) k = L.key[sel];
   else if (n > 0) k = L.key[n - 1];               // short of the target: the whole set
+  __syncthreads();
+  return k;
+}
+
+// The same cut as scan_collected for n <= NT collected logits, without the
+// sort: the mass of the upper set {l >= l_i} of each logit i, and the cut
+// is the largest key whose upper set brings above to target (falling
+// short: as scan_collected). With n <= NT / 4, four neighbouring threads
+// share logit i, each summing a quarter of the entries (combined in the
+// quad); else one thread per logit. L.kcut must hold 0 and L.kmin the
+// smallest collected key, both set before the barrier that ends the
+// collection.
+template <int NT, class LT>
+__device__ uint32_t rank_cut(LT& L, int n, double above, double target) {
+  const int tid = threadIdx.x;
+  const int g = 4 * n <= NT ? 4 : 1;              // threads per logit (uniform)
+  const int i = tid / g, part = tid % g;
+  const int n4 = (n + 3) & ~3;                     // whole vectors of four entries
+  const int per = ((n4 / 4 + g - 1) / g) * 4;      // entries per part, a multiple of 4
+  const int j0 = part * per, j1 = min(j0 + per, n4);
+  const uint32_t ki = i < n ? L.key[i] : 0xFFFFFFFFu;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int j = j0; j < j1; j += 4) {               // lanes of a quad read the same entries
+    const uint4 k4 = *reinterpret_cast<const uint4*>(&L.key[j]);
+    const double2 w01 = *reinterpret_cast<const double2*>(&L.w[j]);
+    const double2 w23 = *reinterpret_cast<const double2*>(&L.w[j + 2]);
+    s[0] += (k4.x >= ki && j < n) ? w01.x : 0.0;
+    s[1] += (k4.y >= ki && j + 1 < n) ? w01.y : 0.0;
+    s[2] += (k4.z >= ki && j + 2 < n) ? w23.x : 0.0;
+    s[3] += (k4.w >= ki && j + 3 < n) ? w23.y : 0.0;
+  }
+  double t = (s[0] + s[1]) + (s[2] + s[3]);
+  if (g == 4) {                                    // the quad's parts, in order
+    const double t1 = __shfl_xor(t, 1), t2 = __shfl_xor(t, 2), t3 = __shfl_xor(t, 3);
+    const int q = part;
+    const double a0 = q == 0 ? t : q == 1 ? t1 : q == 2 ? t2 : t3;     // part 0
+    const double a1 = q == 1 ? t : q == 0 ? t1 : q == 3 ? t2 : t3;     // part 1
+    const double a2 = q == 2 ? t : q == 3 ? t1 : q == 0 ? t2 : t3;     // part 2
+    const double a3 = q == 3 ? t : q == 2 ? t1 : q == 1 ? t2 : t3;     // part 3
+    t = (a0 + a1) + (a2 + a3);
+  }
+  if (i < n && part == 0 && above + t >= target) atomicMax(&L.kcut, ki);
+  __syncthreads();
+  const uint32_t k = L.kcut ? L.kcut : (n > 0 ? L.kmin : 0u);
   __syncthreads();
   return k;
 }
@@ -2053,59 +2169,64 @@ __device__ __forceinline__ int hist_pick(SelLds& L, int* slot, int mine, double 
   return o;
 }
 
-// Inclusive scan of one double per thread (lanes in order within a wave,
-// waves in order). *excl gets the previous thread's result bit for bit and
-// *total the last thread's, so that exactly the thread whose range holds a
-// crossing of a threshold sees excl < t <= incl (up to the order of equal
-// partial sums). wtot: kWaves doubles that no thread reads at the call
-// (each scan of a row takes its own).
-__device__ __forceinline__ double block_scan_x(double v, double* wtot, double* excl, double* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int off = 1; off < 64; off <<= 1) {
-    const double t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  if (lane == 63) wtot[wave] = v;
-  __syncthreads();
-  double pre = 0.0, tot = 0.0;
-  for (int w = 0; w < kWaves; ++w) {
-    if (w == wave) pre = tot;
-    tot += wtot[w];
-  }
-  const double incl = pre + v;
-  const double prev = __shfl_up(incl, 1);
-  *excl = lane == 0 ? pre : prev;
-  *total = tot;
-  return incl;
+// 2^(d - 1/32) for d in [-1/16, 0] or so (a weight relative to the middle
+// of its level-0 bucket): e^x, x = (d + 1/32) ln 2, |x| <= 0.0217, by its
+// Taylor series to x^7 (the remainder is below 2e-18 of the value).
+__device__ __forceinline__ double exp2_small(double d) {
+  const double x = (d + 0.03125) * 0.69314718055994530942;
+  double e = 1.0 / 5040.0;
+  e = fma(e, x, 1.0 / 720.0);
+  e = fma(e, x, 1.0 / 120.0);
+  e = fma(e, x, 1.0 / 24.0);
+  e = fma(e, x, 1.0 / 6.0);
+  e = fma(e, x, 0.5);
+  e = fma(e, x, 1.0);
+  return fma(e, x, 1.0);
 }
+
+// The weight of level-0 bucket k's middle, 2^(-k/16 - 1/32), by which the
+// scan scales the bucket's exp2_small sum.
+__device__ __forceinline__ double bucket_scale(int k) { return exp2(-0.0625 * (double)k - 0.03125); }
 
 // The cut for one criterion among the logits with key >= kfloor: the
 // largest logit value t whose upper set holds at least `want` logits
 // (kMass false) or `want` of their mass (kMass true). Returns the key of t,
-// or 0 to keep them all. Logits below kfloor count as -inf.
-template <int DT, bool kVec, bool kMass>
-__device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, double cd, float mref,
-                               double want, uint32_t kfloor) {
+// or 0 to keep them all. Logits below kfloor count as -inf. Every thread of
+// the src.kNT-thread workgroup calls.
+// Level 0 is one pass of straight-line work per logit: its bucket k and one
+// LDS atomic, the count, or the weight relative to the bucket's middle,
+// 2^(D + k / 16 + 1/32) (a short series, no table), which the scan scales
+// back (bucket_scale); the last bucket (D < -64, -inf) adds no mass. The bucket
+// holding the cut is collected (key and fp64 weight) and cut exactly
+// (rank_cut, or the sort for more than NT logits); with more than kSelCap
+// logits in it, the next level refines it.
+template <bool kMass, class Src, class LT>
+__device__ __forceinline__ uint32_t select_cut(const Src& src, LT& L, double cd, float mref, double want,
+                                               uint32_t kfloor) {
+  constexpr int NT = Src::kNT, last = kSelBuckets0 - 1;
   const int tid = threadIdx.x;
   int64_t parent = 0;
   double above = 0.0, target = want;
-  int level = 0, sel = 0;
-  for (; level < kSelLevels; ++level) {
+  for (int level = 0;; ++level) {
     const int nb = level == 0 ? kSelBuckets0 : kSelBuckets;
-    for (int i = tid; i < nb; i += kThreads) {
-      L.cnt[i] = 0u;
-      L.mass[i] = 0.0;
+    for (int i = tid; i < nb; i += NT) {
+      if (!kMass || level > 0) L.cnt[i] = 0u;
+      if (kMass) L.mass[i] = 0.0;
     }
     __syncthreads();
     if (level == 0) {                              // every logit lands in a bucket
-      for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+      src.each([&](float l, int64_t) {
         const double D = order_key(l) >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
         const int bk = sel_bucket(D, 0, 0);
-        atomicAdd(&L.cnt[bk], 1u);
-        if (kMass) atomicAdd(&L.mass[bk], exp2_weight(D, L.tab));
+        if (kMass) {
+          const double wr = exp2_small(bk < last ? fma((double)bk, 0.0625, D) : 0.0);
+          atomicAdd(&L.mass[bk], bk < last ? wr : 0.0);
+        } else {
+          atomicAdd(&L.cnt[bk], 1u);
+        }
       });
     } else {                                       // only those of the parent bucket
-      for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+      src.each([&](float l, int64_t) {
         const double D = order_key(l) >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
         const int bk = sel_bucket(D, level, parent);
         if (bk >= 0) {
@@ -2115,98 +2236,232 @@ __device__ uint32_t select_cut(const char* row, int n_chunk, int V, SelLds& L, d
       });
     }
     __syncthreads();
-    // inclusive scan over the buckets, nb / kThreads per thread
-    const int per = nb / kThreads;
+    // a scan over the buckets, thread t taking buckets t per ... t per + per - 1
+    const int per = nb >= NT ? nb / NT : 1;
+    auto value = [&](int e) {
+      if (!kMass) return (double)L.cnt[e];
+      return level == 0 ? L.mass[e] * bucket_scale(e) : L.mass[e];
+    };
     double loc = 0.0;
     for (int j = 0; j < per; ++j) {
       const int e = tid * per + j;
-      loc += kMass ? L.mass[e] : (double)L.cnt[e];
+      if (e < nb) loc += value(e);
     }
-    const double incl = block_scan(loc, L.scan);
-    if (level == 0 && kMass) target = want * L.scan[kThreads - 1];
     if (tid == 0) L.sel = INT_MAX;
-    __syncthreads();
-    double run = above + incl - loc;
+    double excl, all;
+    wg_scan<NT>(loc, L.wtot, &excl, &all);
+    if (level == 0 && kMass) target = want * all;
+    // the thread whose buckets hold the crossing leaves the sum before it
+    double run = above + excl;
     for (int j = 0; j < per; ++j) {
       const int e = tid * per + j;
-      run += kMass ? L.mass[e] : (double)L.cnt[e];
-      if (run >= target) {
+      if (e >= nb) break;
+      const double v = value(e);
+      if (run + v >= target) {
         atomicMin(&L.sel, e);
+        L.scan[tid] = run;
         break;
       }
+      run += v;
     }
     __syncthreads();
-    sel = L.sel;
-    if (sel == INT_MAX || (level == 0 && sel == kSelBuckets0 - 1)) return 0u;   // keep all
-    // mass (or count) of the buckets before sel
-    double before = 0.0;
-    for (int j = 0; j < per; ++j) {
-      const int e = tid * per + j;
-      if (e < sel) before += kMass ? L.mass[e] : (double)L.cnt[e];
+    const int sel = L.sel;
+    if (sel == INT_MAX || (level == 0 && sel == last)) return 0u;   // keep all
+    above = L.scan[sel / per];                     // the mass (or count) above bucket sel
+    if (tid == 0) {
+      L.n = 0;
+      L.kcut = 0u;
+      L.kmin = 0xFFFFFFFFu;
     }
-    block_scan(before, L.scan);
-    above += L.scan[kThreads - 1];
-    const unsigned n_sel = L.cnt[sel];
     __syncthreads();
-    if (n_sel <= (unsigned)kSelCap) break;
-    if (level + 1 < kSelLevels) parent = (level == 0) ? sel : parent * kSelBuckets + sel;
-  }
-  if (level == kSelLevels) {
-    // more than kSelCap logits within 2^-20 / 16 of one log2 weight: keep
-    // that whole bucket (its smallest key)
-    if (tid == 0) L.kfloor = 0xFFFFFFFFu;
-    __syncthreads();
-    for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+    // collect the bucket (its smallest key too)
+    src.each([&](float l, int64_t) {
       const uint32_t k = order_key(l);
       const double D = k >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
-      if (sel_bucket(D, kSelLevels - 1, parent) == sel) atomicMin(&L.kfloor, k);
+      if (sel_bucket(D, level, parent) != sel) return;
+      atomicMin(&L.kmin, k);
+      const int slot = atomicAdd(&L.n, 1);
+      if (slot < kSelCap) {
+        L.key[slot] = k;
+        L.w[slot] = kMass ? exp2_weight(D, L.tab) : 1.0;
+      }
     });
     __syncthreads();
-    const uint32_t k = L.kfloor;
+    const int n = L.n;
+    if (n <= NT) return rank_cut<NT>(L, n, above, target);
+    if (n <= kSelCap) return scan_collected<NT>(L, n, above, target);
+    if (level + 1 == kSelLevels) {
+      // more than kSelCap logits within 2^-20 / 16 of one log2 weight: keep
+      // that whole bucket (its smallest key)
+      const uint32_t k = L.kmin;
+      __syncthreads();
+      return k;
+    }
+    parent = level == 0 ? sel : parent * kSelBuckets + sel;
     __syncthreads();
-    return k;
   }
-  // collect the bucket, sort it, scan it
-  if (tid == 0) L.n = 0;
+}
+
+constexpr int kRThreads = 1024;
+constexpr int kRWaves = kRThreads / 64;
+constexpr int kRCap = 32768;                       // logits: 128 KiB of LDS
+constexpr int kRVecs = kRCap / 4 / kRThreads;      // 16-byte loads per thread
+static_assert(kSelCap % kRThreads == 0 && kSelBuckets0 % kRThreads == 0, "whole shares per thread");
+
+struct alignas(16) RSelLds {
+  float4 row[kRCap / 4];
+  union {                                          // the histogram, then the collected logits
+    struct {
+      unsigned cnt[kSelBuckets0];
+      double mass[kSelBuckets0];
+      double scan[kRThreads];                      // per thread: the sum before its pick
+    };
+    struct {
+      uint32_t key[kSelCap];
+      double w[kSelCap];
+    };
+  };
+  double tab[64];                                  // 2^(j / 64)
+  double wtot[kRWaves];
+  float wsum[kRWaves];
+  int n, sel;
+  uint32_t kfloor, kcut, kmin;
+};
+
+// select_cut for a row held in LDS by a workgroup of kRThreads (one bucket
+// of level 0 per thread), with the passes written out so that each is
+// straight-line work per logit, without waits: the level-0 histogram (the
+// bucket from the fp32 log2 weight, the weight relative to the bucket from
+// the fp64 one); the scan, where the one thread whose range holds the
+// crossing names the bucket; then the bucket's logits, which each thread
+// marks in a bit mask, places by a scan of the counts, and writes out (key,
+// fp64 weight) in a loop over its bits; and rank_cut. More than kSelCap
+// logits in the bucket: select_cut, from the start.
+template <bool kMass, int NT, int NV>
+__device__ __forceinline__ uint32_t lds_select_cut(const LdsRow<NT, NV>& src, RSelLds& L, float c, double cd,
+                                                   float mref, double want, uint32_t kfloor) {
+  static_assert(NT == kSelBuckets0 && 4 * NV <= 32, "a bucket per thread; a bit per logit");
+  constexpr int last = kSelBuckets0 - 1;
+  const int tid = threadIdx.x;
+  if (kMass) L.mass[tid] = 0.0;
+  else       L.cnt[tid] = 0u;
+  if (tid == 0) {
+    L.sel = INT_MAX;
+    L.kcut = 0u;
+    L.kmin = 0xFFFFFFFFu;
+  }
   __syncthreads();
-  for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t) {
+  float4 q[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * NT + tid;
+    q[j] = v < src.n_vec ? src.vec[v] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+  }
+  auto logit = [&](int i) {                        // static i: logit i of this thread
+    const float4& v = q[i >> 2];
+    return (i & 3) == 0 ? v.x : (i & 3) == 1 ? v.y : (i & 3) == 2 ? v.z : v.w;
+  };
+  // the bucket from the fp32 log2 weight (any monotone map will do, the
+  // same in every pass; this one lies within 1e-4 of the fp64 one); the
+  // weight from the fp64 one
+  auto bucket = [&](float l) {
+    const float t = -16.f * fmaf(l, c, -mref);
+    const int bk = t < (float)last ? (t > 0.f ? (int)t : 0) : last;   // also -inf and NaN
+    return order_key(l) >= kfloor ? bk : last;
+  };
+#pragma unroll
+  for (int i = 0; i < 4 * NV; ++i) {
+    const float l = logit(i);
+    const int bk = bucket(l);
+    if (kMass) {
+      const double D = (double)l * cd - (double)mref;
+      const double wr = exp2_small(bk < last ? fma((double)bk, 0.0625, D) : 0.0);
+      atomicAdd(&L.mass[bk], bk < last ? wr : 0.0);
+    } else {
+      atomicAdd(&L.cnt[bk], 1u);
+    }
+  }
+  __syncthreads();
+  const double v = kMass ? L.mass[tid] * bucket_scale(tid) : (double)L.cnt[tid];
+  double excl, all;
+  const double incl = wg_scan<NT>(v, L.wtot, &excl, &all);
+  const double target = kMass ? want * all : want;
+  if ((tid == 0 || excl < target) && target <= incl) {   // at most one thread
+    L.sel = tid;
+    L.scan[0] = excl;
+  }
+  __syncthreads();
+  const int sel = L.sel;
+  if (sel == INT_MAX || sel == last) return 0u;    // keep all
+  const double above = L.scan[0];
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < 4 * NV; ++i) m |= (bucket(logit(i)) == sel ? 1u : 0u) << i;
+  double ox, n_all;
+  const int off = (int)(wg_scan<NT>((double)__builtin_popcount(m), L.wtot, &ox, &n_all) - __builtin_popcount(m));
+  const int n = (int)n_all;
+  if (n > kSelCap) return select_cut<kMass>(src, L, cd, mref, want, kfloor);
+  const float* row = reinterpret_cast<const float*>(src.vec);
+  uint32_t kmin = 0xFFFFFFFFu;
+  for (int slot = off; m; ++slot) {
+    const int i = __builtin_ctz(m);
+    m &= m - 1u;
+    const float l = row[(int64_t)((i >> 2) * NT + tid) * 4 + (i & 3)];
     const uint32_t k = order_key(l);
     const double D = k >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
-    if (sel_bucket(D, level, parent) != sel) return;
-    const int slot = atomicAdd(&L.n, 1);
-    if (slot < kSelCap) {
-      L.key[slot] = k;
-      L.w[slot] = kMass ? exp2_weight(D, L.tab) : 1.0;
-    }
-  });
+    L.key[slot] = k;
+    L.w[slot] = kMass ? exp2_weight(D, L.tab) : 1.0;
+    kmin = min(kmin, k);
+  }
+  if (kmin != 0xFFFFFFFFu) atomicMin(&L.kmin, kmin);
   __syncthreads();
-  return scan_collected(L, min(L.n, kSelCap), above, target, nullptr);
+  if (n <= NT) return rank_cut<NT>(L, n, above, target);
+  return scan_collected<NT>(L, n, above, target);
+}
+
+template <bool kMass, class Src, class LT>
+__device__ __forceinline__ uint32_t row_cut(const Src& src, LT& L, float, double cd, float mref, double want,
+                                            uint32_t kfloor) {
+  return select_cut<kMass>(src, L, cd, mref, want, kfloor);
+}
+template <bool kMass, int NT, int NV>
+__device__ __forceinline__ uint32_t row_cut(const LdsRow<NT, NV>& src, RSelLds& L, float c, double cd, float mref,
+                                            double want, uint32_t kfloor) {
+  return lds_select_cut<kMass>(src, L, c, cd, mref, want, kfloor);
 }
 
 // The general search's cut of one row (top-k, then top-p, each by
 // select_cut) and its kept mass: the fp32 sum of the kept weights
 // 2^(l c - mref), without token xe (a one-hot draft's, as the row pass
-// leaves it out; -1: none).
-template <int DT, bool kVec>
-__device__ void general_cut(const char* row, int n_chunk, int V, SelLds& L, float c, double cd, float mref,
-                            int tk, float tp, int xe, float* thr_out, float* s_out) {
+// leaves it out; -1: none). L.tab must hold 2^(j / 64), j < 64.
+template <class Src, class LT>
+__device__ __forceinline__ void general_cut(const Src& src, int V, LT& L, float c, double cd, float mref, int tk,
+                                            float tp, int xe, float* thr_out, float* s_out) {
+  constexpr int NW = Src::kNT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t cut = 0u;
-  if (tk > 0 && tk < V) cut = select_cut<DT, kVec, false>(row, n_chunk, V, L, cd, mref, (double)tk, 0u);
+  if (tk > 0 && tk < V) cut = row_cut<false>(src, L, c, cd, mref, (double)tk, 0u);
   if (tp < 1.f) {                                  // NaN compares false: off
-    const uint32_t cp = select_cut<DT, kVec, true>(row, n_chunk, V, L, cd, mref, (double)tp, cut);
+    const uint32_t cp = row_cut<true>(src, L, c, cd, mref, (double)tp, cut);
     if (cp) cut = cp;
   }
   const float thr = cut ? key_value(cut) : kNegInf;
   float sm = 0.f;
-  for_each_logit<DT, kVec>(row, n_chunk, V, [&](float l, int64_t e) {
+  src.each([&](float l, int64_t e) {
     sm += (l >= thr && e != xe) ? fast_exp2(fmaf(l, c, -mref)) : 0.f;
   });
   sm = wave_sum_all(sm);
   __syncthreads();                                 // earlier readers of L.wsum are done
   if (lane == 0) L.wsum[wave] = sm;
   __syncthreads();
-  *s_out = (L.wsum[0] + L.wsum[1]) + (L.wsum[2] + L.wsum[3]);
+  float v[NW];                                     // the wave sums, added pairwise
+#pragma unroll
+  for (int w = 0; w < NW; ++w) v[w] = L.wsum[w];
+#pragma unroll
+  for (int h = 1; h < NW; h <<= 1)
+#pragma unroll
+    for (int w = 0; w + h < NW; w += 2 * h) v[w] += v[w + h];
+  *s_out = v[0];
   *thr_out = thr;
 }
 
@@ -2295,8 +2550,80 @@ __global__ __launch_bounds__(kThreads, 4) void sv_select_kernel(Args A) {
   const int tk = A.top_k ? A.top_k[b] : 0;
   const float tp = A.top_p ? A.top_p[b] : 1.f;
   float thr, s;
-  general_cut<DT, kVec>(row, A.n_chunk, A.V, L, c, cd, mref, tk, tp, xe, &thr, &s);
+  general_cut(StreamRow<DT, kVec>{row, A.n_chunk, A.V}, A.V, L, c, cd, mref, tk, tp, xe, &thr, &s);
   if (tid == 0) A.rf[rowg] = RowFilter{mref, thr, s, 0.f};
+}
+
+// fp32 rows of at most kRCap logits, one workgroup of kRThreads per row and
+// no row pass before it: the workgroup copies its row to LDS (every load
+// in flight at once; the copy and the sort's entries fill most of the CU's
+// 160 KiB), and finds the row's largest value, its cuts and kept mass there
+// (general_cut, each of its passes over LDS), as a RowFilter; also the
+// row's draft-token logit and (row 0's workgroup) the request's uniforms,
+// which the row pass draws on unfiltered calls.
+template <int MODE, bool kVec>
+__global__ __launch_bounds__(kRThreads) void sv_rselect_kernel(Args A) {
+  __shared__ RSelLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rowg = blockIdx.x;
+  const int b = rowg / A.rows, r = rowg % A.rows;
+  const int V = A.V, n_vec = (V + 3) / 4;
+  const Req rq = request(A, b);
+  const char* row = row_ptr(A, rq, r);
+  float4 x[kRVecs];
+#pragma unroll
+  for (int j = 0; j < kRVecs; ++j) {
+    const int v = j * kRThreads + tid;
+    const int64_t e0 = (int64_t)v * 4;
+    if (kVec && e0 + 4 <= V) {
+      x[j] = *reinterpret_cast<const float4*>(row + e0 * 4);
+    } else {
+      float q[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q[k] = e0 + k < V ? load_one<kF32>(row, e0 + k) : kNegInf;
+      x[j] = make_float4(q[0], q[1], q[2], q[3]);
+    }
+  }
+  auto draw_uniforms = [&]() {
+    if (r == 0 && wave == 0 && lane < A.R) {
+      const Philox4 rnd = philox4x64_10((uint64_t)lane, (uint64_t)b, A.offset, 0ull, A.seeds[b], 0ull);
+      A.unif[(int64_t)b * A.R + lane] = make_float2(top24(rnd.w0), top24(rnd.w1));
+    }
+  };
+  // this row's draft token (target rows 0..K-1, draft rows)
+  const int i = r < A.R ? r : r - A.R;
+  int xt = i < rq.k ? A.tokens[rq.x0 + i] : -1;
+  if ((unsigned)xt >= (unsigned)V) xt = -1;
+  const int xe = MODE == kOneHot ? xt : -1;        // left out of a one-hot row's sums
+  const float T = A.temperature[b];
+  float m = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kRVecs; ++j) {
+    if (j * kRThreads + tid < n_vec) L.row[j * kRThreads + tid] = x[j];
+    m = fmaxf(m, fmaxf(fmaxf(x[j].x, x[j].y), fmaxf(x[j].z, x[j].w)));
+  }
+  m = wave_max_all(m);
+  if (lane == 0) L.wsum[wave] = m;
+  if (tid < 64) L.tab[tid] = exp2((double)tid / 64.0);
+  __syncthreads();
+  float lmax = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kRWaves; ++w) lmax = fmaxf(lmax, L.wsum[w]);
+  const float c = kLog2e / T;
+  const float mref = lmax * c;
+  float thr = kNegInf, s = 0.f, mr = kNegInf;
+  if (T > 0.f && T < __builtin_inff() && mref != kNegInf && mref == mref) {
+    const double cd = 1.4426950408889634 / (double)T;
+    const int tk = A.top_k ? A.top_k[b] : 0;
+    const float tp = A.top_p ? A.top_p[b] : 1.f;
+    general_cut(LdsRow<kRThreads, kRVecs>{L.row, n_vec}, V, L, c, cd, mref, tk, tp, xe, &thr, &s);
+    mr = mref;
+  }
+  if (tid == 0) {
+    A.rf[rowg] = RowFilter{mr, thr, s, 0.f};
+    if (xt >= 0) A.gath[rowg] = reinterpret_cast<const float*>(L.row)[xt];
+  }
+  draw_uniforms();
 }
 
 // bf16 rows, one workgroup per row and no row pass before it: the one-pass
@@ -2366,7 +2693,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
     const bool k_on = tk > 0 && tk < A.V;
     if (k_on || A.V > 2 * 65535) {
       double ce, ct;
-      const double ci = block_scan_x((double)cl, L.wtot, &ce, &ct);
+      const double ci = wg_scan<kThreads, true>((double)cl, L.wtot, &ce, &ct);
       general = ct != (double)A.V;
       if (k_on && !general) {
         const double target = (double)tk;
@@ -2431,7 +2758,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
       }
       ml += mx;
       double me, zk;
-      const double mi = block_scan_x(ml, L.wtot2, &me, &zk);
+      const double mi = wg_scan<kThreads, true>(ml, L.wtot2, &me, &zk);
       const bool p_on = tp < 1.f;                  // NaN compares false: off
       int o_p = -1;
       double at_p = 0.0;
@@ -2500,7 +2827,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
     return;
   }
   float thr, s;
-  general_cut<kBF16, kVec>(row, A.n_chunk, A.V, L, c, cd, mref, tk, tp, xe, &thr, &s);
+  general_cut(StreamRow<kBF16, kVec>{row, A.n_chunk, A.V}, A.V, L, c, cd, mref, tk, tp, xe, &thr, &s);
   if (tid == 0) A.rf[rowg] = RowFilter{mref, thr, s, 0.f};
   draw_uniforms();
 }
@@ -3120,7 +3447,8 @@ void launch_residual_dt(const Args& A, bool vec, unsigned grid, hipStream_t st, 
 }
 
 // Filtered verification: per row the cut and kept mass (bf16: the one-pass
-// histogram kernel; fp32: the row pass, then the select pass), one
+// histogram kernel; fp32 rows of at most kRCap logits: the register-resident
+// select; longer fp32 rows: the row pass, then the select pass), one
 // workgroup per row; then the filtered rule and the draw, one workgroup per
 // request. With draft logits the residual pass that follows runs the rule
 // itself.
@@ -3130,6 +3458,10 @@ void launch_filtered_dt(const Args& A, bool vec, unsigned grid, hipStream_t st) 
   if constexpr (DT == kBF16) {
     if (vec) hipLaunchKernelGGL((sv_hselect_kernel<MODE, true>), rows, wg, 0, st, A);
     else     hipLaunchKernelGGL((sv_hselect_kernel<MODE, false>), rows, wg, 0, st, A);
+  } else if (A.V <= kRCap) {
+    const dim3 rwg(kRThreads);
+    if (vec) hipLaunchKernelGGL((sv_rselect_kernel<MODE, true>), rows, rwg, 0, st, A);
+    else     hipLaunchKernelGGL((sv_rselect_kernel<MODE, false>), rows, rwg, 0, st, A);
   } else {
     if (vec) {
       SV_LAUNCH((sv_rows_kernel<MODE, DT, true, false, false, false>), grid, st, A);

@@ -761,6 +761,54 @@ def test_filtered_bf16_counter_carry():
                    np.array([0.9, 0.95, 0.5], np.float32), near_frac=1.0)
 
 
+def _onehot_f32(B, V, seed):
+    """A one-hot workload with fp32 rows (the C3 generator's values)."""
+    wl = make("c3_onehot", data_seed=seed, B=B, V=V)
+    vals = oracle.logits_f64(wl["target"].reshape(-1), "bf16").reshape(wl["target"].shape)
+    return dict(wl, target=vals.astype(np.float32), dtype="f32")
+
+
+@pytest.mark.parametrize("V", [32768, 32767, 40000])
+def test_filtered_f32_row_lengths(V):
+    """fp32 rows at the longest length one workgroup holds in LDS (32768
+    logits: whole 16-byte vectors; 32767: the unaligned element path), and
+    past it (40000: the row pass, then the streaming select), one-hot and
+    with draft logits, under a spread of top-k and top-p."""
+    wl = _onehot_f32(12, V, 434)
+    top_k, top_p = mixed_filters(12, V, 435)
+    check_filtered(wl, f"f32 one-hot V={V}", top_k, top_p)
+    check_filtered(wl, f"f32 one-hot V={V} top-p", None, np.full(12, 0.95, np.float32))
+    wl = make("c2_stoch", data_seed=436, B=10, V=V)
+    top_k, top_p = mixed_filters(10, V, 437)
+    check_filtered(wl, f"f32 explicit V={V}", top_k, top_p)
+
+
+def test_filtered_f32_odd_rows():
+    """fp32 rows on the LDS-resident select: a logit far above the rest (it
+    alone holds top-p), half the vocabulary at -inf, few distinct values
+    (wide ties), every logit equal (more equal values than one sort holds),
+    and a logit of 1e4, each with one-hot drafts."""
+    B, V = 6, 9000
+    wl = _onehot_f32(B, V, 438)
+    vals = wl["target"].copy()
+    vals[0, :, 11] = 80.0
+    vals[1, :, : V // 2] = -np.inf
+    vals[2] = np.round(vals[2] * 2) / 2
+    vals[3] = 1.5
+    vals[4, :, 3] = 1e4
+    wl = dict(wl, target=vals)
+    top_k = np.array([0, 5, 40, 0, 2, 0], np.int32)
+    top_p = np.array([0.9, 0.95, 0.5, 0.8, 0.95, 0.99], np.float32)
+    check_filtered(wl, "f32 odd rows", top_k, top_p, near_frac=0.5)
+
+
+def test_filtered_full_size_c2():
+    """C2 at its full size (fp32, draft logits) with top_p 0.95, every request."""
+    wl = make("c2_stoch", data_seed=1)
+    top_p = np.full(wl["B"], 0.95, np.float32)
+    check_filtered(wl, "c2 full top-p 0.95", None, top_p)
+
+
 def test_filtered_bf16_explicit_draft():
     wl = make("c2_stoch", data_seed=422, B=12, V=8192 + 100)
     wl = dict(wl, target=f32_to_bf16_bits(wl["target"]), dtype="bf16",
