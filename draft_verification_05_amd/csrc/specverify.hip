@@ -3168,6 +3168,105 @@ __global__ __launch_bounds__(kThreads) void sv_residual_kernel(Args A) {
   if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + a] = y;
 }
 
+// Filtered verification with draft logits on fp32 rows of at most
+// kRes1Chunks chunks: one workgroup of kDrawThreads per request. Wave 0 runs the
+// filtered rule and writes the outputs; the bonus token is drawn by all 16
+// waves (filtered_draw). For a request that stopped at a < K every wave sums
+// max(0, p'_a - q'_a) over its chunks of the stop row pair into LDS (two
+// chunks' loads of both rows in flight), and wave 0 finds the chunk and the
+// token: the chunk sums never leave the workgroup (no publish, no ticket).
+// Unfiltered calls keep the residual pass of several workgroups per request,
+// whose bonus draw reuses the row pass's chunk sums.
+constexpr int kRes1Chunks = 4 * kDrawWaves;
+
+template <int DT, bool kVec>
+__global__ __launch_bounds__(kDrawThreads) void sv_fresidual_kernel(Args A) {
+  constexpr int kCE = Chunk<DT>::kElems, kPer = Elem<DT>::kPerVec, E = kCE / 64;
+  __shared__ Record s_rc;
+  __shared__ float s_part[kRes1Chunks];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int b = blockIdx.x;
+  if (wave == 0) {
+    const Record r0 = filtered_tail<DT, kVec, kExplicit>(A, b, true);
+    if (lane == 0) s_rc = r0;
+  }
+  __syncthreads();
+  const Record rc = s_rc;
+  if (rc.draw) {                                   // all accepted: the bonus token
+    filtered_draw<DT, kVec>(A, b, rc, kDrawWaves);
+    return;
+  }
+  if (!rc.pending) return;
+  const int a = rc.a;
+  const float c = rc.c;
+  const float ip = 1.f / rc.Sp, iq = 1.f / rc.Sq;
+  const Req req = request(A, b);
+  const char* rowp = row_ptr(A, req, a);
+  const char* rowq = row_ptr(A, req, A.R + a);
+  // chunks wave, wave + kDrawWaves, ...: two at a time, all four row loads in flight
+  for (int ch0 = wave; ch0 < A.n_chunk; ch0 += 2 * kDrawWaves) {
+    ChunkRaw rp[2], rq[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int ch = ch0 + g * kDrawWaves;
+      const int64_t c0 = (int64_t)ch * kCE;
+      if (ch >= A.n_chunk) break;
+      if (kVec && ch < A.n_full) {
+        issue_chunk<DT>(rowp, c0, rp[g]);
+        issue_chunk<DT>(rowq, c0, rq[g]);
+      } else {
+        load_chunk_checked<DT, kVec>(rowp, c0, A.V, rp[g]);
+        load_chunk_checked<DT, kVec>(rowq, c0, A.V, rq[g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int ch = ch0 + g * kDrawWaves;
+      const int64_t c0 = (int64_t)ch * kCE;
+      if (ch >= A.n_chunk) break;
+      float sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < kLoadsPerLane; ++j)
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const float yp = raw_elem<DT>(rp[g], j, k), yq = raw_elem<DT>(rq[g], j, k);
+          const float wp = yp >= rc.tp ? fast_exp2(fmaf(yp, c, -rc.Mp)) * ip : 0.f;
+          const float wq = yq >= rc.tq ? fast_exp2(fmaf(yq, c, -rc.Mq)) * iq : 0.f;
+          sm += fmaxf(wp - wq, 0.f);
+        }
+      sm = wave_sum_all(sm);
+      if (lane == 0) s_part[ch] = sm;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;                           // the draw is one wave's work
+  int found;
+  float t_in;
+  const float Z = wave_locate(A.n_chunk, rc.u, [&](int sg) { return s_part[sg]; }, &found, &t_in);
+  int y = -1;
+  if (Z > 0.f && found >= 0) {
+    const int64_t c0 = (int64_t)found * kCE;
+    float xp[E], xq[E], w[E];
+    load_lane_run<DT, kVec, E>(rowp, c0, A.V, xp);
+    load_lane_run<DT, kVec, E>(rowq, c0, A.V, xq);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const float wp = xp[k] >= rc.tp ? fast_exp2(fmaf(xp[k], c, -rc.Mp)) * ip : 0.f;
+      const float wq = xq[k] >= rc.tq ? fast_exp2(fmaf(xq[k], c, -rc.Mq)) * iq : 0.f;
+      w[k] = fmaxf(wp - wq, 0.f);
+    }
+    y = wave_pick<E>(w, c0, t_in);
+  }
+  if (y < 0) {                                     // p'_a and q'_a agree everywhere: draw from p'_a
+    Record d = rc;
+    d.xe = -1;
+    filtered_draw<DT, kVec>(A, b, d, 1);           // this wave alone
+    return;
+  }
+  if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + a] = y;
+}
+
 // The workspace header's give-up count, copied to out (and cleared when
 // reset is set) in stream order.
 __global__ void sv_errors_kernel(unsigned* err, uint32_t* out, int reset) {
@@ -3442,8 +3541,19 @@ void launch_residual_dd(const Args& A, bool vec, unsigned grid, hipStream_t st) 
 
 template <int DT>
 void launch_residual_dt(const Args& A, bool vec, unsigned grid, hipStream_t st, bool decide) {
-  if (decide) launch_residual_dd<DT, true>(A, vec, grid, st);
-  else        launch_residual_dd<DT, false>(A, vec, grid, st);
+  if constexpr (DT == kF32) {                      // bf16 chunks would not fit its registers
+    if (decide && A.filtered && A.n_chunk <= kRes1Chunks) {   // one workgroup per request
+      const dim3 reqs((unsigned)A.B), wg(kDrawThreads);
+      if (vec) hipLaunchKernelGGL((sv_fresidual_kernel<DT, true>), reqs, wg, 0, st, A);
+      else     hipLaunchKernelGGL((sv_fresidual_kernel<DT, false>), reqs, wg, 0, st, A);
+      return;
+    }
+  }
+  if (decide) {
+    launch_residual_dd<DT, true>(A, vec, grid, st);
+  } else {
+    launch_residual_dd<DT, false>(A, vec, grid, st);
+  }
 }
 
 // Filtered verification: per row the cut and kept mass (bf16: the one-pass
