@@ -8,7 +8,8 @@ no fallback: without the built library every call raises.
 Entry points (same names as the C ABI):
   spec_verify_sample(target, draft, draft_tokens, temperature, seeds, offset)
   spec_verify_greedy(target, draft_tokens)
-  spec_verify_tree(target, node_tokens, parents)
+  spec_verify_tree(target, node_tokens, parents)           (parents: host [N], or device [B, N]
+                                                          for a tree per request)
   spec_verify_sample_ragged / spec_verify_greedy_ragged   (per-request draft counts)
   spec_verify_sample_masked / spec_verify_greedy_masked   (grammar bitmasks)
   spec_verify_sample_lazy                                 (early exit at the first rejection)
@@ -72,6 +73,8 @@ _SIGNATURES = {
                                           _vp, _c_size, _vp]),
     "spec_verify_tree": (ctypes.c_int, [_PSV, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
                                         _vp, _c_size, _vp]),
+    "spec_verify_tree_dynamic": (ctypes.c_int, [_PSV, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
+                                                _vp, _c_size, _vp]),
     "spec_verify_sample_ragged": (ctypes.c_int, [_PSV, _PSV, _vp, _c_i32, _vp, _vp, _vp, _c_u64,
                                                  _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp,
                                                  _c_size, _vp]),
@@ -488,23 +491,30 @@ def spec_verify_greedy_masked(target: torch.Tensor, draft_tokens: torch.Tensor, 
 
 
 def spec_verify_tree(target: torch.Tensor, node_tokens: torch.Tensor, parents):
-    """Tree verification. ``parents`` is a host sequence. Returns (tokens [B,N], accept_len [B], best [B])."""
+    """Tree verification. ``parents`` is a host sequence of N entries (one tree for the
+    batch), or an int32 tensor [B, N] on the target's device (a tree per request:
+    spec_verify_tree_dynamic). Returns (tokens [B,N], accept_len [B], best [B])."""
     lib = load_library()
     B, N, V = target.shape
     dev = target.device
     tdesc = _desc(target, "target")
     _check(node_tokens, "node_tokens", torch.int32, (B, N), dev)
-    if len(parents) != N:
-        raise ValueError("parents must have one entry per node")
-    par = (ctypes.c_int32 * N)(*[int(v) for v in parents])
+    dynamic = isinstance(parents, torch.Tensor) and parents.dim() == 2
+    if dynamic:
+        _check(parents, "parents", torch.int32, (B, N), dev)
+        par_ptr, fn, name = ctypes.c_void_p(parents.data_ptr()), lib.spec_verify_tree_dynamic, \
+            "spec_verify_tree_dynamic"
+    else:
+        if len(parents) != N:
+            raise ValueError("parents must have one entry per node")
+        par = (ctypes.c_int32 * N)(*[int(v) for v in parents])
+        par_ptr, fn, name = ctypes.cast(par, ctypes.c_void_p), lib.spec_verify_tree, "spec_verify_tree"
     tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
     alen = torch.empty((B,), dtype=torch.int32, device=dev)
     best = torch.empty((B,), dtype=torch.int32, device=dev)
     ws = _workspace(dev, spec_verify_workspace_size(SV_OP_TREE, B, N, V))
-    rc = lib.spec_verify_tree(ctypes.byref(tdesc), node_tokens.data_ptr(),
-                              ctypes.cast(par, ctypes.c_void_p), N, B, V, tokens.data_ptr(),
-                              alen.data_ptr(), best.data_ptr(), ws.data_ptr(), ws.numel(),
-                              _stream_ptr(dev))
+    rc = fn(ctypes.byref(tdesc), node_tokens.data_ptr(), par_ptr, N, B, V, tokens.data_ptr(),
+            alen.data_ptr(), best.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(dev))
     if rc:
-        raise SpecVerifyError(rc, "spec_verify_tree")
+        raise SpecVerifyError(rc, name)
     return tokens, alen, best

@@ -121,6 +121,7 @@ struct Args {
   int n_nodes;
   int8_t parent[SV_MAX_TREE_NODES];
   int8_t depth[SV_MAX_TREE_NODES];   // depth of each node (root 0)
+  const int32_t* dyn_parents;        // dynamic trees: [B, N] parent arrays on the device (else null)
 };
 
 // The tail keeps a request's partials in LDS when they fit, so the draw
@@ -1052,23 +1053,44 @@ template <bool kTagged>
 __device__ void tree_tail(const Args& A, int b, int* sg) {
   const int lane = threadIdx.x & 63, N = A.n_nodes;
   const int xn = lane < N ? A.tokens[(int64_t)b * N + lane] : -1;
+  // this request's tree: the call's static one, or its own row of a
+  // dynamic batch (loaded with the tokens, checked below)
+  int par = lane < N ? (A.dyn_parents ? A.dyn_parents[(int64_t)b * N + lane] : A.parent[lane]) : -1;
+  int32_t* out = A.out_tokens + (int64_t)b * A.out_cols;
+  auto refuse = [&]() {
+    if (lane < N) out[lane] = -1;
+    if (lane == 0) {
+      A.out_len[b] = 0;
+      if (A.out_aux) A.out_aux[b] = -1;
+    }
+  };
   WStaged ws;
   const float2 identity = make_float2(kNegInf, __int_as_float(INT_MAX));
   if constexpr (kTagged) {
     if (!wstage_tagged(A, b, N, identity, ws)) {   // the wait gave up: refuse the request
       count_give_up(A);
-      if (lane < N) A.out_tokens[(int64_t)b * A.out_cols + lane] = -1;
-      if (lane == 0) {
-        A.out_len[b] = 0;
-        if (A.out_aux) A.out_aux[b] = -1;
-      }
+      refuse();
       return;
     }
   } else {
     wstage_issue(A, b, N, identity, ws);
   }
-  const int par = lane < N ? A.parent[lane] : -1;
-  const int dep = lane < N ? A.depth[lane] : 0;
+  int dep = lane < N ? A.depth[lane] : 0;
+  if (A.dyn_parents) {
+    // a row that is not a tree (the root's parent not -1, or a parent not
+    // before its child) refuses its request; depths by N - 1 relaxation steps
+    const bool bad = lane < N && (lane == 0 ? par != -1 : (par < 0 || par >= lane));
+    if (__ballot(bad) != 0ull) {
+      refuse();
+      if constexpr (kTagged) wclear_tagged(A, b, N, ws);
+      return;
+    }
+    dep = 0;
+    for (int it = 1; it < N; ++it) {              // uniform; parents precede children
+      const int pd = __shfl(dep, par < 0 ? 0 : par);
+      dep = (lane > 0 && lane < N) ? pd + 1 : 0;
+    }
+  }
   merge_argmax_rows(A, b, N, sg, ws);
   const int g_par = sg[par < 0 ? 0 : par];
   const bool ok = lane == 0 || (lane < N && xn == g_par);
@@ -1083,10 +1105,9 @@ __device__ void tree_tail(const Args& A, int b, int* sg) {
   const int kmax = (int)wave_max_all((float)key);
   const int best = 127 - (kmax & 127), len = kmax >> 7;
   uint64_t on_path = 0ull;
-  for (int n = best; n > 0; n = A.parent[n]) on_path |= 1ull << n;
+  for (int n = best; n > 0; n = __shfl(par, n)) on_path |= 1ull << n;   // uniform walk to the root
   // each position once: path nodes fill 0..len-1 (one node per depth), then
   // the argmax at the deepest node, then -1
-  int32_t* out = A.out_tokens + (int64_t)b * A.out_cols;
   if (lane > 0 && lane < N && ((on_path >> lane) & 1ull)) out[dep - 1] = xn;
   if (lane == len) out[len] = sg[best];
   if (lane > len && lane < N) out[lane] = -1;
@@ -3479,6 +3500,7 @@ void fill_common(Args& A, const sv_logits* t, int B, int K, int V, int R, int ro
   A.temperature = nullptr; A.seeds = nullptr; A.offset = 0;
   A.n_nodes = 0;
   for (int i = 0; i < SV_MAX_TREE_NODES; ++i) { A.parent[i] = -1; A.depth[i] = 0; }
+  A.dyn_parents = nullptr;
 }
 
 #define SV_LAUNCH(KERNEL, grid, st, A) \
@@ -3864,6 +3886,53 @@ int greedy_impl(const sv_logits* target, const int32_t* cu, int32_t total_k, con
 
 }  // namespace
 
+namespace {
+
+// Tree verification, static (host parents, checked here) or dynamic (one
+// parent row per request on the device, checked by the tail).
+int tree_impl(const sv_logits* target, const int32_t* node_tokens, const int32_t* parents, bool dynamic,
+              int32_t N, int32_t B, int32_t V, int32_t* out_tokens, int32_t* out_accept_len,
+              int32_t* out_best_node, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(target);
+  if (st) return st;
+  if (!node_tokens || !parents || !out_tokens || !out_accept_len) return SV_ERR_NULL;
+  if (B < 1 || B > SV_MAX_BATCH || V < 1 || V > SV_MAX_VOCAB || N < 2 || N > SV_MAX_TREE_NODES)
+    return SV_ERR_SHAPE;
+  if (!dynamic) {
+    if (parents[0] != -1) return SV_ERR_TREE;
+    for (int n = 1; n < N; ++n)
+      if (parents[n] < 0 || parents[n] >= n) return SV_ERR_TREE;
+  }
+  if (!workspace) return SV_ERR_WORKSPACE;
+  if (workspace_bytes < layout(B, N, V).total) return SV_ERR_WORKSPACE;
+  if ((st = device_status())) return st;
+  Args A;
+  fill_common(A, target, B, 0, V, N, N, workspace);
+  A.tokens = node_tokens;
+  A.out_cols = N;
+  A.out_tokens = out_tokens;
+  A.out_len = out_accept_len;
+  A.out_aux = out_best_node;
+  A.n_nodes = N;
+  if (dynamic) {
+    A.dyn_parents = parents;
+  } else {
+    for (int n = 0; n < N; ++n) {
+      A.parent[n] = (int8_t)parents[n];
+      A.depth[n] = (int8_t)(n == 0 ? 0 : A.depth[parents[n]] + 1);   // parents[n] < n
+    }
+  }
+  argmax_runs(A);
+  const int64_t wgs = (int64_t)B * N * A.wpr;
+  if ((st = check_grid(wgs))) return st;
+  plan_one_launch(A, kTree, wgs);
+  launch_rows<kTree>(A, target->dtype, aligned16(target), (unsigned)wgs,
+                     static_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t spec_verify_workspace_size(int32_t op, int32_t B, int32_t K_or_N, int32_t V,
@@ -4019,36 +4088,16 @@ int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
                      const int32_t* parents, int32_t N, int32_t B, int32_t V,
                      int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_best_node,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_desc(target);
-  if (st) return st;
-  if (!node_tokens || !parents || !out_tokens || !out_accept_len) return SV_ERR_NULL;
-  if (B < 1 || B > SV_MAX_BATCH || V < 1 || V > SV_MAX_VOCAB || N < 2 || N > SV_MAX_TREE_NODES)
-    return SV_ERR_SHAPE;
-  if (parents[0] != -1) return SV_ERR_TREE;
-  for (int n = 1; n < N; ++n)
-    if (parents[n] < 0 || parents[n] >= n) return SV_ERR_TREE;
-  if (!workspace) return SV_ERR_WORKSPACE;
-  if (workspace_bytes < layout(B, N, V).total) return SV_ERR_WORKSPACE;
-  if ((st = device_status())) return st;
-  Args A;
-  fill_common(A, target, B, 0, V, N, N, workspace);
-  A.tokens = node_tokens;
-  A.out_cols = N;
-  A.out_tokens = out_tokens;
-  A.out_len = out_accept_len;
-  A.out_aux = out_best_node;
-  A.n_nodes = N;
-  for (int n = 0; n < N; ++n) {
-    A.parent[n] = (int8_t)parents[n];
-    A.depth[n] = (int8_t)(n == 0 ? 0 : A.depth[parents[n]] + 1);   // parents[n] < n
-  }
-  argmax_runs(A);
-  const int64_t wgs = (int64_t)B * N * A.wpr;
-  if ((st = check_grid(wgs))) return st;
-  plan_one_launch(A, kTree, wgs);
-  launch_rows<kTree>(A, target->dtype, aligned16(target), (unsigned)wgs,
-                     static_cast<hipStream_t>(stream));
-  return hip_status();
+  return tree_impl(target, node_tokens, parents, false, N, B, V, out_tokens, out_accept_len, out_best_node,
+                   workspace, workspace_bytes, stream);
+}
+
+int spec_verify_tree_dynamic(const sv_logits* target, const int32_t* node_tokens,
+                             const int32_t* parents, int32_t N, int32_t B, int32_t V,
+                             int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_best_node,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return tree_impl(target, node_tokens, parents, true, N, B, V, out_tokens, out_accept_len, out_best_node,
+                   workspace, workspace_bytes, stream);
 }
 
 int spec_verify_workspace_errors(void* workspace, size_t workspace_bytes, uint32_t* out_count,

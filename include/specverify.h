@@ -365,6 +365,25 @@ int spec_verify_tree(const sv_logits* target, const int32_t* node_tokens,
                      int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_best_node,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Greedy verification of dynamic draft trees: a tree per request, as the
+ * drafter builds it for each context (EAGLE-2, "推测解码与 MTP" §4.3: the
+ * best tree differs by position and context, so each step keeps only the
+ * most promising nodes). The rule per request is spec_verify_tree's.
+ *
+ * parents      [B, N] int32, device, row-major: request b's tree is row b,
+ *              with parents[b, 0] == -1 and 0 <= parents[b, n] < n
+ * Every other argument, output and host error as spec_verify_tree (the
+ * workspace of SV_OP_TREE with the same B, N, V). The rows are checked on
+ * the device: a request whose row is not such a tree is refused
+ * (out_accept_len 0, out_tokens -1, out_best_node -1) and the others are
+ * verified as usual.
+ */
+int spec_verify_tree_dynamic(const sv_logits* target, const int32_t* node_tokens,
+                             const int32_t* parents, int32_t N, int32_t B, int32_t V,
+                             int32_t* out_tokens, int32_t* out_accept_len, int32_t* out_best_node,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* spec_verify_status_string(int status);
 

@@ -417,22 +417,37 @@ def tree_depths(parents) -> list:
 
 
 def spec_verify_tree(target, node_tokens, parents, dtype="f32"):
-    """Greedy verification of a static draft tree (Medusa style).
+    """Greedy verification of a static draft tree (Medusa style), or of a
+    tree per request (dynamic trees, EAGLE-2: "推测解码与 MTP" §4.3).
 
     target [B, N, V]: logits at every node (row n predicts the token after
-    node n); node_tokens [B, N] (column 0, the root, is ignored).
+    node n); node_tokens [B, N] (column 0, the root, is ignored); parents
+    [N] (one tree for the batch; a malformed one raises ValueError) or
+    [B, N] (row b is request b's tree; a request whose row is not a tree is
+    refused: tokens -1, accept_len 0, best_node -1).
     Returns (tokens [B, N] -1 padded, accept_len [B], best_node [B]).
     """
     B, N, V = target.shape
-    depth = tree_depths(parents)
+    par = np.asarray(parents)
+    per_request = par.ndim == 2
+    shared_depth = None if per_request else tree_depths(par)
     tokens = np.full((B, N), -1, dtype=np.int32)
     accept_len = np.zeros(B, dtype=np.int32)
     best_node = np.zeros(B, dtype=np.int32)
     for b in range(B):
+        pb = par[b] if per_request else par
+        if per_request:
+            try:
+                depth = tree_depths(pb)
+            except ValueError:
+                best_node[b] = -1
+                continue
+        else:
+            depth = shared_depth
         g = [argmax_lowest(logits_f64(target[b, n], dtype)) for n in range(N)]
         acc = [True] + [False] * (N - 1)
         for n in range(1, N):
-            p = int(parents[n])
+            p = int(pb[n])
             acc[n] = acc[p] and int(node_tokens[b, n]) == g[p]
         best = 0
         for n in range(1, N):
@@ -442,7 +457,7 @@ def spec_verify_tree(target, node_tokens, parents, dtype="f32"):
         n = best
         while n != 0:
             path.append(int(node_tokens[b, n]))
-            n = int(parents[n])
+            n = int(pb[n])
         path.reverse()
         row = path + [g[best]]
         tokens[b, :len(row)] = row

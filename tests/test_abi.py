@@ -128,6 +128,18 @@ def test_tree_argument_errors(lib):
     assert tr(ctypes.byref(t), FAKE, ok, 3, 1, 5, FAKE, FAKE, None, FAKE, 100, None) == sv.SV_ERR_WORKSPACE
 
 
+def test_tree_dynamic_argument_errors(lib):
+    """The per-request parents live on the device: the host checks pointers,
+    shapes and the workspace, and leaves the rows to the kernel."""
+    tr = lib.spec_verify_tree_dynamic
+    t = desc()
+    assert tr(ctypes.byref(t), FAKE, None, 3, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_NULL
+    assert tr(ctypes.byref(t), FAKE, FAKE, 1, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+    assert tr(ctypes.byref(t), FAKE, FAKE, 65, 1, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+    assert tr(ctypes.byref(t), FAKE, FAKE, 3, 0, 5, FAKE, FAKE, None, FAKE, BIG_WS, None) == sv.SV_ERR_SHAPE
+    assert tr(ctypes.byref(t), FAKE, FAKE, 3, 1, 5, FAKE, FAKE, None, FAKE, 100, None) == sv.SV_ERR_WORKSPACE
+
+
 def test_workspace_init_null(lib):
     assert lib.spec_verify_workspace_init(None, 100, None) == sv.SV_ERR_NULL
 

@@ -255,6 +255,45 @@ def test_tree_random_shapes(seed):
     check_tree(wl, parents, f"tree N={N} V={V}")
 
 
+@pytest.mark.parametrize("one_launch", ["1", "0"])
+def test_tree_dynamic_per_request(one_launch, monkeypatch):
+    """A tree per request (dynamic trees): random trees of N = 31 nodes, two
+    rows that are not trees (refused alone), against the oracle; then every
+    row the same tree, bitwise equal to the static call. One launch and two."""
+    monkeypatch.setenv("SPECVERIFY_ONE_LAUNCH", one_launch)
+    rng = np.random.default_rng(320)
+    B, N, V = 24, 31, 9000
+    parents = np.array([[-1] + [int(rng.integers(0, n)) for n in range(1, N)] for _ in range(B)], np.int32)
+    parents[5, 0] = 3
+    parents[17, 20] = 25
+    tgt = rng.normal(0, 1, (B, N, V)).astype(np.float32)
+    g = tgt.argmax(-1)
+    tok = rng.integers(0, V, (B, N)).astype(np.int32)
+    for b in range(B):                       # make acceptance likely along some edges
+        for n in range(1, N):
+            if rng.random() < 0.7 and 0 <= parents[b, n] < N:
+                tok[b, n] = g[b, parents[b, n]]
+    print(f"[case] dynamic trees one_launch={one_launch} B={B} N={N} V={V}", flush=True)
+    d_tgt = torch.from_numpy(tgt).to(DEV)
+    d_tok = torch.from_numpy(tok).to(DEV)
+    d_par = torch.from_numpy(parents).to(DEV)
+    out = sv.spec_verify_tree(d_tgt, d_tok, d_par)
+    torch.cuda.synchronize()
+    o_tok, o_len, o_best = oracle.spec_verify_tree(tgt, tok, parents)
+    np.testing.assert_array_equal(out[2].cpu().numpy(), o_best)
+    np.testing.assert_array_equal(out[1].cpu().numpy(), o_len)
+    np.testing.assert_array_equal(out[0].cpu().numpy(), o_tok)
+    assert o_len[5] == 0 and o_len[17] == 0
+    shared = parents[0]
+    dyn = sv.spec_verify_tree(d_tgt, d_tok, torch.from_numpy(np.tile(shared, (B, 1))).to(DEV))
+    sta = sv.spec_verify_tree(d_tgt, d_tok, list(shared))
+    torch.cuda.synchronize()
+    for x, y in zip(dyn, sta):
+        np.testing.assert_array_equal(x.cpu().numpy(), y.cpu().numpy())
+    print(f"[parity] dynamic trees one_launch={one_launch}: exact, accept_len histogram="
+          f"{np.bincount(o_len).tolist()}", flush=True)
+
+
 def test_chain_tree_equals_greedy_on_gpu():
     wl = make("c4_greedy", data_seed=22, B=16, K=5, V=10000)
     d = to_device(wl, DEV)

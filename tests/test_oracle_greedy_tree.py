@@ -112,6 +112,46 @@ def test_tree_brute_force_over_paths(seed):
         assert np.all(tok[b, len(seq):] == -1)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_tree_per_request_brute_force_over_paths(seed):
+    """A tree per request ([B, N] parents, dynamic trees): each request against
+    the brute force over its own tree's paths; a row that is not a tree
+    refuses only its own request."""
+    rng = np.random.default_rng(200 + seed)
+    B, N, V = 10, int(rng.integers(2, 16)), 5
+    parents = np.array([[-1] + [int(rng.integers(0, n)) for n in range(1, N)] for _ in range(B)], np.int32)
+    bad = {3: (0, 0), 7: (N - 1, N - 1)}             # root with a parent; a node its own parent
+    for b, (n, v) in bad.items():
+        parents[b, n] = v
+    tgt = rng.normal(0, 1, (B, N, V)).astype(np.float32)
+    node_tok = rng.integers(0, V, (B, N)).astype(np.int32)
+    tok, alen, best = oracle.spec_verify_tree(tgt, node_tok, parents)
+    for b in range(B):
+        if b in bad:
+            assert (alen[b], best[b]) == (0, -1) and np.all(tok[b] == -1)
+            continue
+        paths = _paths(parents[b])
+        g = [slow_argmax(tgt[b, n].tolist()) for n in range(N)]
+        ok = [n for n, path in paths.items()
+              if all(node_tok[b, c] == g[p] for p, c in zip(path[:-1], path[1:]))]
+        deepest = max(len(paths[n]) for n in ok)
+        want = min(n for n in ok if len(paths[n]) == deepest)
+        assert best[b] == want
+        seq = [int(node_tok[b, n]) for n in paths[want][1:]] + [g[want]]
+        assert alen[b] == len(seq)
+        np.testing.assert_array_equal(tok[b, :len(seq)], seq)
+        assert np.all(tok[b, len(seq):] == -1)
+
+
+def test_tree_shared_parents_equal_per_request_rows():
+    wl = make("c5_tree", data_seed=6, B=5, V=300)
+    par = wl["parents"]
+    a = oracle.spec_verify_tree(wl["target"], wl["draft_tokens"], par)
+    b = oracle.spec_verify_tree(wl["target"], wl["draft_tokens"], np.tile(par, (5, 1)))
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_medusa_tree_golden():
     with open(os.path.join(GOLDEN, "medusa_tree_3x3x2.json")) as f:
         gold = json.load(f)
