@@ -841,6 +841,20 @@ def test_filtered_f32_odd_rows():
     check_filtered(wl, "f32 odd rows", top_k, top_p, near_frac=0.5)
 
 
+@pytest.mark.parametrize("V", [1, 3, 17])
+def test_filtered_tiny_vocab(V):
+    """Rows of 1, 3 and 17 logits (a partial vector in the LDS-resident select,
+    a single chunk in the residual pass), fp32 one-hot and with draft logits,
+    bf16 one-hot; top_p 0 keeps the largest value only, top_k 1 likewise."""
+    top_k = np.array([0, 1, 2, 0, 0, V], np.int32)
+    top_p = np.array([0.0, 1.0, 0.9, 0.5, 0.95, 0.99], np.float32)
+    check_filtered(_onehot_f32(6, V, 440), f"f32 one-hot V={V}", top_k, top_p, near_frac=0.5)
+    check_filtered(make("c2_stoch", data_seed=441, B=6, K=2, V=V), f"f32 explicit V={V}", top_k, top_p,
+                   near_frac=0.5)
+    check_filtered(make("c3_onehot", data_seed=442, B=6, K=2, V=V), f"bf16 one-hot V={V}", top_k, top_p,
+                   near_frac=0.5)
+
+
 def test_filtered_full_size_c2():
     """C2 at its full size (fp32, draft logits) with top_p 0.95, every request."""
     wl = make("c2_stoch", data_seed=1)
