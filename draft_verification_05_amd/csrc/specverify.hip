@@ -1668,11 +1668,13 @@ constexpr int kHBins = 4096;                      // per sign: magnitudes [2^-16
 constexpr uint32_t kHMagLo = 0x3780u;             // bf16 magnitude bits of 2^-16
 constexpr int kHOrd = 2 * kHBins + 2;             // ordered positions (hist_value)
 // Word of magnitude m (table: kHMagLo <= m < kHMagLo + kHBins) and sign s:
-// kHOff + (m - kHMagLo) + s * kHNeg; values below / above the table land in
-// the spare words just before / after their sign's table (kHOff - 1,
-// kHOff + kHBins). Both tables start 16-byte aligned.
-constexpr int kHOff = 4, kHNeg = kHBins + 8;
-constexpr int kHWords = kHOff + kHNeg + kHBins + 4;
+// kHOff + (m - kHMagLo) + s * kHNeg, the negative table right after the
+// positive one (the sign bit, shifted, is the byte offset of the negative
+// table). Values outside the table are counted at their sign's last word
+// and taken out again after the pass.
+constexpr int kHOff = 0, kHNeg = kHBins;
+constexpr int kHWords = 2 * kHBins;
+static_assert(kHNeg * 4 == 0x4000, "the sign bit shifted right by one is the negative table's byte offset");
 
 struct alignas(16) SelLds {
   union {
@@ -1682,7 +1684,7 @@ struct alignas(16) SelLds {
       uint32_t key[kSelCap];
       double w[kSelCap];
     };
-    uint32_t hcnt[kHWords];                        // the two tables and their spare words
+    uint32_t hcnt[kHWords];                        // the positive table, then the negative one
   };
   double scan[kThreads];
   double tab[64];                                  // 2^(j / 64)
@@ -1693,7 +1695,7 @@ struct alignas(16) SelLds {
   uint32_t kfloor;
   unsigned tiny_n, ninf_n, tiny_max;               // tiny count, -inf count, largest tiny order key
   int big;                                         // a value outside the table that is not -inf
-  int sel_max, sel_k, sel_p;                       // picked positions (INT_MAX: none)
+  int sel_max[kWaves], sel_k[kWaves], sel_p[kWaves];   // each wave's smallest pick candidate
   uint32_t kcut, kmin;                             // rank_cut's picks
 };
 
@@ -1750,6 +1752,14 @@ __device__ __forceinline__ double dpp_d(double v) {
   const uint64_t u = (uint64_t)__double_as_longlong(v);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, kRows, 0xF, false);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl, kRows, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Lane l's value of v, in every lane (l wave-uniform).
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
@@ -2038,6 +2048,7 @@ struct HistRare {
   float s1, s2, s3;                                // sums of l, l^2, l^3 over tiny magnitudes
   unsigned n, ninf, kmax;                          // tiny count, -inf count, largest tiny order key
   bool big;                                        // NaN, +inf or |l| >= 2^16
+  uint32_t undo_p, undo_n;                         // what they added to each sign's last word
   __device__ __forceinline__ void add(uint32_t h) {
     if ((h & 0x7FFFu) < kHMagLo) {
       const float v = __uint_as_float(h << 16);
@@ -2056,15 +2067,17 @@ struct HistRare {
 
 // One pass over a bf16 row into the counters (zeroed, with the tallies and
 // pick slots, while the first loads are in flight), then the lanes'
-// tallies folded into L. A magnitude is
-// clamped to the table's range plus one spare word each side, so a value
-// outside the table costs no extra instruction on the common path; the
-// lanes holding one also take the rare path.
+// tallies folded into L. Both logits of a 32-bit word are indexed at once
+// in 16-bit lanes: magnitude - kHMagLo, wrapping below the table, clamped
+// to the table's last position, so that a value outside the table (tiny,
+// -inf, NaN, |l| >= 2^16) costs no extra instruction on the common path;
+// one compare finds the words holding one, whose lanes take the rare path
+// and later take their counts back out of the last words.
+typedef unsigned short HU16x2 __attribute__((ext_vector_type(2)));
 template <bool kVec>
 __device__ __forceinline__ void hist_pass(const char* row, int n_chunk, int V, SelLds& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr uint32_t lo = kHMagLo - 1u, hi = kHMagLo + kHBins;
-  HistRare t{0.f, 0.f, 0.f, 0u, 0u, 0u, false};
+  HistRare t{0.f, 0.f, 0.f, 0u, 0u, 0u, false, 0u, 0u};
   auto zero = [&]() {
     uint4* z = reinterpret_cast<uint4*>(L.hcnt);
     for (int j = threadIdx.x; j < kHWords / 4; j += kThreads) z[j] = make_uint4(0u, 0u, 0u, 0u);
@@ -2073,25 +2086,30 @@ __device__ __forceinline__ void hist_pass(const char* row, int n_chunk, int V, S
       L.ninf_n = 0u;
       L.tiny_max = 0u;
       L.big = 0;
-      L.sel_max = INT_MAX;
-      L.sel_k = INT_MAX;
-      L.sel_p = INT_MAX;
     }
     if (threadIdx.x < 64) L.tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
     __syncthreads();
   };
+  char* const base = reinterpret_cast<char*>(L.hcnt);
   for_each_word_bf16<kVec>(row, n_chunk, V, zero, [&](uint32_t w, int64_t) {
-    const uint32_t m0 = w & 0x7FFFu, m1 = (w >> 16) & 0x7FFFu;
-    const uint32_t c0 = min(max(m0, lo), hi), c1 = min(max(m1, lo), hi);
-    const uint32_t i0 = c0 + ((w >> 15) & 1u) * (uint32_t)kHNeg, i1 = c1 + (w >> 31) * (uint32_t)kHNeg;
-    atomicAdd(&L.hcnt[i0 - (kHMagLo - kHOff)], 1u);
-    atomicAdd(&L.hcnt[i1 - (kHMagLo - kHOff)], 0x10000u);
-    // outside the table: the offset decides, not the clamp (the magnitudes
-    // next to the table clamp to themselves)
-    const bool o0 = m0 - kHMagLo >= (uint32_t)kHBins, o1 = m1 - kHMagLo >= (uint32_t)kHBins;
-    if (o0 || o1) {
-      if (o0) t.add(w & 0xFFFFu);
-      if (o1) t.add(w >> 16);
+    constexpr unsigned short lo = kHMagLo, top = kHBins - 1;
+    const HU16x2 d = __builtin_bit_cast(HU16x2, w & 0x7FFF7FFFu) - HU16x2{lo, lo};
+    const HU16x2 e = __builtin_elementwise_min(d, HU16x2{top, top});
+    // byte offsets of the two words: 4 e, plus the negative table's 0x4000
+    const uint32_t a = __builtin_bit_cast(uint32_t, HU16x2(e << (unsigned short)2)) | ((w >> 1) & 0x40004000u);
+    atomicAdd(reinterpret_cast<uint32_t*>(base + (a & 0xFFFFu)), 1u);
+    atomicAdd(reinterpret_cast<uint32_t*>(base + (a >> 16)), 0x10000u);
+    if (__builtin_bit_cast(uint32_t, e) != __builtin_bit_cast(uint32_t, d)) {
+      if (e.x != d.x) {
+        if (w & 0x8000u) t.undo_n += 1u;
+        else t.undo_p += 1u;
+        t.add(w & 0xFFFFu);
+      }
+      if (e.y != d.y) {
+        if (w & 0x80000000u) t.undo_n += 0x10000u;
+        else t.undo_p += 0x10000u;
+        t.add(w >> 16);
+      }
     }
   });
   const float s1 = wave_sum_all(t.s1), s2 = wave_sum_all(t.s2), s3 = wave_sum_all(t.s3);
@@ -2106,6 +2124,8 @@ __device__ __forceinline__ void hist_pass(const char* row, int n_chunk, int V, S
   }
   if (t.ninf) atomicAdd(&L.ninf_n, t.ninf);
   if (t.big) L.big = 1;
+  if (t.undo_p) atomicSub(&L.hcnt[kHOff + kHBins - 1], t.undo_p);
+  if (t.undo_n) atomicSub(&L.hcnt[kHOff + kHNeg + kHBins - 1], t.undo_n);
   __syncthreads();
 }
 
@@ -2176,15 +2196,24 @@ __device__ __forceinline__ int hist_owner(int o) {
 
 // Every thread passes its candidate position (INT_MAX: none) and the
 // running sum there; returns the smallest candidate over the workgroup (-1:
-// none), gathered in *slot (INT_MAX since the row's start), and its sum in
-// *at (from L.scan, where each candidate leaves its own).
-__device__ __forceinline__ int hist_pick(SelLds& L, int* slot, int mine, double mine_at, double* at) {
-  if (mine != INT_MAX) {
-    atomicMin(slot, mine);
-    L.scan[threadIdx.x] = mine_at;
-  }
+// none), and its sum in *at (from L.scan, where each candidate leaves its
+// own). Each wave's smallest candidate, found on the DPP network, goes to
+// picks[wave] with one store: LDS atomics from every lane to one word queue
+// behind the counting of the CU's other workgroups (measured: 2 us).
+__device__ __forceinline__ int hist_pick(SelLds& L, int* picks, int mine, double mine_at, double* at) {
+  if (mine != INT_MAX) L.scan[threadIdx.x] = mine_at;
+  int m = mine;
+  m = min(m, dpp_i<kDppXor1>(m));
+  m = min(m, dpp_i<kDppXor2>(m));
+  m = min(m, dpp_i<kDppHalfMirror>(m));
+  m = min(m, dpp_i<kDppMirror>(m));
+  m = min(min(__builtin_amdgcn_readlane(m, 0), __builtin_amdgcn_readlane(m, 16)),
+          min(__builtin_amdgcn_readlane(m, 32), __builtin_amdgcn_readlane(m, 48)));
+  if ((threadIdx.x & 63) == 0) picks[threadIdx.x >> 6] = m;
   __syncthreads();
-  const int o = *slot;
+  int o = picks[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) o = min(o, picks[w]);
   if (o == INT_MAX) return -1;
   *at = L.scan[hist_owner(o)];
   return o;
@@ -2708,7 +2737,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
     int o_max, o_k = -1;
     double at;
     // the largest value: the first counted position
-    o_max = hist_pick(L, &L.sel_max, j1 < kHPerT ? hb.o0 + j1 : (hb.nx ? hb.ox : INT_MAX), 0.0, &at);
+    o_max = hist_pick(L, L.sel_max, j1 < kHPerT ? hb.o0 + j1 : (hb.nx ? hb.ox : INT_MAX), 0.0, &at);
     // counts: the top-k cut, and the total (a carry between the halves of a
     // word, possible only when V / 2 > 65535, shows as a total other than V)
     const bool k_on = tk > 0 && tk < A.V;
@@ -2728,7 +2757,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
           }
           if (mine == INT_MAX) mine = hb.ox;       // the extra position completes it
         }
-        o_k = hist_pick(L, &L.sel_k, mine, 0.0, &at);
+        o_k = hist_pick(L, L.sel_k, mine, 0.0, &at);
       }
     }
     if (!general && (o_max < 0 || o_max == kHOrd - 1)) {   // nothing but -inf: no mass
@@ -2787,34 +2816,54 @@ __global__ __launch_bounds__(kThreads, 4) void sv_hselect_kernel(Args A) {
         const double target = fmax((double)tp * zk, __DBL_MIN__);
         int mine = INT_MAX;
         double mine_at = 0.0;
-        if (me < target && mi >= target) {
-          const double rr = exp2_weight(-ucd, L.tab);
-          double run = me, w = j1 < kHPerT ? exp2_weight((double)(hb.v0 - (float)j1 * hb.u) * cd - (double)mref, L.tab)
-                                           : 0.0;
+        // The run holding the crossing is walked by its thread's whole
+        // wave, lane j at the run's position j: its count from the table,
+        // its weight by its own exp2 (one thread walking 32 positions in a
+        // dependent chain took 2.4 us on a CU busy with other rows). The
+        // first position whose running mass reaches the target is the
+        // cut; a sum that rounds short of the scan's takes the run's last
+        // position of positive mass, then the tiny ones, as the sequential
+        // walk did.
+        const uint64_t cross = __ballot(me < target && mi >= target);
+        if (cross) {                               // uniform within the wave
+          const int c = __builtin_ctzll(cross);
+          const int o0 = __builtin_amdgcn_readlane(hb.o0, c), j1c = __builtin_amdgcn_readlane(j1, c);
+          const int limc = __builtin_amdgcn_readlane(lim, c), oxc = __builtin_amdgcn_readlane(hb.ox, c);
+          const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hb.v0), c));
+          const float uu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hb.u), c));
+          const double mec = readlane_d(me, c), mic = readlane_d(mi, c), mxc = readlane_d(mx, c);
+          const int j = lane;
+          double x = 0.0;
+          if (j < kHPerT && j >= j1c && j <= limc) {
+            const int o = o0 + j;
+            const uint32_t wd = L.hcnt[o < kHBins ? kHOff + (kHBins - 1 - o) : kHOff + kHNeg + (o - kHBins - 1)];
+            const uint32_t n = (wd & 0xFFFFu) + (wd >> 16);
+            if (n) x = (double)n * exp2_weight((double)(v0 - (float)j * uu) * cd - (double)mref, L.tab);
+          }
+          const double pre = wave_scan_incl_d(x);
+          const uint64_t hit = __ballot(x > 0.0 && mec + pre >= target);
           int last = -1;
-#pragma unroll
-          for (int j = 0; j < kHPerT; ++j) {
-            if (j >= j1) {
-              const double x = j <= lim ? (double)hb.n[j] * w : 0.0;
-              w *= rr;
-              if (x > 0.0 && run < target) {
-                run += x;
-                last = hb.o0 + j;
-              }
+          double at = 0.0;
+          if (hit) {
+            const int h = __builtin_ctzll(hit);
+            last = o0 + h;
+            at = mec + readlane_d(pre, h);
+          } else {
+            const uint64_t any = __ballot(x > 0.0);
+            double run = mec + readlane_d(pre, 63);
+            if (any) last = o0 + 63 - __builtin_clzll(any);
+            if (run < target && mxc > 0.0) {
+              run += mxc;
+              last = oxc;
             }
+            at = run >= target ? run : mic;
           }
-          if (run < target && mx > 0.0) {
-            run += mx;
-            last = hb.ox;
-          }
-          // a sequential sum that rounds short of the scan's: the run's
-          // last position of positive mass
-          if (last >= 0) {
+          if (lane == c && last >= 0) {
             mine = last;
-            mine_at = run >= target ? run : mi;
+            mine_at = at;
           }
         }
-        o_p = hist_pick(L, &L.sel_p, mine, mine_at, &at_p);
+        o_p = hist_pick(L, L.sel_p, mine, mine_at, &at_p);
       }
       if (!(p_on && o_p == kHBins)) {              // a cut among the tiny magnitudes: general search
         int o_c = o_k;
