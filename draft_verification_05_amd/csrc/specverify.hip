@@ -2265,14 +2265,16 @@ __device__ __forceinline__ uint32_t select_cut(const Src& src, LT& L, double cd,
     }
     __syncthreads();
     if (level == 0) {                              // every logit lands in a bucket
+      // the last one (D < -64, -inf, below kfloor) is not tallied: it
+      // weighs nothing, and a count cut there keeps the whole row, as
+      // does a target that no bucket's running count reaches; its atomics
+      // would all hit one word (rows with many -inf logits)
       src.each([&](float l, int64_t) {
         const double D = order_key(l) >= kfloor ? (double)l * cd - (double)mref : -INFINITY;
         const int bk = sel_bucket(D, 0, 0);
-        if (kMass) {
-          const double wr = exp2_small(bk < last ? fma((double)bk, 0.0625, D) : 0.0);
-          atomicAdd(&L.mass[bk], bk < last ? wr : 0.0);
-        } else {
-          atomicAdd(&L.cnt[bk], 1u);
+        if (bk < last) {
+          if (kMass) atomicAdd(&L.mass[bk], exp2_small(fma((double)bk, 0.0625, D)));
+          else       atomicAdd(&L.cnt[bk], 1u);
         }
       });
     } else {                                       // only those of the parent bucket
@@ -2419,16 +2421,22 @@ __device__ __forceinline__ uint32_t lds_select_cut(const LdsRow<NT, NV>& src, RS
     const int bk = t < (float)last ? (t > 0.f ? (int)t : 0) : last;   // also -inf and NaN
     return order_key(l) >= kfloor ? bk : last;
   };
+  // The last bucket (D < -64, -inf, below kfloor, and the slots past V) is
+  // not tallied: it weighs nothing, and a count cut there keeps the whole
+  // row, as does a target that no bucket's running count reaches. Its
+  // atomics would all hit one word (a row of 1000 logits: 31,768 padding
+  // slots, 51 us per call).
 #pragma unroll
   for (int i = 0; i < 4 * NV; ++i) {
     const float l = logit(i);
     const int bk = bucket(l);
-    if (kMass) {
-      const double D = (double)l * cd - (double)mref;
-      const double wr = exp2_small(bk < last ? fma((double)bk, 0.0625, D) : 0.0);
-      atomicAdd(&L.mass[bk], bk < last ? wr : 0.0);
-    } else {
-      atomicAdd(&L.cnt[bk], 1u);
+    if (bk < last) {
+      if (kMass) {
+        const double D = (double)l * cd - (double)mref;
+        atomicAdd(&L.mass[bk], exp2_small(fma((double)bk, 0.0625, D)));
+      } else {
+        atomicAdd(&L.cnt[bk], 1u);
+      }
     }
   }
   __syncthreads();
@@ -3025,8 +3033,13 @@ __device__ __forceinline__ float raw_logit(const uint32_t (&wd)[16], int k) {
 // Sums of the kept weights 2^(l c - M) (l >= thr, token xe left out) of
 // chunks w, w + nw, ... of one row, published to out[chunk]; lane l sums
 // the E consecutive logits of the chunk that the draw gives it. Each wave
-// has the loads of G chunks in flight at once.
-template <int DT, bool kVec, int G = 4>
+// has the loads of G chunks in flight at once. One chunk at a time: with
+// every request reading its row at once (B = 256, bf16 rows of 128256
+// logits, 16 waves per request) the call took 99.5 us against 101.5 with
+// one chunk in flight while another is summed and 102.2 with four in
+// flight; the waves whose loads came back last then still had all their
+// exponentials to do.
+template <int DT, bool kVec, int G = 1>
 __device__ __forceinline__ void kept_chunk_sums(const char* row, int n_chunk, int V, float c, float M, float thr, int xe,
                                                 float* out, int w, int nw) {
   constexpr int kCE = Chunk<DT>::kElems, E = kCE / 64;

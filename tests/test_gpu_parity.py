@@ -841,6 +841,32 @@ def test_filtered_f32_odd_rows():
     check_filtered(wl, "f32 odd rows", top_k, top_p, near_frac=0.5)
 
 
+@pytest.mark.parametrize("V", [1000, 40000])
+def test_filtered_f32_mostly_neg_inf(V):
+    """fp32 rows whose logits are nearly all -inf (a few finite ones per row:
+    5, 40 or all but a handful), on the LDS-resident select (V = 1000) and the
+    streaming one (V = 40000): top-k above the finite count keeps every
+    finite logit, top-k and top-p cuts fall among the few finite values, and
+    the slots past V stay out of the cut."""
+    B = 8
+    rng = np.random.default_rng(443)
+    wl = _onehot_f32(B, V, 444)
+    vals = np.full_like(wl["target"], -np.inf)
+    for b in range(B):
+        keep = rng.choice(V, size=(5, 40, V - 3)[b % 3], replace=False)
+        vals[b][:, keep] = wl["target"][b][:, keep]
+    wl = dict(wl, target=vals)
+    # drafts on finite logits, so that the one-hot rule has mass to test
+    tok = wl["draft_tokens"].copy()
+    for b in range(B):
+        fin = np.flatnonzero(np.isfinite(vals[b, 0]))
+        tok[b] = fin[rng.integers(0, len(fin), size=tok.shape[1])]
+    wl = dict(wl, draft_tokens=tok)
+    top_k = np.array([0, 50, 3, 0, 100, 0, 7, 0], np.int32)
+    top_p = np.array([0.9, 1.0, 0.95, 0.5, 0.99, 0.0, 0.8, 0.95], np.float32)
+    check_filtered(wl, f"f32 mostly -inf V={V}", top_k, top_p, near_frac=0.5)
+
+
 @pytest.mark.parametrize("V", [1, 3, 17])
 def test_filtered_tiny_vocab(V):
     """Rows of 1, 3 and 17 logits (a partial vector in the LDS-resident select,
