@@ -3041,12 +3041,15 @@ __device__ __forceinline__ float raw_logit(const uint32_t (&wd)[16], int k) {
 // exponentials to do.
 template <int DT, bool kVec, int G = 1>
 __device__ __forceinline__ void kept_chunk_sums(const char* row, int n_chunk, int V, float c, float M, float thr, int xe,
-                                                float* out, int w, int nw) {
+                                                float* out, int w, int nw, bool to_lds = false) {
   constexpr int kCE = Chunk<DT>::kElems, E = kCE / 64;
   const int lane = threadIdx.x & 63;
   auto put = [&](int ch, float sm) {
     sm = wave_sum_all(sm);
-    if (lane == 0) publish(out + ch, sm);
+    if (lane == 0) {
+      if (to_lds) out[ch] = sm;
+      else publish(out + ch, sm);
+    }
   };
   // chunks wholly inside an aligned row: G at a time, raw 16-byte loads
   const int n_full = kVec ? V / kCE : 0;
@@ -3089,21 +3092,27 @@ __device__ __forceinline__ void kept_chunk_sums(const char* row, int n_chunk, in
 // kept weights; one-hot: without rc.xe) by nw waves of the calling
 // workgroup, all of whose threads call when nw > 1: the chunk sums go to
 // the row's workspace slice, then wave 0 finds the chunk and the token.
-// Only the one row a request draws from is read.
+// Only the one row a request draws from is read. lds (nw > 1): room for
+// kDrawLdsChunks sums in the workgroup's LDS, used when the row's chunks
+// fit; wave 0 then reads them there rather than back from memory (C3 with
+// top_p 0.95: about 1 us per call).
+constexpr int kDrawLdsChunks = 2048;
+
 template <int DT, bool kVec>
-__device__ __forceinline__ void filtered_draw(const Args& A, int b, const Record& rc, int nw) {
+__device__ __forceinline__ void filtered_draw(const Args& A, int b, const Record& rc, int nw, float* lds = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const Req rq = request(A, b);
   const char* row = row_ptr(A, rq, rc.a);
-  float* fp = A.fpart + ((int64_t)b * A.rows + rc.a) * A.n_chunk;
-  kept_chunk_sums<DT, kVec>(row, A.n_chunk, A.V, rc.c, rc.Mp, rc.tp, rc.xe, fp, wave, nw);
+  const bool in_lds = lds != nullptr && nw > 1 && A.n_chunk <= kDrawLdsChunks;
+  float* fp = in_lds ? lds : A.fpart + ((int64_t)b * A.rows + rc.a) * A.n_chunk;
+  kept_chunk_sums<DT, kVec>(row, A.n_chunk, A.V, rc.c, rc.Mp, rc.tp, rc.xe, fp, wave, nw, in_lds);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);                   // this wave's sums are in memory
   if (nw > 1) __syncthreads();
   if (wave != 0) return;
   int y = draw_from_partials<DT, kVec, false, true>(A, b, rq, rc.a, rc.c, rc.Mp, rc.xe, rc.u, rc.tp,
-                                                    [&](int s) { return make_float2(rc.Mp, fetch(fp + s)); });
+                                                    [&](int s) { return make_float2(rc.Mp, in_lds ? fp[s] : fetch(fp + s)); });
   if (y < 0) y = ((unsigned)rc.xe < (unsigned)A.V) ? rc.xe : 0;   // no kept mass: p_a's mode
   if (lane == 0) A.out_tokens[(int64_t)b * A.out_cols + rc.a] = y;
 }
@@ -3117,6 +3126,7 @@ constexpr int kDrawWaves = kDrawThreads / 64;
 template <int MODE, int DT, bool kVec>
 __global__ __launch_bounds__(kDrawThreads) void sv_ftail_kernel(Args A) {
   __shared__ Record s_rc;
+  __shared__ float s_sums[kDrawLdsChunks];
   const int b = blockIdx.x;
   if (threadIdx.x < 64) {
     const Record rc = filtered_tail<DT, kVec, MODE>(A, b);
@@ -3124,7 +3134,7 @@ __global__ __launch_bounds__(kDrawThreads) void sv_ftail_kernel(Args A) {
   }
   __syncthreads();
   const Record rc = s_rc;
-  if (rc.draw) filtered_draw<DT, kVec>(A, b, rc, kDrawWaves);
+  if (rc.draw) filtered_draw<DT, kVec>(A, b, rc, kDrawWaves, s_sums);
 }
 
 // ------------------------------------------------------ residual pass ---
