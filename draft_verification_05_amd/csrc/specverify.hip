@@ -1798,9 +1798,11 @@ __device__ __forceinline__ double wg_scan(double v, double* wtot, double* excl, 
 
 // Every logit of a row once (f(l, index)), chunk by chunk, the next chunk's
 // load in flight during the current chunk's math; past the row's end f
-// sees -inf.
+// sees -inf. Always inlined: called out of line, a lambda's captured
+// references put its state in scratch memory (the bf16 select kernel's
+// fallback path gave that kernel a private segment).
 template <int DT, bool kVec, class F>
-__device__ void for_each_logit(const char* row, int n_chunk, int V, F f) {
+__device__ __forceinline__ void for_each_logit(const char* row, int n_chunk, int V, F f) {
   constexpr int kCE = Chunk<DT>::kElems, kPT = Chunk<DT>::kPerThread;
   float nx[kPT];
   auto load = [&](int ch) {
